@@ -1,0 +1,182 @@
+"""Python binding of libmoe, the MI355X routed low-bit MoE FFN layer.
+
+Argument marshalling only: every step of the layer runs in the HIP kernels
+of ``libmoe.so`` (built in-tree by ``python -m bit_expert_ffn_router_amd.build``).
+PyTorch is used for device memory and streams.  The functions keep the names
+and argument order of the C ABI in ``include/moe.h``; buffers may be torch
+tensors (their ``data_ptr()`` is passed) or raw integer addresses, and
+``stream`` defaults to torch's current stream.  A negative status raises
+``MoeError`` carrying ``moe_last_error()``.
+
+There is no fallback: importing this package without the built library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "MOE_OK", "MOE_EINVAL", "MOE_EUNSUPPORTED", "MOE_EHIP", "MOE_ENOSPACE",
+    "MOE_Q2SM32", "MOE_Q3S32", "MOE_F32", "MOE_BF16", "MOE_FLAG_RMSNORM_INPUT",
+    "MoeError", "MoeShape", "MoeExpertTable", "MoeMiss", "MoeSlotTable",
+    "moe_packed_expert_bytes", "moe_pack_weights", "moe_unpack_weights",
+    "moe_workspace_bytes", "moe_layer_forward", "moe_slot_table_init",
+    "moe_slot_table_update", "moe_route", "moe_permute_workspace_bytes", "moe_permute",
+    "moe_last_error", "moe_abi_version", "LIB_PATH",
+]
+
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EHIP, MOE_ENOSPACE = 0, -1, -2, -3, -4
+MOE_Q2SM32, MOE_Q3S32 = 1, 2
+MOE_F32, MOE_BF16 = 0, 1
+MOE_FLAG_RMSNORM_INPUT = 1
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        "libmoe.so is not built (%s); run `python -m bit_expert_ffn_router_amd.build` "
+        "(hipcc, gfx950)" % LIB_PATH)
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__("moe status %d: %s" % (status, msg))
+        self.status = status
+
+
+class MoeShape(ctypes.Structure):
+    _fields_ = [("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32),
+                ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("d_ff_shared", ctypes.c_int32), ("qfmt", ctypes.c_int32)]
+
+
+class MoeExpertTable(ctypes.Structure):
+    _fields_ = [("routed", ctypes.c_void_p), ("expert_stride", ctypes.c_size_t),
+                ("slot_of", ctypes.c_void_p), ("n_slots", ctypes.c_int32),
+                ("shared", ctypes.c_void_p)]
+
+
+class MoeMiss(ctypes.Structure):
+    _fields_ = [("token", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("expert", ctypes.c_int32), ("gate", ctypes.c_float)]
+
+
+class MoeSlotTable(ctypes.Structure):
+    _fields_ = [("n_experts", ctypes.c_int32), ("n_slots", ctypes.c_int32),
+                ("slot_of", ctypes.c_void_p), ("expert_of_slot", ctypes.c_void_p),
+                ("host_slot_of", ctypes.c_void_p), ("host_expert_of_slot", ctypes.c_void_p),
+                ("storage", ctypes.c_void_p), ("stride", ctypes.c_size_t),
+                ("expert_bytes", ctypes.c_size_t)]
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_Z = ctypes.c_size_t
+_sigs = {
+    "moe_abi_version": (_I, []),
+    "moe_last_error": (ctypes.c_char_p, []),
+    "moe_packed_expert_bytes": (_Z, [ctypes.POINTER(MoeShape), _I]),
+    "moe_pack_weights": (_I, [ctypes.POINTER(MoeShape), _I, _I, _P, _P, _P, _P, _Z, _P]),
+    "moe_unpack_weights": (_I, [ctypes.POINTER(MoeShape), _I, _I, _P, _Z, _P, _P, _P, _P]),
+    "moe_workspace_bytes": (_Z, [ctypes.POINTER(MoeShape), _I]),
+    "moe_layer_forward": (_I, [ctypes.POINTER(MoeShape), _I, _P, _I, ctypes.c_uint32, _P,
+                               ctypes.POINTER(MoeExpertTable), _P, _I, _P, _I, _P, _P, _Z, _P]),
+    "moe_slot_table_init": (_I, [ctypes.POINTER(MoeSlotTable), _P]),
+    "moe_slot_table_update": (_I, [ctypes.POINTER(MoeSlotTable), _I, _P, _P, _P, _P]),
+    "moe_route": (_I, [_P, _I, _I, _I, _P, _P, _P]),
+    "moe_permute_workspace_bytes": (_Z, [_I, _I, _I]),
+    "moe_permute": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _Z, _P]),
+}
+for _name, (_res, _args) in _sigs.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+
+def _ptr(v):
+    """Device/host address of a tensor, an int address, or None (NULL)."""
+    if v is None:
+        return None
+    if isinstance(v, int):
+        return v
+    return v.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int) -> None:
+    if status != MOE_OK:
+        raise MoeError(status, moe_last_error())
+
+
+def moe_abi_version() -> int:
+    return _lib.moe_abi_version()
+
+
+def moe_last_error() -> str:
+    return _lib.moe_last_error().decode()
+
+
+def moe_packed_expert_bytes(shape: MoeShape, d_ff: int) -> int:
+    return _lib.moe_packed_expert_bytes(ctypes.byref(shape), d_ff)
+
+
+def moe_pack_weights(shape, n, d_ff, codes, scale, min, dst, dst_stride, stream=None):
+    _check(_lib.moe_pack_weights(ctypes.byref(shape), n, d_ff, _ptr(codes), _ptr(scale),
+                                 _ptr(min), _ptr(dst), dst_stride, _stream(stream)))
+
+
+def moe_unpack_weights(shape, n, d_ff, src, src_stride, codes, scale, min, stream=None):
+    _check(_lib.moe_unpack_weights(ctypes.byref(shape), n, d_ff, _ptr(src), src_stride,
+                                   _ptr(codes), _ptr(scale), _ptr(min), _stream(stream)))
+
+
+def moe_workspace_bytes(shape: MoeShape, tokens: int) -> int:
+    return _lib.moe_workspace_bytes(ctypes.byref(shape), tokens)
+
+
+def moe_layer_forward(shape, tokens, x, x_dtype, flags, router_logits, table, out, out_dtype,
+                      miss, miss_cap, miss_count, ws, ws_bytes, stream=None):
+    _check(_lib.moe_layer_forward(ctypes.byref(shape), tokens, _ptr(x), x_dtype, flags,
+                                  _ptr(router_logits), ctypes.byref(table), _ptr(out), out_dtype,
+                                  _ptr(miss), miss_cap, _ptr(miss_count), _ptr(ws), ws_bytes,
+                                  _stream(stream)))
+
+
+def moe_slot_table_init(table: MoeSlotTable, stream=None):
+    _check(_lib.moe_slot_table_init(ctypes.byref(table), _stream(stream)))
+
+
+def moe_slot_table_update(table: MoeSlotTable, slots, experts, src_ptrs, stream=None):
+    """slots, experts: sequences of ints; src_ptrs: sequence of addresses (or tensors/None)."""
+    n = len(slots)
+    s_arr = (ctypes.c_int32 * max(n, 1))(*slots)
+    e_arr = (ctypes.c_int32 * max(n, 1))(*experts)
+    p_arr = (ctypes.c_void_p * max(n, 1))(*[_ptr(p) for p in src_ptrs])
+    _check(_lib.moe_slot_table_update(ctypes.byref(table), n, ctypes.cast(s_arr, _P),
+                                      ctypes.cast(e_arr, _P), ctypes.cast(p_arr, _P),
+                                      _stream(stream)))
+
+
+def moe_route(logits, tokens, n_experts, top_k, idx, gate, stream=None):
+    _check(_lib.moe_route(_ptr(logits), tokens, n_experts, top_k, _ptr(idx), _ptr(gate),
+                          _stream(stream)))
+
+
+def moe_permute_workspace_bytes(tokens: int, top_k: int, n_experts: int) -> int:
+    return _lib.moe_permute_workspace_bytes(tokens, top_k, n_experts)
+
+
+def moe_permute(idx, tokens, top_k, n_experts, offsets, sorted_pairs, inv, ws, ws_bytes,
+                stream=None):
+    _check(_lib.moe_permute(_ptr(idx), tokens, top_k, n_experts, _ptr(offsets),
+                            _ptr(sorted_pairs), _ptr(inv), _ptr(ws), ws_bytes, _stream(stream)))

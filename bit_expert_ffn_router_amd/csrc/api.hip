@@ -1,0 +1,324 @@
+// C ABI of libmoe: argument validation, workspace sizing and dispatch.
+// Every entry point validates on the host, returns a negative status with a
+// message (moe_last_error) on a bad call and launches nothing in that case.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <vector>
+
+#include "../../include/moe.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+moe_status fail(moe_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+moe_status ok() {
+  g_err[0] = '\0';
+  return MOE_OK;
+}
+
+moe_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MOE_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned256(const void* p) { return ((uintptr_t)p & 255u) == 0; }
+
+// Shape checks shared by every entry point.
+moe_status check_shape(const moe_shape* s) {
+  if (!s) return fail(MOE_EINVAL, "shape is NULL");
+  if (s->qfmt != MOE_Q2SM32 && s->qfmt != MOE_Q3S32)
+    return fail(MOE_EINVAL, "unknown qfmt %d", (int)s->qfmt);
+  if (s->d_model <= 0 || s->d_model % 256 != 0)
+    return fail(MOE_EINVAL, "d_model %d must be a positive multiple of 256", (int)s->d_model);
+  if (s->d_ff <= 0 || s->d_ff % 32 != 0)
+    return fail(MOE_EINVAL, "d_ff %d must be a positive multiple of 32", (int)s->d_ff);
+  if (s->d_ff_shared < 0 || s->d_ff_shared % 32 != 0)
+    return fail(MOE_EINVAL, "d_ff_shared %d must be a non-negative multiple of 32",
+                (int)s->d_ff_shared);
+  if (s->n_experts <= 0 || s->n_experts > 2048)
+    return fail(MOE_EINVAL, "n_experts %d must be in 1..2048", (int)s->n_experts);
+  if (s->top_k < 1 || s->top_k > 32 || s->top_k > s->n_experts)
+    return fail(MOE_EINVAL, "top_k %d must be in 1..min(32, n_experts)", (int)s->top_k);
+  return ok();
+}
+
+bool use_decode_path(int T) { return T <= moe::kDecodeMaxT; }
+
+size_t forward_ws_bytes(const moe_shape* s, int T) {
+  if (T <= 0) return 0;
+  if (use_decode_path(T))
+    return moe::decode_ws_bytes(T, s->d_model, s->d_ff, s->d_ff_shared, s->n_experts, s->top_k);
+  return moe::prefill_ws_bytes(T, s->d_model, s->d_ff, s->d_ff_shared, s->n_experts, s->top_k);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_last_error(void) { return g_err; }
+
+size_t moe_packed_expert_bytes(const moe_shape* shape, int32_t d_ff) {
+  if (check_shape(shape) != MOE_OK) return 0;
+  if (d_ff <= 0 || d_ff % 32 != 0) return 0;
+  return moe::packed_bytes(shape->d_model, d_ff, shape->qfmt);
+}
+
+moe_status moe_pack_weights(const moe_shape* shape, int32_t n, int32_t d_ff, const void* codes,
+                            const uint16_t* scale, const uint16_t* min, void* dst,
+                            size_t dst_stride, moe_stream_t stream) {
+  moe_status s = check_shape(shape);
+  if (s != MOE_OK) return s;
+  if (n < 0) return fail(MOE_EINVAL, "n %d < 0", (int)n);
+  if (d_ff <= 0 || d_ff % 32 != 0) return fail(MOE_EINVAL, "d_ff %d must be a multiple of 32", (int)d_ff);
+  if (n == 0) return ok();
+  if (!codes || !scale || !dst) return fail(MOE_EINVAL, "codes, scale and dst are required");
+  if (shape->qfmt == MOE_Q2SM32 && !min) return fail(MOE_EINVAL, "Q2SM needs min");
+  const size_t need = moe::packed_bytes(shape->d_model, d_ff, shape->qfmt);
+  if (dst_stride < need || dst_stride % 256 != 0)
+    return fail(MOE_EINVAL, "dst_stride %zu must be >= %zu and a multiple of 256", dst_stride, need);
+  if (!aligned256(dst)) return fail(MOE_EINVAL, "dst must be 256-byte aligned");
+  if (((uintptr_t)codes & 7u) || ((uintptr_t)scale & 1u) || (min && ((uintptr_t)min & 1u)))
+    return fail(MOE_EINVAL, "codes must be 8-byte aligned, scale/min 2-byte aligned");
+  return hip_status(moe::launch_pack(shape->qfmt, shape->d_model, d_ff, n, codes, scale,
+                                     shape->qfmt == MOE_Q2SM32 ? min : nullptr, dst, dst_stride,
+                                     (hipStream_t)stream),
+                    "pack launch");
+}
+
+moe_status moe_unpack_weights(const moe_shape* shape, int32_t n, int32_t d_ff, const void* src,
+                              size_t src_stride, void* codes, uint16_t* scale, uint16_t* min,
+                              moe_stream_t stream) {
+  moe_status s = check_shape(shape);
+  if (s != MOE_OK) return s;
+  if (n < 0) return fail(MOE_EINVAL, "n %d < 0", (int)n);
+  if (d_ff <= 0 || d_ff % 32 != 0) return fail(MOE_EINVAL, "d_ff %d must be a multiple of 32", (int)d_ff);
+  if (n == 0) return ok();
+  if (!src || !codes || !scale) return fail(MOE_EINVAL, "src, codes and scale are required");
+  if (shape->qfmt == MOE_Q2SM32 && !min) return fail(MOE_EINVAL, "Q2SM needs min");
+  const size_t need = moe::packed_bytes(shape->d_model, d_ff, shape->qfmt);
+  if (src_stride < need || src_stride % 256 != 0)
+    return fail(MOE_EINVAL, "src_stride %zu must be >= %zu and a multiple of 256", src_stride, need);
+  if (!aligned256(src)) return fail(MOE_EINVAL, "src must be 256-byte aligned");
+  if (((uintptr_t)codes & 7u) || ((uintptr_t)scale & 1u) || (min && ((uintptr_t)min & 1u)))
+    return fail(MOE_EINVAL, "codes must be 8-byte aligned, scale/min 2-byte aligned");
+  return hip_status(moe::launch_unpack(shape->qfmt, shape->d_model, d_ff, n, src, src_stride,
+                                       codes, scale, min, (hipStream_t)stream),
+                    "unpack launch");
+}
+
+size_t moe_workspace_bytes(const moe_shape* shape, int32_t tokens) {
+  if (check_shape(shape) != MOE_OK || tokens < 0) return 0;
+  return forward_ws_bytes(shape, tokens);
+}
+
+moe_status moe_layer_forward(const moe_shape* shape, int32_t tokens, const void* x,
+                             int32_t x_dtype, uint32_t flags, const float* router_logits,
+                             const moe_expert_table* table, void* out, int32_t out_dtype,
+                             moe_miss* miss, int32_t miss_cap, int32_t* miss_count, void* ws,
+                             size_t ws_bytes, moe_stream_t stream) {
+  moe_status s = check_shape(shape);
+  if (s != MOE_OK) return s;
+  const int T = tokens;
+  if (T < 0) return fail(MOE_EINVAL, "tokens %d < 0", T);
+  if (!table) return fail(MOE_EINVAL, "table is NULL");
+  if (x_dtype != MOE_BF16 && x_dtype != MOE_F32) return fail(MOE_EINVAL, "bad x_dtype %d", (int)x_dtype);
+  if (out_dtype != MOE_BF16 && out_dtype != MOE_F32)
+    return fail(MOE_EINVAL, "bad out_dtype %d", (int)out_dtype);
+  if (flags & ~(uint32_t)MOE_FLAG_RMSNORM_INPUT) return fail(MOE_EINVAL, "unknown flags 0x%x", flags);
+  const size_t need_e = moe::packed_bytes(shape->d_model, shape->d_ff, shape->qfmt);
+  if (!table->routed) return fail(MOE_EINVAL, "table->routed is NULL");
+  if (table->expert_stride < need_e || table->expert_stride % 256 != 0)
+    return fail(MOE_EINVAL, "expert_stride %zu must be >= %zu and a multiple of 256",
+                table->expert_stride, need_e);
+  if (!aligned256(table->routed)) return fail(MOE_EINVAL, "table->routed must be 256-byte aligned");
+  if ((shape->d_ff_shared > 0) != (table->shared != nullptr))
+    return fail(MOE_EINVAL, "table->shared must be given iff d_ff_shared > 0");
+  if (table->shared && !aligned256(table->shared))
+    return fail(MOE_EINVAL, "table->shared must be 256-byte aligned");
+  const bool slots = table->slot_of != nullptr;
+  if (slots) {
+    if (table->n_slots <= 0) return fail(MOE_EINVAL, "n_slots must be > 0 with a slot table");
+    if (!miss || !miss_count) return fail(MOE_EINVAL, "slot mode needs miss and miss_count");
+    if ((int64_t)miss_cap < (int64_t)T * shape->top_k)
+      return fail(MOE_ENOSPACE, "miss_cap %d < tokens*top_k = %lld", (int)miss_cap,
+                  (long long)T * shape->top_k);
+  }
+  if (T == 0) return ok();
+  if (!x || !router_logits || !out || !ws) return fail(MOE_EINVAL, "x, router_logits, out, ws are required");
+  if (!aligned256(ws)) return fail(MOE_EINVAL, "ws must be 256-byte aligned");
+  if (((uintptr_t)x & 15u) || ((uintptr_t)router_logits & 3u) || ((uintptr_t)out & 3u))
+    return fail(MOE_EINVAL, "x must be 16-byte aligned, logits and out 4-byte aligned");
+  const size_t need_ws = forward_ws_bytes(shape, T);
+  if (ws_bytes < need_ws) return fail(MOE_ENOSPACE, "ws_bytes %zu < %zu", ws_bytes, need_ws);
+  if (use_decode_path(T)) {
+    if (shape->d_model > 4096 || shape->d_ff > 1024 || shape->d_ff_shared > 1024)
+      return fail(MOE_EUNSUPPORTED, "decode path supports d_model <= 4096, d_ff <= 1024");
+    moe::DecodeArgs a;
+    a.T = T;
+    a.D = shape->d_model;
+    a.F = shape->d_ff;
+    a.Fs = shape->d_ff_shared;
+    a.E = shape->n_experts;
+    a.k = shape->top_k;
+    a.fmt = shape->qfmt;
+    a.x = x;
+    a.x_bf16 = x_dtype == MOE_BF16;
+    a.rmsnorm = (flags & MOE_FLAG_RMSNORM_INPUT) != 0;
+    a.logits = router_logits;
+    a.routed = (const uint8_t*)table->routed;
+    a.stride = table->expert_stride;
+    a.slot_of = table->slot_of;
+    a.shared = (const uint8_t*)table->shared;
+    a.out = out;
+    a.out_bf16 = out_dtype == MOE_BF16;
+    a.miss = (moe::MissRec*)miss;
+    a.miss_count = miss_count;
+    const moe::DecodeWs w = moe::decode_ws_carve(ws, T, a.D, a.F, a.Fs, a.E, a.k);
+    return hip_status(moe::launch_decode(a, w, (hipStream_t)stream), "decode launch");
+  }
+  if (slots) return fail(MOE_EUNSUPPORTED, "slot tables are supported on the decode path (tokens <= 4)");
+  if (shape->qfmt != MOE_Q2SM32) return fail(MOE_EUNSUPPORTED, "prefill path supports Q2SM only");
+  moe::PrefillArgs a;
+  a.T = T;
+  a.D = shape->d_model;
+  a.F = shape->d_ff;
+  a.Fs = shape->d_ff_shared;
+  a.E = shape->n_experts;
+  a.k = shape->top_k;
+  a.fmt = shape->qfmt;
+  a.x = x;
+  a.x_bf16 = x_dtype == MOE_BF16;
+  a.rmsnorm = (flags & MOE_FLAG_RMSNORM_INPUT) != 0;
+  a.logits = router_logits;
+  a.routed = (const uint8_t*)table->routed;
+  a.stride = table->expert_stride;
+  a.shared = (const uint8_t*)table->shared;
+  a.out = out;
+  a.out_bf16 = out_dtype == MOE_BF16;
+  return hip_status(moe::launch_prefill(a, ws, (hipStream_t)stream), "prefill launch");
+}
+
+moe_status moe_slot_table_init(moe_slot_table* t, moe_stream_t stream) {
+  if (!t) return fail(MOE_EINVAL, "table is NULL");
+  if (t->n_experts <= 0 || t->n_slots <= 0) return fail(MOE_EINVAL, "n_experts and n_slots must be > 0");
+  if (!t->slot_of || !t->expert_of_slot || !t->host_slot_of || !t->host_expert_of_slot)
+    return fail(MOE_EINVAL, "map arrays and host mirrors are required");
+  for (int i = 0; i < t->n_experts; ++i) t->host_slot_of[i] = -1;
+  for (int i = 0; i < t->n_slots; ++i) t->host_expert_of_slot[i] = -1;
+  return hip_status(moe::launch_slot_init(t->slot_of, t->n_experts, t->expert_of_slot, t->n_slots,
+                                          (hipStream_t)stream),
+                    "slot init launch");
+}
+
+moe_status moe_slot_table_update(moe_slot_table* t, int32_t n, const int32_t* slots,
+                                 const int32_t* experts, const void* const* src,
+                                 moe_stream_t stream) {
+  if (!t) return fail(MOE_EINVAL, "table is NULL");
+  if (n < 0) return fail(MOE_EINVAL, "n %d < 0", (int)n);
+  if (n == 0) return ok();
+  if (!slots || !experts) return fail(MOE_EINVAL, "slots and experts are required");
+  if (!t->slot_of || !t->expert_of_slot || !t->host_slot_of || !t->host_expert_of_slot ||
+      !t->storage)
+    return fail(MOE_EINVAL, "table arrays are required");
+  if (t->stride % 256 != 0 || t->expert_bytes > t->stride || !aligned256(t->storage))
+    return fail(MOE_EINVAL, "storage must be 256-byte aligned, stride a multiple of 256 >= expert_bytes");
+  const int E = t->n_experts, S = t->n_slots;
+  std::vector<char> slot_named(S, 0), expert_named(E, 0);
+  for (int i = 0; i < n; ++i) {
+    const int sl = slots[i], ex = experts[i];
+    if (sl < 0 || sl >= S) return fail(MOE_EINVAL, "slot %d out of range", sl);
+    if (ex < -1 || ex >= E) return fail(MOE_EINVAL, "expert %d out of range", ex);
+    if (slot_named[sl]) return fail(MOE_EINVAL, "slot %d named twice", sl);
+    slot_named[sl] = 1;
+    if (ex >= 0) {
+      if (expert_named[ex]) return fail(MOE_EINVAL, "expert %d named twice", ex);
+      expert_named[ex] = 1;
+      if (!src || !src[i]) return fail(MOE_EINVAL, "src[%d] is NULL for an install", i);
+    }
+  }
+  for (int i = 0; i < n; ++i) {
+    const int ex = experts[i];
+    if (ex >= 0) {
+      const int cur = t->host_slot_of[ex];
+      if (cur >= 0 && !slot_named[cur])
+        return fail(MOE_EINVAL, "expert %d is already resident in slot %d", ex, cur);
+    }
+  }
+  // Validated: apply.  Copies first, then the map edits, all stream-ordered.
+  std::vector<moe::SlotEdit> edits(n);
+  for (int i = 0; i < n; ++i) {
+    edits[i].slot = slots[i];
+    edits[i].expert = experts[i];
+    edits[i].old_expert = t->host_expert_of_slot[slots[i]];
+    edits[i].pad = 0;
+    if (experts[i] >= 0) {
+      hipError_t e = hipMemcpyAsync((uint8_t*)t->storage + (size_t)slots[i] * t->stride, src[i],
+                                    t->expert_bytes, hipMemcpyDefault, (hipStream_t)stream);
+      if (e != hipSuccess) return hip_status(e, "slot copy");
+    }
+  }
+  for (int i0 = 0; i0 < n; i0 += moe::kSlotEditsPerLaunch) {
+    const int m = n - i0 < moe::kSlotEditsPerLaunch ? n - i0 : moe::kSlotEditsPerLaunch;
+    hipError_t e = moe::launch_slot_edits(t->slot_of, t->expert_of_slot, edits.data() + i0, m,
+                                          (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e, "slot edit launch");
+  }
+  // Host mirror: evictions first, then installs.
+  for (int i = 0; i < n; ++i)
+    if (edits[i].old_expert >= 0) t->host_slot_of[edits[i].old_expert] = -1;
+  for (int i = 0; i < n; ++i) {
+    t->host_expert_of_slot[slots[i]] = experts[i];
+    if (experts[i] >= 0) t->host_slot_of[experts[i]] = slots[i];
+  }
+  return ok();
+}
+
+moe_status moe_route(const float* logits, int32_t tokens, int32_t n_experts, int32_t top_k,
+                     int32_t* idx, float* gate, moe_stream_t stream) {
+  if (tokens < 0) return fail(MOE_EINVAL, "tokens < 0");
+  if (n_experts <= 0 || n_experts > 2048) return fail(MOE_EINVAL, "n_experts must be in 1..2048");
+  if (top_k < 1 || top_k > 32 || top_k > n_experts) return fail(MOE_EINVAL, "top_k out of range");
+  if (tokens == 0) return ok();
+  if (!logits || !idx || !gate) return fail(MOE_EINVAL, "logits, idx, gate are required");
+  return hip_status(moe::launch_route(logits, tokens, n_experts, top_k, idx, gate,
+                                      (hipStream_t)stream),
+                    "route launch");
+}
+
+size_t moe_permute_workspace_bytes(int32_t tokens, int32_t top_k, int32_t n_experts) {
+  if (tokens < 0 || top_k < 1 || n_experts < 1) return 0;
+  return moe::perm_ws_bytes(tokens, top_k, n_experts);
+}
+
+moe_status moe_permute(const int32_t* idx, int32_t tokens, int32_t top_k, int32_t n_experts,
+                       int32_t* offsets, int32_t* sorted_pairs, int32_t* inv, void* ws,
+                       size_t ws_bytes, moe_stream_t stream) {
+  if (tokens < 0) return fail(MOE_EINVAL, "tokens < 0");
+  if (n_experts <= 0 || n_experts > 2048) return fail(MOE_EINVAL, "n_experts must be in 1..2048");
+  if (top_k < 1 || top_k > 32 || top_k > n_experts) return fail(MOE_EINVAL, "top_k out of range");
+  if (!offsets) return fail(MOE_EINVAL, "offsets is required");
+  if ((int64_t)tokens * top_k > (int64_t)1 << 30) return fail(MOE_EINVAL, "too many pairs");
+  if (tokens > 0 && (!idx || !sorted_pairs || !inv || !ws))
+    return fail(MOE_EINVAL, "idx, sorted_pairs, inv, ws are required");
+  const size_t need = moe::perm_ws_bytes(tokens, top_k, n_experts);
+  if (tokens > 0 && ws_bytes < need) return fail(MOE_ENOSPACE, "ws_bytes %zu < %zu", ws_bytes, need);
+  const moe::PermWs w = moe::perm_ws_carve(ws, tokens, top_k, n_experts);
+  return hip_status(moe::launch_permute(idx, tokens, top_k, n_experts, offsets, sorted_pairs, inv,
+                                        w, (hipStream_t)stream),
+                    "permute launch");
+}
+
+}  // extern "C"

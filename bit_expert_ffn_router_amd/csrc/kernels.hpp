@@ -1,0 +1,101 @@
+// Internal launch interface between the C ABI (api.hip) and the kernels.
+#pragma once
+
+#include "common.hpp"
+
+namespace moe {
+
+// A non-resident (token, rank) pair; same layout as moe_miss in moe.h.
+struct MissRec {
+  int32_t token, rank, expert;
+  float gate;
+};
+
+// ---------------------------------------------------------------- packing
+hipError_t launch_pack(int fmt, int D, int F, int n, const void* codes, const uint16_t* scale,
+                       const uint16_t* mins, void* dst, size_t dst_stride, hipStream_t st);
+hipError_t launch_unpack(int fmt, int D, int F, int n, const void* src, size_t src_stride,
+                         void* codes, uint16_t* scale, uint16_t* mins, hipStream_t st);
+
+// ---------------------------------------------------------------- routing
+hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* idx, float* gate,
+                        hipStream_t st);
+
+// ---------------------------------------------------------------- permutation
+struct PermWs {
+  int32_t* chunk_counts;  // [E][nchunks] (expert-major)
+  int32_t* totals;        // [E]
+  int nchunks;
+};
+constexpr int kPermChunk = 256;
+size_t perm_ws_bytes(int T, int k, int E);
+PermWs perm_ws_carve(void* ws, int T, int k, int E);
+hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offsets,
+                          int32_t* sorted_pairs, int32_t* inv, const PermWs& w, hipStream_t st);
+
+// ---------------------------------------------------------------- decode path (T <= 4)
+constexpr int kDecodeMaxT = 4;
+
+struct DecodeWs {
+  int32_t* idx;        // [T*k]
+  float* gate;         // [T*k]
+  int32_t* nwork;      // [1]
+  int32_t* work_ref;   // [Wmax] routed index (expert or slot) or -1 = shared
+  float* work_gate;    // [Wmax][4]
+  uint16_t* xa_hi;     // [T][D] bf16 operand
+  uint16_t* xa_lo;     // [T][D] bf16 residual (fp32 inputs)
+  float2* xs;          // [T][D/32] block sums (X, X')
+  uint16_t* hh;        // [Wmax][T][Fp] bf16 hi of h
+  uint16_t* hl;        // [Wmax][T][Fp] bf16 lo of h
+  float2* hs;          // [Wmax][T][Fp/32] block sums of h
+  int Wmax;            // routed work capacity + 1 (shared)
+  int Fp;              // padded FFN width of the h rows
+};
+
+struct DecodeArgs {
+  int T, D, F, Fs, E, k, fmt;
+  const void* x;
+  int x_bf16;       // 1: x is bf16, 0: fp32
+  int rmsnorm;      // MOE_FLAG_RMSNORM_INPUT
+  const float* logits;
+  const uint8_t* routed;
+  size_t stride;
+  const int32_t* slot_of;  // NULL = all resident
+  const uint8_t* shared;   // NULL = no shared expert
+  void* out;
+  int out_bf16;
+  MissRec* miss;
+  int32_t* miss_count;
+};
+
+size_t decode_ws_bytes(int T, int D, int F, int Fs, int E, int k);
+DecodeWs decode_ws_carve(void* ws, int T, int D, int F, int Fs, int E, int k);
+hipError_t launch_decode(const DecodeArgs& a, const DecodeWs& w, hipStream_t st);
+
+// ---------------------------------------------------------------- prefill path
+struct PrefillArgs {
+  int T, D, F, Fs, E, k, fmt;
+  const void* x;
+  int x_bf16;
+  int rmsnorm;
+  const float* logits;
+  const uint8_t* routed;
+  size_t stride;
+  const uint8_t* shared;
+  void* out;
+  int out_bf16;
+};
+size_t prefill_ws_bytes(int T, int D, int F, int Fs, int E, int k);
+hipError_t launch_prefill(const PrefillArgs& a, void* ws, hipStream_t st);
+
+// ---------------------------------------------------------------- slot table
+struct SlotEdit {
+  int32_t slot, expert, old_expert, pad;
+};
+constexpr int kSlotEditsPerLaunch = 32;
+hipError_t launch_slot_edits(int32_t* slot_of, int32_t* expert_of_slot, const SlotEdit* edits,
+                             int n, hipStream_t st);
+hipError_t launch_slot_init(int32_t* slot_of, int E, int32_t* expert_of_slot, int S,
+                            hipStream_t st);
+
+}  // namespace moe

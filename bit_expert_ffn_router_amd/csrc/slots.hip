@@ -1,0 +1,49 @@
+// Resident-expert slot table edits.  The pages keep the most used experts
+// resident on the GPU and swap them while serving ([AF] "个人开发者用 AI 十天
+// 写出 Strata 引擎…", section "命中率七成，代价是答案会变"; [JD]
+// "5070ti16g单卡跑qwen 3.8 flash next …", section "为什么从 18t/s 变成
+// 60-90t/s").  The host validates each update against its mirror of the
+// table; these kernels apply the already-validated map edits on the stream.
+#include "kernels.hpp"
+
+namespace moe {
+
+struct SlotEditBatch {
+  SlotEdit e[kSlotEditsPerLaunch];
+};
+
+// One thread per edit.  Evictions are applied before installs (a slot's old
+// expert may be installed elsewhere by the same batch).
+__global__ void slot_edit_kernel(int32_t* slot_of, int32_t* expert_of_slot, SlotEditBatch b,
+                                 int n) {
+  const int i = threadIdx.x;
+  if (i < n && b.e[i].old_expert >= 0) slot_of[b.e[i].old_expert] = -1;
+  __syncthreads();
+  if (i < n) {
+    expert_of_slot[b.e[i].slot] = b.e[i].expert;
+    if (b.e[i].expert >= 0) slot_of[b.e[i].expert] = b.e[i].slot;
+  }
+}
+
+__global__ void slot_init_kernel(int32_t* slot_of, int E, int32_t* expert_of_slot, int S) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < E) slot_of[i] = -1;
+  if (i < S) expert_of_slot[i] = -1;
+}
+
+hipError_t launch_slot_edits(int32_t* slot_of, int32_t* expert_of_slot, const SlotEdit* edits,
+                             int n, hipStream_t st) {
+  SlotEditBatch b;
+  for (int i = 0; i < n; ++i) b.e[i] = edits[i];
+  slot_edit_kernel<<<1, kSlotEditsPerLaunch, 0, st>>>(slot_of, expert_of_slot, b, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_slot_init(int32_t* slot_of, int E, int32_t* expert_of_slot, int S,
+                            hipStream_t st) {
+  const int m = E > S ? E : S;
+  slot_init_kernel<<<(m + 255) / 256, 256, 0, st>>>(slot_of, E, expert_of_slot, S);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,270 @@
+/*
+ * moe.h -- C ABI of libmoe, the routed low-bit mixture-of-experts FFN layer
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Sources ("the pages"):
+ *   [KC-en] "Running Qwen3.8-Flash-Next on a 12GB GPU: Custom Engine Hits 65 tok/s"
+ *   [JD]    "5070ti16g单卡跑qwen 3.8 flash next 新方案最高90t/s Hermes调用60t/s"
+ *   [AF]    "个人开发者用 AI 十天写出 Strata 引擎，让 12GB 显存跑起 1250 亿参数的
+ *            Qwen 3.8 Flash Next"
+ *   [SL]    daily.steinslab.io, "一台装着 12GB 显存游戏显卡的家用电脑…"
+ *
+ * The layer: each of 48 layers has 512 routed experts; a token uses the 10
+ * most relevant of them plus one shared expert ([AF] section "1250 亿参数，
+ * 每个词只用得上 2%"; [SL] section "12GB 显存装下 1250 亿参数").  Expert
+ * weights are low-bit block-quantised ([KC-en] section "Hardware
+ * Configuration and Quantization Approach").  Hot experts stay resident on
+ * the GPU, the others are computed elsewhere and added into the same layer
+ * ([AF] section "命中率七成，代价是答案会变").  The pages give no formulas;
+ * the readings this library implements are:
+ *   out_t = sum_{j<k} g_tj * FFN_{e_tj}(x_t) + FFN_shared(x_t)
+ *   FFN(x) = W_down (silu(W_gate x) * (W_up x)),  silu(a) = a / (1 + e^-a)
+ *   e_t0..e_t(k-1): the k largest fp32 logits of token t, ties to the lower
+ *   expert id, -0.0 == +0.0;  g_tj = exp(l_j - l_0) / sum_i exp(l_i - l_0).
+ *
+ * Conventions for every entry point:
+ *   - Pointers named "device" are HIP device (HBM) addresses; "host" are
+ *     CPU addresses.  The caller allocates and frees every buffer, including
+ *     the workspace; the library allocates no memory and keeps no state
+ *     between calls (moe_last_error's per-thread message aside).
+ *   - All device work is enqueued on the caller's stream (NULL = the null
+ *     stream); nothing waits on the host.  Device-resident results (outputs,
+ *     miss lists, counts) are valid after the caller synchronises the stream.
+ *   - Arguments are validated on the host before anything is enqueued; a
+ *     rejected call returns a negative moe_status, sets moe_last_error(),
+ *     and launches nothing.  A failed launch returns MOE_EHIP.  Faults inside
+ *     a kernel surface at the caller's next synchronisation of the stream.
+ *   - Calls are re-entrant for distinct buffers; two calls that share a
+ *     workspace or output must be ordered by the caller (same stream).
+ *   - No C++ exception crosses this interface.
+ *
+ * ---------------------------------------------------------------------------
+ * Quantised formats (one block = 32 consecutive weights along the reduction
+ * dimension of one output row; the pages name 2- and 3-bit expert formats,
+ * [KC-en] section "Detailed Performance Numbers", but give no layout):
+ *   MOE_Q2SM32: u in {0,1,2,3}, fp16 scale s and fp16 min m per block:
+ *               w = s*u + m                                (3.0 bits/weight)
+ *   MOE_Q3S32:  q in {-4..3}, fp16 scale s per block: w = s*q  (3.5 bits/weight)
+ *
+ * Logical (unpacked) expert weights, the input of moe_pack_weights, for an
+ * expert of model width D and FFN width F: three matrices in the order
+ * W_gate [F][D], W_up [F][D], W_down [D][F], each row-major; codes are one
+ * byte per weight ([3][F*D]; Q2SM: u; Q3S: q as a signed byte); scales and
+ * mins are fp16 bit patterns, one per block ([3][F*D/32], row-major over
+ * [rows][K/32]).
+ *
+ * Packed layout (the "pack" the pages build once before serving, [JD]
+ * section "为什么从 18t/s 变成 60-90t/s"; this layout is this library's
+ * own).  A matrix with R rows and reduction length K is cut into records of
+ * 16 rows x 256 columns (8 blocks, one "octet"); K is padded with zero
+ * codes and zero scale/min up to a multiple of 256.  Inside a record, lane
+ * L = 16*q + n (n = row within the record, q = 0..3) owns four 32-bit code
+ * words; word w covers blocks 2w and 2w+1 of the octet; slot s = 0..7 of a
+ * word holds block b = 2w + s/4 and pair j = s%4: the code of column
+ * 32*b + 8*q + 2*j is at bits 2s..2s+1 and the code of the next column at
+ * bits 16+2s..17+2s.
+ *   Q2SM record, 1536 bytes: bytes [0,1024) code words, lane-major (word
+ *     (L, w) at byte 16*L + 4*w); bytes [1024,1536): for n in 0..15, b in
+ *     0..7, the fp16 scale then the fp16 min of (row n, block b), at byte
+ *     1024 + 4*(8*n + b).
+ *   Q3S record, 1792 bytes: bytes [0,1024) low-plane words as above holding
+ *     (q+4) & 3; bytes [1024,1536): high-plane words, two per lane (word
+ *     (L, h) at byte 1024 + 8*L + 4*h); high word h serves low words 2h and
+ *     2h+1: the high bit ((q+4) >> 2) of the code at bit p of low word 2h is
+ *     bit p+1 of the high word, of low word 2h+1 bit p; bytes [1536,1792):
+ *     the fp16 scale of (row n, block b) at byte 1536 + 2*(8*n + b).
+ * A packed expert is its gate/up region followed by its down region:
+ *   gate/up: for g in 0..F/16-1, for matrix in (W_gate, W_up), for each
+ *     octet o of D: the record of rows 16g..16g+15, columns 256o..256o+255;
+ *   down: for r in 0..D/16-1, for each octet o of F (padded): the record of
+ *     W_down rows 16r..16r+15.
+ * Requirements: D % 256 == 0, F % 32 == 0.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* moe_stream_t; /* the same type as hipStream_t */
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = -1,       /* bad argument: null pointer, bad size or shape, conflict */
+  MOE_EUNSUPPORTED = -2, /* valid request this build does not implement */
+  MOE_EHIP = -3,         /* a HIP runtime call or kernel launch failed */
+  MOE_ENOSPACE = -4      /* workspace or miss-list capacity too small */
+} moe_status;
+
+typedef enum { MOE_Q2SM32 = 1, MOE_Q3S32 = 2 } moe_qfmt;
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Input flag of moe_layer_forward: normalise each token's input first,
+ * x <- bf16(x / sqrt(mean(x^2) + 1e-6)), computed in fp32.  The pages stack
+ * 48 layers but print nothing of the rest of a block; this parameter-free
+ * RMS step stands in for it when layers are chained. */
+#define MOE_FLAG_RMSNORM_INPUT 1u
+
+/* Layer geometry.  d_model % 256 == 0; d_ff and d_ff_shared are multiples
+ * of 32 (d_ff_shared may be 0: no shared expert); 1 <= top_k <= min(32,
+ * n_experts); n_experts <= 2048. */
+typedef struct {
+  int32_t d_model;
+  int32_t d_ff;
+  int32_t n_experts;
+  int32_t top_k;
+  int32_t d_ff_shared;
+  int32_t qfmt; /* moe_qfmt */
+} moe_shape;
+
+/* Where the packed experts live.
+ *   routed:        device; routed expert (or slot) i starts at
+ *                  routed + i*expert_stride.  expert_stride must be at least
+ *                  moe_packed_expert_bytes(shape, d_ff) and a multiple of 256.
+ *   slot_of:       device int32 [n_experts] or NULL.  NULL: all n_experts
+ *                  experts are resident, expert e at index e.  Otherwise
+ *                  expert e is at slot slot_of[e] (0 <= slot < n_slots) or not
+ *                  resident (-1) -- the hot-expert cache of the pages ([AF]
+ *                  section "命中率七成，代价是答案会变").
+ *   n_slots:       slots in `routed` when slot_of != NULL.
+ *   shared:        device; the packed shared expert (width d_ff_shared), or
+ *                  NULL when d_ff_shared == 0.  256-byte aligned. */
+typedef struct {
+  const void* routed;
+  size_t expert_stride;
+  const int32_t* slot_of;
+  int32_t n_slots;
+  const void* shared;
+} moe_expert_table;
+
+/* One routed (token, rank) pair whose expert is not resident. */
+typedef struct {
+  int32_t token;
+  int32_t rank;
+  int32_t expert;
+  float gate;
+} moe_miss;
+
+/* Size in bytes of one packed expert of FFN width d_ff under shape->qfmt and
+ * shape->d_model (0 if the shape is invalid). */
+size_t moe_packed_expert_bytes(const moe_shape* shape, int32_t d_ff);
+
+/* Pack n logical experts (layout above) into the packed format.
+ *   codes:  device, n*3*d_ff*d_model bytes (Q2SM: u in 0..3; Q3S: signed q
+ *           in -4..3; only the low 2 resp. 3 bits of u resp. q+4 are used).
+ *   scale:  device fp16 bits, n*3*d_ff*d_model/32.
+ *   min:    device fp16 bits, same size (Q2SM), NULL for Q3S.
+ *   dst:    device; expert i is written at dst + i*dst_stride
+ *           (dst_stride >= moe_packed_expert_bytes, multiple of 256).
+ * Deterministic; the output bytes depend only on the inputs. */
+moe_status moe_pack_weights(const moe_shape* shape, int32_t n, int32_t d_ff,
+                            const void* codes, const uint16_t* scale, const uint16_t* min,
+                            void* dst, size_t dst_stride, moe_stream_t stream);
+
+/* Inverse of moe_pack_weights (padding dropped), for round trips and
+ * inspection.  Q3S codes come back as signed q; min is not written for Q3S
+ * (may be NULL). */
+moe_status moe_unpack_weights(const moe_shape* shape, int32_t n, int32_t d_ff,
+                              const void* src, size_t src_stride,
+                              void* codes, uint16_t* scale, uint16_t* min,
+                              moe_stream_t stream);
+
+/* Workspace bytes moe_layer_forward needs for `tokens` tokens. */
+size_t moe_workspace_bytes(const moe_shape* shape, int32_t tokens);
+
+/* One MoE FFN layer.
+ *   tokens:        T >= 0 (T == 0: nothing is launched, *miss_count is not
+ *                  touched).
+ *   x:             device [T][d_model], dtype x_dtype (MOE_BF16 or MOE_F32).
+ *   flags:         0 or MOE_FLAG_RMSNORM_INPUT.
+ *   router_logits: device fp32 [T][n_experts]; must be finite.
+ *   table:         where the experts are (see moe_expert_table).
+ *   out:           device [T][d_model], dtype out_dtype.  Written in full.
+ *                  Without a slot table: the layer output.  With one: the
+ *                  partial output -- the shared expert plus every pair whose
+ *                  expert is resident, weighted by the full top-k gates.
+ *   miss, miss_cap, miss_count: used only when table->slot_of != NULL
+ *                  (then all three are required): device array of capacity
+ *                  miss_cap >= T*top_k (else MOE_ENOSPACE), receiving every
+ *                  non-resident pair in (token, rank) order, and a device
+ *                  int32 receiving their number.  partial + sum over misses
+ *                  of gate * FFN_expert(x_token) is the whole layer.
+ *   ws, ws_bytes:  device workspace, ws_bytes >= moe_workspace_bytes(shape,
+ *                  T), 256-byte aligned.
+ * Paths: T <= 4 runs the decode path (dequantising MFMA GEMV that streams
+ * each distinct selected expert once); larger T runs the prefill path
+ * (routing, stable token permutation, grouped MFMA GEMM, combine).  The
+ * prefill path supports MOE_Q2SM32 only (MOE_EUNSUPPORTED otherwise).
+ * Results are deterministic: the same inputs give the same output bits. */
+moe_status moe_layer_forward(const moe_shape* shape, int32_t tokens,
+                             const void* x, int32_t x_dtype, uint32_t flags,
+                             const float* router_logits, const moe_expert_table* table,
+                             void* out, int32_t out_dtype,
+                             moe_miss* miss, int32_t miss_cap, int32_t* miss_count,
+                             void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/* Resident-expert slot table (the GPU hot-expert cache of the pages, [AF]
+ * section "命中率七成，代价是答案会变"; [JD] section "为什么从 18t/s 变成
+ * 60-90t/s").  The caller owns all arrays; the host mirror lets updates be
+ * validated without reading device memory. */
+typedef struct {
+  int32_t n_experts;
+  int32_t n_slots;
+  int32_t* slot_of;              /* device [n_experts], -1 = not resident */
+  int32_t* expert_of_slot;       /* device [n_slots], -1 = empty */
+  int32_t* host_slot_of;         /* host mirror of slot_of */
+  int32_t* host_expert_of_slot;  /* host mirror of expert_of_slot */
+  void* storage;                 /* device [n_slots][stride] packed experts */
+  size_t stride;                 /* bytes per slot, multiple of 256 */
+  size_t expert_bytes;           /* bytes copied per install (<= stride) */
+} moe_slot_table;
+
+/* Mark every slot empty and every expert non-resident (device arrays and
+ * host mirror). */
+moe_status moe_slot_table_init(moe_slot_table* t, moe_stream_t stream);
+
+/* Install or evict n experts.  For each i: slots[i] is the slot to change;
+ * experts[i] >= 0 installs that expert there (copying expert_bytes from
+ * src[i], a device or pinned-host pointer, into the slot, and evicting the
+ * slot's previous occupant); experts[i] == -1 only evicts.  `slots`,
+ * `experts` and `src` are host arrays.  Rejected with MOE_EINVAL (nothing
+ * changed): an id out of range, a slot named twice, an expert named twice,
+ * an expert that is already resident in a slot this call does not change,
+ * a NULL src for an install.  Copies and map edits are ordered on the
+ * stream, so a later moe_layer_forward on the same stream sees them; the
+ * host mirror is updated before return. */
+moe_status moe_slot_table_update(moe_slot_table* t, int32_t n, const int32_t* slots,
+                                 const int32_t* experts, const void* const* src,
+                                 moe_stream_t stream);
+
+/* Routing alone (the first step of the layer): device fp32 logits [T][E] ->
+ * device int32 idx [T][k] and fp32 gates [T][k], as defined above. */
+moe_status moe_route(const float* logits, int32_t tokens, int32_t n_experts, int32_t top_k,
+                     int32_t* idx, float* gate, moe_stream_t stream);
+
+/* Stable token-to-expert permutation of routed pairs p = t*k + j:
+ *   offsets [E+1]: offsets[e] = number of pairs routed to experts < e;
+ *   sorted_pairs [T*k]: pair ids grouped by expert, ascending within a group;
+ *   inv [T*k]: inv[p] = position of p in sorted_pairs.
+ * All device int32.  ws: moe_permute_workspace_bytes(T, k, E) bytes. */
+size_t moe_permute_workspace_bytes(int32_t tokens, int32_t top_k, int32_t n_experts);
+moe_status moe_permute(const int32_t* idx, int32_t tokens, int32_t top_k, int32_t n_experts,
+                       int32_t* offsets, int32_t* sorted_pairs, int32_t* inv,
+                       void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/* The calling thread's message for its last failed call ("" if none). */
+const char* moe_last_error(void);
+
+/* ABI version of this header. */
+#define MOE_ABI_VERSION 1
+int32_t moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

@@ -1,0 +1,55 @@
+"""Shared test helpers: oracle-side weights, comparisons and tensor conversions."""
+from __future__ import annotations
+
+import os
+import re
+
+import numpy as np
+
+import synth
+from oracle import moe_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+RTOL_L2 = 5e-3          # relative L2 bar of the layer outputs
+GATE_ATOL = 2e-6        # gates: fp32 GPU vs fp64 oracle
+
+
+def rel_l2(got, ref) -> float:
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+
+
+class OracleWeights:
+    """Dequantised float64 expert matrices, regenerated on the host and cached."""
+
+    def __init__(self, seed, layer, d_model, d_ff, d_ff_shared, n_experts, fmt):
+        self.a = (seed, layer, d_model, d_ff, d_ff_shared, n_experts, fmt)
+        self.cache = {}
+
+    def __call__(self, e):
+        seed, layer, D, F, Fs, E, fmt = self.a
+        if e not in self.cache:
+            f = Fs if e == E else F
+            c, s, m = synth.expert_weights(seed, layer, e, D, f, fmt)
+            self.cache[e] = O.expert_matrices(c, s, m, D, f, fmt)
+        return self.cache[e]
+
+    @property
+    def shared(self):
+        return self(self.a[5])
+
+
+def header_functions():
+    """Function names declared in include/moe.h."""
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", src)))
+
+
+def ensure_built():
+    lib = os.path.join(ROOT, "bit_expert_ffn_router_amd", "libmoe.so")
+    syn = os.path.join(ROOT, "synth", "libmoe_synth.so")
+    if not (os.path.exists(lib) and os.path.exists(syn)):
+        from bit_expert_ffn_router_amd.build import build
+        build()
