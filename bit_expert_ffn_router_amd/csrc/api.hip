@@ -164,8 +164,8 @@ moe_status moe_layer_forward(const moe_shape* shape, int32_t tokens, const void*
   const size_t need_ws = forward_ws_bytes(shape, T);
   if (ws_bytes < need_ws) return fail(MOE_ENOSPACE, "ws_bytes %zu < %zu", ws_bytes, need_ws);
   if (use_decode_path(T)) {
-    if (shape->d_model > 4096 || shape->d_ff > 1024 || shape->d_ff_shared > 1024)
-      return fail(MOE_EUNSUPPORTED, "decode path supports d_model <= 4096, d_ff <= 1024");
+    if (shape->d_model > 4096 || shape->d_ff > 512 || shape->d_ff_shared > 512)
+      return fail(MOE_EUNSUPPORTED, "decode path supports d_model <= 4096, d_ff <= 512");
     moe::DecodeArgs a;
     a.T = T;
     a.D = shape->d_model;

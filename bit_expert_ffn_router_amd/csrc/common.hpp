@@ -27,11 +27,14 @@ __host__ __device__ inline size_t packed_bytes(int D, int F, int fmt) {
   return down_offset(D, F, fmt) + (size_t)(D / 16) * octets(F) * rec_bytes(fmt);
 }
 
-// D = (A & M) | C with all three operands in VGPRs (gfx9 VOP3 takes no literal).
+// D = (A & M) | C.  Written in plain C so that the compiler emits (and
+// tracks hazards for) v_and_or_b32 itself; M and C arrive in VGPRs (see
+// dq_consts), so no literal operand blocks the fused form.  Inline asm is
+// avoided on purpose: the hazard recognizer does not see through it, and an
+// asm write to a register still owned by an in-flight MFMA result gets
+// overwritten when the MFMA retires.
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
-  uint32_t d;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(m), "v"(c));
-  return d;
+  return (a & m) | c;
 }
 
 // 16x16x32 bf16 MFMA: D = A(16x32) * B(32x16) + C.  Lane l holds A[l%16][8*(l/16)+0..7],

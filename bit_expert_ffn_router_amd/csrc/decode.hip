@@ -35,7 +35,7 @@ namespace {
 constexpr int kGuWaves = 8;      // gate/up block: 2 h-groups x {gate, up} x 2 K halves
 constexpr int kDnWaves = 16;     // down block: waves share the expert list
 constexpr int kMaxOctPerWave = 8;  // d_model <= 4096 on the decode path
-constexpr int kMaxDecodeFOct = 4;  // d_ff, d_ff_shared <= 1024 on the decode path
+constexpr int kMaxDecodeFOct = 2;  // d_ff, d_ff_shared <= 512 on the decode path
 
 __host__ __device__ inline size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
@@ -509,34 +509,37 @@ __global__ __launch_bounds__(1024) void decode_down_kernel(DecodeArgs a, DecodeW
 }
 
 // ----------------------------------------------------------------------------
-// Allow a kernel to use more than the default 64 KiB of dynamic LDS (gfx950
-// has 160 KiB per CU).  Set once per kernel instantiation.
+// Raise a kernel's dynamic-LDS limit when a launch needs more than the
+// default 64 KiB (gfx950 has 160 KiB per CU).  `cur` caches the value set.
 template <typename K>
-static hipError_t allow_lds(K kernel, bool& done) {
-  if (done) return hipSuccess;
+static hipError_t allow_lds(K kernel, size_t bytes, size_t& cur) {
+  if (bytes <= 65536 || bytes <= cur) return hipSuccess;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-  done = e == hipSuccess;
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess) cur = bytes;
   return e;
 }
 
 template <int T, int FMT>
 static hipError_t launch_decode_t(const DecodeArgs& a, const DecodeWs& w, hipStream_t st) {
-  static bool lds_gu_lo = false, lds_gu = false, lds_dn = false;
+  static size_t lds_gu_lo = 0, lds_gu = 0, lds_dn = 0;
+  const bool has_lo = !a.x_bf16 && !a.rmsnorm;
+  const size_t lds = (size_t)T * a.D * 2 * (has_lo ? 2 : 1) + (size_t)T * (a.D / 32) * 8;
+  const size_t lds_down = (size_t)kDnWaves * T * 2 * w.Fp * 2;
   hipError_t e;
-  if ((e = allow_lds(decode_gateup_kernel<T, FMT, true>, lds_gu_lo)) != hipSuccess) return e;
-  if ((e = allow_lds(decode_gateup_kernel<T, FMT, false>, lds_gu)) != hipSuccess) return e;
-  if ((e = allow_lds(decode_down_kernel<T, FMT>, lds_dn)) != hipSuccess) return e;
+  if (has_lo) {
+    if ((e = allow_lds(decode_gateup_kernel<T, FMT, true>, lds, lds_gu_lo)) != hipSuccess) return e;
+  } else {
+    if ((e = allow_lds(decode_gateup_kernel<T, FMT, false>, lds, lds_gu)) != hipSuccess) return e;
+  }
+  if ((e = allow_lds(decode_down_kernel<T, FMT>, lds_down, lds_dn)) != hipSuccess) return e;
   decode_prep_kernel<T><<<1, 256, 0, st>>>(a, w);
   const int Wr = w.Wmax - 1;
   const int nblk = Wr * (a.F / 32) + (a.shared ? a.Fs / 32 : 0);
-  const bool has_lo = !a.x_bf16 && !a.rmsnorm;
-  const size_t lds = (size_t)T * a.D * 2 * (has_lo ? 2 : 1) + (size_t)T * (a.D / 32) * 8;
   if (has_lo)
     decode_gateup_kernel<T, FMT, true><<<nblk, 512, lds, st>>>(a, w);
   else
     decode_gateup_kernel<T, FMT, false><<<nblk, 512, lds, st>>>(a, w);
-  const size_t lds_down = (size_t)kDnWaves * T * 2 * w.Fp * 2;
   decode_down_kernel<T, FMT><<<a.D / 16, 1024, lds_down, st>>>(a, w);
   return hipGetLastError();
 }
