@@ -1,0 +1,378 @@
+#!/usr/bin/env python3
+"""MoE-layer throughput on one MI355X, with roofline fraction and a CPU-oracle baseline.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads a,b,...] [--no-cpu]
+
+A "step" is one pass of the whole layer path (routing, expert selection or
+permutation, dequantising expert GEMV/GEMM, SwiGLU, combine) over one batch
+of synthetic input.  The primary line is the single-token decode workload
+(1 token x 1 layer, weights rotated over 48 resident layers so that the
+256 MB Infinity Cache cannot hold them); the other workloads are attached
+under "workloads".  The timed steps are captured once into a HIP graph and
+replayed: exactly K steps between two synchronisations.
+
+Workloads (shapes from the pages' model: 48 layers x 512 experts, top-10 +
+one shared expert; d_model 3072, d_ff 512; 2-bit blocks of 32 with fp16
+scale and min, or signed 3-bit blocks with an fp16 scale):
+  decode_t1          1 token x 1 layer, Zipf(1.1)-biased logits
+  mtp_verify_t4_48l  4 tokens (1 + 3 drafts) x 48 chained layers
+  prefill_8192       8192 tokens x 1 layer
+  slot_q3s_t1_48l    1 token x 48 layers, 128 of 512 experts resident per
+                     layer (hit rate about 70 %), misses returned
+
+Output: one JSON line (see the end of main()).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = "MoE-layer tokens/s (decode B=1/4, prefill 8192) + % HBM/MFMA peak"
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps of the primary workload")
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workloads", default="decode_t1,mtp_verify_t4_48l,prefill_8192,slot_q3s_t1_48l")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--no-graph", action="store_true", help="launch steps eagerly")
+    return ap.parse_args()
+
+
+def src_sha(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "bit_expert_ffn_router_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(kernel_key, src_files, bytes_per_launch_alg):
+    """HBM bytes per launch from stored rocprofv3 counter runs, if still current."""
+    p = os.path.join(PROFILES, "pmc_traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        rec = json.load(open(p)).get(kernel_key)
+    except Exception:
+        return None
+    if not rec or rec.get("source_sha") != src_sha(*src_files):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# ----------------------------------------------------------------------------
+class Ctx:
+    def __init__(self):
+        import torch
+        import numpy as np
+        import bit_expert_ffn_router_amd as moe
+        import synth
+        from synth.layers import build_layer, stride_of
+        self.torch, self.np, self.moe, self.synth = torch, np, moe, synth
+        self.build_layer, self.stride_of = build_layer, stride_of
+        self.dev = torch.device("cuda:0")
+
+    def shape(self, w):
+        return self.moe.MoeShape(w["d_model"], w["d_ff"], w["n_experts"], w["top_k"],
+                                 w["d_ff_shared"], w["fmt"])
+
+    def dev_u16(self, a):
+        return self.torch.from_numpy(self.np.ascontiguousarray(a).view(self.np.int16)).to(self.dev)
+
+    def dev_f32(self, a):
+        return self.torch.from_numpy(self.np.ascontiguousarray(a, dtype=self.np.float32)).to(self.dev)
+
+
+def run_steps(ctx, launch, K, W, use_graph, timer_events=None):
+    """Warm up W eager steps, then time exactly K steps.  Returns (seconds, per-kernel ms list)."""
+    torch = ctx.torch
+    for i in range(W):
+        launch(i)
+    torch.cuda.synchronize()
+    evs = None
+    if timer_events:
+        evs = [(torch.cuda.Event(enable_timing=True, external=True),
+                torch.cuda.Event(enable_timing=True, external=True)) for _ in range(K)]
+        for b, a in evs:      # torch creates the HIP event on its first record
+            b.record()
+            a.record()
+        torch.cuda.synchronize()
+    if use_graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(K):
+                if evs:
+                    ctx.moe.moe_set_kernel_timer(*evs[i])
+                launch(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        g.replay()
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+    else:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(K):
+            if evs:
+                ctx.moe.moe_set_kernel_timer(*evs[i])
+            launch(i)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+    kms = [b.elapsed_time(a) for b, a in evs] if evs else None
+    return dt, kms
+
+
+# ----------------------------------------------------------------------------
+def decode_stack(ctx, name, layers_needed):
+    """Build the 48-layer Q2SM stack (shared by the decode workloads)."""
+    w = ctx.synth.WORKLOADS[name]
+    shape = ctx.shape(w)
+    layers = [ctx.build_layer(shape, 0, l, ctx.dev) for l in range(layers_needed)]
+    return w, shape, layers
+
+
+def unique_counts(ctx, shape, logits_dev, T):
+    """Distinct routed experts per layer (from the library's own router)."""
+    torch, moe = ctx.torch, ctx.moe
+    out = []
+    for lg in logits_dev:
+        idx = torch.empty(T * shape.top_k, dtype=torch.int32, device=ctx.dev)
+        gate = torch.empty(T * shape.top_k, dtype=torch.float32, device=ctx.dev)
+        moe.moe_route(lg, T, shape.n_experts, shape.top_k, idx, gate)
+        out.append(len(set(idx.cpu().tolist())))
+    return out
+
+
+def bench_decode_t1(ctx, stack, K, W, use_graph):
+    torch, moe, synth = ctx.torch, ctx.moe, ctx.synth
+    w, shape, layers = stack
+    L, T, D = len(layers), 1, w["d_model"]
+    logits = [ctx.dev_f32(synth.router_logits(0, l, T, w["n_experts"], zipf_s=w["zipf_s"],
+                                              alpha=w["alpha"])) for l in range(L)]
+    xs = [ctx.dev_u16(synth.activations_bf16(0, l, T, D)) for l in range(L)]
+    wsb = moe.moe_workspace_bytes(shape, T)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=ctx.dev)
+    out = torch.empty(T * D, dtype=torch.int16, device=ctx.dev)
+    tables = [ly.table() for ly in layers]
+
+    def launch(i):
+        l = i % L
+        moe.moe_layer_forward(shape, T, xs[l], moe.MOE_BF16, 0, logits[l], tables[l], out,
+                              moe.MOE_BF16, None, 0, None, ws, wsb)
+
+    launch(0)
+    torch.cuda.synchronize()
+    dt, kms = run_steps(ctx, launch, K, W, use_graph, timer_events=True)
+    U = unique_counts(ctx, shape, logits, T)
+    gu_bytes_expert = moe.moe_packed_expert_bytes(shape, w["d_ff"]) * 2 // 3
+    # algorithmic bytes of one gate/up launch: each distinct expert's gate+up
+    # weights once (+ shared), the activations in and h out.
+    bytes_per = [(U[i % L] + 1) * gu_bytes_expert + T * D * 2 + (U[i % L] + 1) * T * w["d_ff"] * 4
+                 for i in range(K)]
+    layer_bytes = [(U[i % L] + 1) * moe.moe_packed_expert_bytes(shape, w["d_ff"]) for i in range(K)]
+    kavg = sum(kms) / len(kms) * 1e-3
+    return dict(tokens=K * T, seconds=dt, kernel_s=kavg, bytes_per_launch=sum(bytes_per) / K,
+                layer_bytes=sum(layer_bytes) / K, unique=sum(U) / len(U))
+
+
+def bench_chain(ctx, stack, K, W, use_graph, T, slot=None):
+    """T tokens through all layers of the stack, chained (RMS input rule)."""
+    torch, moe, synth = ctx.torch, ctx.moe, ctx.synth
+    w, shape, layers = stack
+    L, D = len(layers), w["d_model"]
+    logits = [ctx.dev_f32(synth.router_logits(0, l, T, w["n_experts"], zipf_s=w["zipf_s"],
+                                              alpha=w["alpha"])) for l in range(L)]
+    x0 = ctx.dev_u16(synth.activations_bf16(0, 0, T, D))
+    wsb = moe.moe_workspace_bytes(shape, T)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=ctx.dev)
+    acts = [torch.empty(T * D, dtype=torch.int16, device=ctx.dev) for _ in range(L)]
+    kcap = T * w["top_k"]
+    miss = torch.empty(L * kcap * 4, dtype=torch.int32, device=ctx.dev)
+    mcount = torch.zeros(L, dtype=torch.int32, device=ctx.dev)
+    tables = [ly.table() if slot is None else slot[l] for l, ly in enumerate(layers)]
+
+    def launch(i):
+        for l in range(L):
+            x = x0 if l == 0 else acts[l - 1]
+            fl = 0 if l == 0 else moe.MOE_FLAG_RMSNORM_INPUT
+            if slot is None:
+                moe.moe_layer_forward(shape, T, x, moe.MOE_BF16, fl, logits[l], tables[l], acts[l],
+                                      moe.MOE_BF16, None, 0, None, ws, wsb)
+            else:
+                moe.moe_layer_forward(shape, T, x, moe.MOE_BF16, fl, logits[l], tables[l], acts[l],
+                                      moe.MOE_BF16, miss.data_ptr() + l * kcap * 16, kcap,
+                                      mcount.data_ptr() + 4 * l, ws, wsb)
+
+    launch(0)
+    torch.cuda.synchronize()
+    dt, _ = run_steps(ctx, launch, K, W, use_graph)
+    res = dict(tokens=K * T, seconds=dt)
+    if slot is not None:
+        res["misses_per_layer"] = float(mcount.float().mean().item())
+        res["hit_rate"] = 1.0 - res["misses_per_layer"] / w["top_k"] / T
+    return res
+
+
+def build_slot_stack(ctx, name):
+    torch, moe, synth, np = ctx.torch, ctx.moe, ctx.synth, ctx.np
+    w = synth.WORKLOADS[name]
+    shape = ctx.shape(w)
+    E, S = w["n_experts"], w["n_slots"]
+    tables, keep = [], []
+    for l in range(w["layers"]):
+        ranks = synth.expert_ranks(0, l, E)
+        resident = [int(e) for e in np.argsort(ranks)[:S]]          # the S most popular
+        staged = ctx.build_layer(shape, 0, l, ctx.dev, experts=resident)
+        stride = staged.stride
+        slot_of = torch.empty(E, dtype=torch.int32, device=ctx.dev)
+        eos = torch.empty(S, dtype=torch.int32, device=ctx.dev)
+        hs, he = np.empty(E, np.int32), np.empty(S, np.int32)
+        storage = torch.empty(S * stride, dtype=torch.uint8, device=ctx.dev)
+        t = moe.MoeSlotTable(E, S, slot_of.data_ptr(), eos.data_ptr(), hs.ctypes.data,
+                             he.ctypes.data, storage.data_ptr(), stride,
+                             moe.moe_packed_expert_bytes(shape, w["d_ff"]))
+        moe.moe_slot_table_init(t)
+        for i0 in range(0, S, 32):
+            moe.moe_slot_table_update(t, list(range(i0, i0 + 32)), resident[i0:i0 + 32],
+                                      [staged.routed.data_ptr() + i * stride for i in range(i0, i0 + 32)])
+        torch.cuda.synchronize()
+        del staged.routed
+        keep.append((slot_of, eos, hs, he, storage, staged))
+        tables.append(moe.MoeExpertTable(storage.data_ptr(), stride, slot_of.data_ptr(), S,
+                                         staged.shared.data_ptr()))
+    layers = [k[5] for k in keep]
+    return (w, shape, layers), tables, keep
+
+
+# ----------------------------------------------------------------------------
+def cpu_baseline_decode(budget_s=15.0):
+    """The fp64 oracle on single-token, single-layer decode: a bounded sample."""
+    import numpy as np
+    import synth
+    from oracle import moe_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count()
+    w = synth.WORKLOADS["decode_t1"]
+    D, F, E, k = w["d_model"], w["d_ff"], w["n_experts"], w["top_k"]
+    done, t_compute = 0, 0.0
+    for l in range(48):
+        lg = synth.router_logits(0, l, 1, E, zipf_s=w["zipf_s"], alpha=w["alpha"])
+        x = O.bf16_to_f64(synth.activations_bf16(0, l, 1, D))
+        idx, _ = O.route(lg, k)
+        logical = {e: synth.expert_weights(0, l, e, D, F, 1) for e in list(idx[0]) + [E]}
+        t0 = time.perf_counter()
+        mats = {e: O.expert_matrices(c, s, m, D, F, 1) for e, (c, s, m) in logical.items()}
+        O.layer_forward(x, lg, k, lambda e: mats[e], mats[E])
+        t_compute += time.perf_counter() - t0
+        done += 1
+        if t_compute > budget_s:
+            break
+    return dict(value=done / t_compute, unit="tokens/s", cores=int(cores), kind="oracle",
+                sample="%d single-token layer passes (layers 0..%d of the decode stack), "
+                       "fp64 numpy: dequantisation of the 11 touched experts + routing + SwiGLU "
+                       "FFNs; weight generation not timed" % (done, done - 1))
+
+
+# ----------------------------------------------------------------------------
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    wl = [s for s in args.workloads.split(",") if s]
+    use_graph = not args.no_graph
+    ctx = Ctx()
+    torch, moe = ctx.torch, ctx.moe
+    K = args.steps if args.steps is not None else 960
+    W = args.warmup if args.warmup is not None else 48
+    results = {}
+
+    stack = None
+    if "decode_t1" in wl or "mtp_verify_t4_48l" in wl:
+        t0 = time.perf_counter()
+        stack = decode_stack(ctx, "mtp_verify_t4_48l", 48)
+        print("built 48-layer Q2SM stack in %.1fs" % (time.perf_counter() - t0), file=sys.stderr,
+              flush=True)
+    prim = None
+    if "decode_t1" in wl:
+        r = bench_decode_t1(ctx, stack, K, W, use_graph)
+        prim = r
+        print("decode_t1: %.1f us/step, gate/up kernel %.2f us" %
+              (r["seconds"] / K * 1e6, r["kernel_s"] * 1e6), file=sys.stderr, flush=True)
+    if "mtp_verify_t4_48l" in wl:
+        Kc = max(1, K // 48)
+        r = bench_chain(ctx, stack, Kc, 2, use_graph, T=4)
+        results["mtp_verify_t4_48l"] = dict(
+            value=r["tokens"] / r["seconds"], unit="tokens/s", steps=Kc,
+            ms_per_step=r["seconds"] / Kc * 1e3,
+            config="4 tokens x 48 chained layers (RMS input rule), Q2SM, 43.6 GB resident")
+        print("mtp_verify_t4_48l: %.3f ms/step" % (r["seconds"] / Kc * 1e3), file=sys.stderr,
+              flush=True)
+    if stack is not None:
+        del stack
+        torch.cuda.empty_cache()
+    if "slot_q3s_t1_48l" in wl:
+        sstack, tables, keep = build_slot_stack(ctx, "slot_q3s_t1_48l")
+        Kc = max(1, K // 48)
+        r = bench_chain(ctx, sstack, Kc, 2, use_graph, T=1, slot=tables)
+        results["slot_q3s_t1_48l"] = dict(
+            value=r["tokens"] / r["seconds"], unit="tokens/s", steps=Kc,
+            ms_per_step=r["seconds"] / Kc * 1e3, hit_rate=r["hit_rate"],
+            config="1 token x 48 chained layers, Q3S, 128/512 experts resident per layer")
+        print("slot_q3s_t1_48l: %.3f ms/step hit %.3f" % (r["seconds"] / Kc * 1e3, r["hit_rate"]),
+              file=sys.stderr, flush=True)
+        del keep, tables, sstack
+        torch.cuda.empty_cache()
+    if "prefill_8192" in wl:
+        results["prefill_8192"] = dict(value=None, unit="tokens/s",
+                                       note="prefill path not built in this version")
+
+    line = {
+        "metric": METRIC, "value": None, "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": W, "ms_per_step": None, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "decode_t1: 1 token x 1 MoE layer (d_model 3072, d_ff 512, "
+                               "512 routed experts, top-10 + 1 shared, Q2SM 2-bit blocks of 32 "
+                               "with fp16 scale+min), layer weights rotated over 48 resident "
+                               "layers (43.6 GB)",
+                   "graph_replay": use_graph},
+    }
+    if prim is not None:
+        line["value"] = prim["tokens"] / prim["seconds"]
+        line["ms_per_step"] = prim["seconds"] / K * 1e3
+        achieved = prim["bytes_per_launch"] / prim["kernel_s"] / 1e9
+        line["roofline"] = {
+            "bound": "hbm", "kernel": "decode_gateup_kernel (dequantising MFMA GEMV + SwiGLU)",
+            "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic_from_profile("decode_gateup_t1", ["decode.hip", "common.hpp"],
+                                            prim["bytes_per_launch"]),
+            "bytes_per_launch": prim["bytes_per_launch"],
+            "kernel_us": prim["kernel_s"] * 1e6,
+        }
+        line["layer_hbm_frac"] = prim["layer_bytes"] / (prim["seconds"] / K) / 1e9 / HBM_PEAK_GBS
+    if not args.no_cpu and prim is not None:
+        line["cpu_baseline"] = cpu_baseline_decode()
+    line["workloads"] = results
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,7 +1,7 @@
 """Python binding of libmoe, the MI355X routed low-bit MoE FFN layer.
 
 Argument marshalling only: every step of the layer runs in the HIP kernels
-of ``libmoe.so`` (built in-tree by ``python -m bit_expert_ffn_router_amd.build``).
+of ``libmoe.so`` (built in-tree by ``python bit_expert_ffn_router_amd/build.py``).
 PyTorch is used for device memory and streams.  The functions keep the names
 and argument order of the C ABI in ``include/moe.h``; buffers may be torch
 tensors (their ``data_ptr()`` is passed) or raw integer addresses, and
@@ -22,7 +22,7 @@ __all__ = [
     "moe_packed_expert_bytes", "moe_pack_weights", "moe_unpack_weights",
     "moe_workspace_bytes", "moe_layer_forward", "moe_slot_table_init",
     "moe_slot_table_update", "moe_route", "moe_permute_workspace_bytes", "moe_permute",
-    "moe_last_error", "moe_abi_version", "LIB_PATH",
+    "moe_last_error", "moe_abi_version", "moe_set_kernel_timer", "LIB_PATH",
 ]
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EHIP, MOE_ENOSPACE = 0, -1, -2, -3, -4
@@ -34,7 +34,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        "libmoe.so is not built (%s); run `python -m bit_expert_ffn_router_amd.build` "
+        "libmoe.so is not built (%s); run `python bit_expert_ffn_router_amd/build.py` "
         "(hipcc, gfx950)" % LIB_PATH)
 
 _lib = ctypes.CDLL(LIB_PATH)
@@ -88,6 +88,7 @@ _sigs = {
     "moe_route": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "moe_permute_workspace_bytes": (_Z, [_I, _I, _I]),
     "moe_permute": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _Z, _P]),
+    "moe_set_kernel_timer": (_I, [_P, _P]),
 }
 for _name, (_res, _args) in _sigs.items():
     _f = getattr(_lib, _name)
@@ -180,3 +181,16 @@ def moe_permute(idx, tokens, top_k, n_experts, offsets, sorted_pairs, inv, ws, w
                 stream=None):
     _check(_lib.moe_permute(_ptr(idx), tokens, top_k, n_experts, _ptr(offsets),
                             _ptr(sorted_pairs), _ptr(inv), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def moe_set_kernel_timer(before, after):
+    """Time the dominant kernel of this thread's next forward call.
+
+    before/after: torch.cuda.Event(enable_timing=True) objects (their raw
+    handles are passed), raw hipEvent_t addresses, or None, None.
+    """
+    def h(ev):
+        if ev is None or isinstance(ev, int):
+            return ev
+        return ev.cuda_event
+    _check(_lib.moe_set_kernel_timer(h(before), h(after)))

@@ -1,6 +1,8 @@
 """Build the HIP libraries in-tree for gfx950.
 
-    python -m bit_expert_ffn_router_amd.build
+    python bit_expert_ffn_router_amd/build.py
+
+(Run it by path: importing the package loads the library it builds.)
 
 Produces bit_expert_ffn_router_amd/libmoe.so (the layer) and
 synth/libmoe_synth.so (the device side of the seeded input generator).

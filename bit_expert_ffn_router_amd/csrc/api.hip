@@ -64,9 +64,36 @@ size_t forward_ws_bytes(const moe_shape* s, int T) {
 
 }  // namespace
 
+namespace moe {
+
+KernelTimer& kernel_timer() {
+  thread_local KernelTimer t;
+  return t;
+}
+
+hipError_t record_timer_event(hipEvent_t ev, hipStream_t st) {
+  if (!ev) return hipSuccess;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(st, &cs);
+  if (e != hipSuccess) return e;
+  return hipEventRecordWithFlags(ev, st,
+                                 cs == hipStreamCaptureStatusActive ? hipEventRecordExternal
+                                                                    : hipEventRecordDefault);
+}
+
+}  // namespace moe
+
 extern "C" {
 
 int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+moe_status moe_set_kernel_timer(void* before, void* after) {
+  if ((before == nullptr) != (after == nullptr))
+    return fail(MOE_EINVAL, "before and after must both be set or both be NULL");
+  moe::kernel_timer().before = (hipEvent_t)before;
+  moe::kernel_timer().after = (hipEvent_t)after;
+  return ok();
+}
 
 const char* moe_last_error(void) { return g_err; }
 

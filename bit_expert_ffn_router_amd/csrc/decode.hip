@@ -536,10 +536,14 @@ static hipError_t launch_decode_t(const DecodeArgs& a, const DecodeWs& w, hipStr
   decode_prep_kernel<T><<<1, 256, 0, st>>>(a, w);
   const int Wr = w.Wmax - 1;
   const int nblk = Wr * (a.F / 32) + (a.shared ? a.Fs / 32 : 0);
+  KernelTimer& tm = kernel_timer();
+  if ((e = record_timer_event(tm.before, st)) != hipSuccess) return e;
   if (has_lo)
     decode_gateup_kernel<T, FMT, true><<<nblk, 512, lds, st>>>(a, w);
   else
     decode_gateup_kernel<T, FMT, false><<<nblk, 512, lds, st>>>(a, w);
+  if ((e = record_timer_event(tm.after, st)) != hipSuccess) return e;
+  tm.before = tm.after = nullptr;
   decode_down_kernel<T, FMT><<<a.D / 16, 1024, lds_down, st>>>(a, w);
   return hipGetLastError();
 }

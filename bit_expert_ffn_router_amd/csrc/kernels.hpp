@@ -11,6 +11,15 @@ struct MissRec {
   float gate;
 };
 
+// ---------------------------------------------------------------- timing hook
+// Events set by moe_set_kernel_timer, consumed by the next forward call.
+struct KernelTimer {
+  hipEvent_t before = nullptr, after = nullptr;
+};
+KernelTimer& kernel_timer();
+// Record ev on st (as an external node when st is capturing); no-op for NULL.
+hipError_t record_timer_event(hipEvent_t ev, hipStream_t st);
+
 // ---------------------------------------------------------------- packing
 hipError_t launch_pack(int fmt, int D, int F, int n, const void* codes, const uint16_t* scale,
                        const uint16_t* mins, void* dst, size_t dst_stride, hipStream_t st);

@@ -256,6 +256,16 @@ moe_status moe_permute(const int32_t* idx, int32_t tokens, int32_t top_k, int32_
                        int32_t* offsets, int32_t* sorted_pairs, int32_t* inv,
                        void* ws, size_t ws_bytes, moe_stream_t stream);
 
+/* Profiling aid: time the dominant kernel of the calling thread's next
+ * moe_layer_forward call.  `before` and `after` are hipEvent_t handles
+ * created by the caller with timing enabled; the call records `before` on
+ * its stream just before launching the dominant kernel (decode path: the
+ * gate/up GEMV; prefill path: the gate/up grouped GEMM) and `after` just
+ * after it, then forgets both.  Under stream capture the records become
+ * external event nodes of the graph.  NULL, NULL clears a pending pair.
+ * Thread-local; no device work is done by this call itself. */
+moe_status moe_set_kernel_timer(void* before, void* after);
+
 /* The calling thread's message for its last failed call ("" if none). */
 const char* moe_last_error(void);
 

@@ -15,7 +15,7 @@ from . import tables, FMT_Q2SM
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_synth.so")
 if not os.path.exists(LIB_PATH):
-    raise ImportError("libmoe_synth.so is not built; run `python -m bit_expert_ffn_router_amd.build`")
+    raise ImportError("libmoe_synth.so is not built; run `python bit_expert_ffn_router_amd/build.py`")
 _lib = ctypes.CDLL(LIB_PATH)
 _lib.synth_fill_expert_weights.restype = ctypes.c_int
 _lib.synth_fill_expert_weights.argtypes = [

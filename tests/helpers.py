@@ -51,5 +51,5 @@ def ensure_built():
     lib = os.path.join(ROOT, "bit_expert_ffn_router_amd", "libmoe.so")
     syn = os.path.join(ROOT, "synth", "libmoe_synth.so")
     if not (os.path.exists(lib) and os.path.exists(syn)):
-        from bit_expert_ffn_router_amd.build import build
-        build()
+        import runpy
+        runpy.run_path(os.path.join(ROOT, "bit_expert_ffn_router_amd", "build.py"))["build"]()
