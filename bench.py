@@ -96,42 +96,88 @@ class Ctx:
         return self.torch.from_numpy(self.np.ascontiguousarray(a, dtype=self.np.float32)).to(self.dev)
 
 
-def run_steps(ctx, launch, K, W, use_graph, timer_events=None):
-    """Warm up W eager steps, then time exactly K steps.  Returns (seconds, per-kernel ms list)."""
+class HipEvents:
+    """Raw hipEvent_t pairs (torch's events cannot be external nodes on ROCm)."""
+
+    def __init__(self, n):
+        import ctypes
+        self.ct = ctypes
+        lib = ctypes.CDLL("libamdhip64.so")
+        lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        lib.hipEventCreate.restype = ctypes.c_int
+        lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                            ctypes.c_void_p]
+        lib.hipEventElapsedTime.restype = ctypes.c_int
+        lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.lib = lib
+        self.pairs = []
+        for _ in range(n):
+            b, a = ctypes.c_void_p(), ctypes.c_void_p()
+            if lib.hipEventCreate(ctypes.byref(b)) or lib.hipEventCreate(ctypes.byref(a)):
+                raise RuntimeError("hipEventCreate failed")
+            self.pairs.append((b.value, a.value))
+
+    def elapsed_ms(self):
+        out = []
+        for b, a in self.pairs:
+            ms = self.ct.c_float()
+            rc = self.lib.hipEventElapsedTime(self.ct.byref(ms), b, a)
+            if rc:
+                raise RuntimeError("hipEventElapsedTime failed (%d)" % rc)
+            out.append(ms.value)
+        return out
+
+    def close(self):
+        for b, a in self.pairs:
+            self.lib.hipEventDestroy(b)
+            self.lib.hipEventDestroy(a)
+        self.pairs = []
+
+
+def run_steps(ctx, launch, K, W, use_graph, timer_events=False):
+    """Warm up W eager steps, then time exactly K steps.
+
+    The timed region replays the K steps captured into one HIP graph (or
+    launches them eagerly with use_graph=False), bracketed by synchronisations.
+    With timer_events, a second pass launches the same K steps eagerly with
+    the library recording a HIP event pair around its dominant kernel in
+    each step; that pass is queued behind a device-side spin so the GPU runs
+    the steps back to back and the events do not include host launch gaps.
+    Returns (seconds of the timed region, per-step dominant-kernel ms or None).
+    """
     torch = ctx.torch
     for i in range(W):
         launch(i)
     torch.cuda.synchronize()
-    evs = None
-    if timer_events:
-        evs = [(torch.cuda.Event(enable_timing=True, external=True),
-                torch.cuda.Event(enable_timing=True, external=True)) for _ in range(K)]
-        for b, a in evs:      # torch creates the HIP event on its first record
-            b.record()
-            a.record()
-        torch.cuda.synchronize()
     if use_graph:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for i in range(K):
-                if evs:
-                    ctx.moe.moe_set_kernel_timer(*evs[i])
                 launch(i)
+        g.replay()                      # one untimed replay (first-touch of graph resources)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         g.replay()
         torch.cuda.synchronize()
         dt = time.perf_counter() - t0
+        del g
     else:
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(K):
-            if evs:
-                ctx.moe.moe_set_kernel_timer(*evs[i])
             launch(i)
         torch.cuda.synchronize()
         dt = time.perf_counter() - t0
-    kms = [b.elapsed_time(a) for b, a in evs] if evs else None
+    kms = None
+    if timer_events:
+        evs = HipEvents(K)
+        torch.cuda._sleep(int(2.0e5 * K))     # ~ tens of microseconds of GPU spin per step
+        for i in range(K):
+            ctx.moe.moe_set_kernel_timer(*evs.pairs[i])
+            launch(i)
+        torch.cuda.synchronize()
+        kms = evs.elapsed_ms()
+        evs.close()
     return dt, kms
 
 

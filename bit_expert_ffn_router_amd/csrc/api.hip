@@ -208,6 +208,7 @@ moe_status moe_layer_forward(const moe_shape* shape, int32_t tokens, const void*
     a.routed = (const uint8_t*)table->routed;
     a.stride = table->expert_stride;
     a.slot_of = table->slot_of;
+    a.n_slots = table->n_slots;
     a.shared = (const uint8_t*)table->shared;
     a.out = out;
     a.out_bf16 = out_dtype == MOE_BF16;

@@ -11,31 +11,38 @@
 // "命中率七成，代价是答案会变").  So the kernels stream each distinct selected
 // expert's packed bytes exactly once for all tokens that chose it.
 //
-// Three launches:
-//   decode_prep:    top-k + gates per token, the list of distinct resident
-//                   experts (first-occurrence order) with per-token gates,
-//                   the miss list, and the bf16 activation operand with its
-//                   per-block sums.
-//   decode_gateup:  one block per (expert, 32 FFN rows): dequantising MFMA
-//                   GEMV of W_gate and W_up, SwiGLU, h in bf16 hi + lo.
+// Two launches:
+//   decode_gateup:  one block per (listed expert, 16 FFN rows).  Every block
+//                   first routes the tokens itself (top-k + gates, the list of
+//                   distinct resident experts in first-occurrence order, the
+//                   miss list) while its other waves stage the activations in
+//                   LDS; block 0 publishes the list for the second kernel.
+//                   Then: dequantising MFMA GEMV of W_gate and W_up, SwiGLU,
+//                   h in bf16 hi + lo with per-block sums.
 //   decode_down:    one block per 16 output rows: W_down GEMV of every listed
 //                   expert, gate-weighted sum in a fixed order, output write.
 //
 // Dequantisation (see DqConsts): a code word is turned into bf16 operands
-// (c + u) with two VALU ops per pair of weights and no conversion; the MFMA
-// sums (c + u) * x over one 32-weight block; the block result is scaled by
-// the fp16 block scale, and the constant parts (c * x, and the block min
-// times sum x) are subtracted/added from per-block activation sums.
+// (c + u) with one VALU op per pair of weights plus shared shifts and no
+// conversion; the MFMA sums (c + u) * x over one 32-weight block; the block
+// result is scaled by the fp16 block scale, and the constant parts (c * x,
+// and the block min times sum x) come from per-block activation sums.
 #include "route_common.hpp"
 
 namespace moe {
 
 namespace {
 
-constexpr int kGuWaves = 8;      // gate/up block: 2 h-groups x {gate, up} x 2 K halves
-constexpr int kDnWaves = 16;     // down block: waves share the expert list
-constexpr int kMaxOctPerWave = 8;  // d_model <= 4096 on the decode path
+constexpr int kGuWaves = 4;        // gate/up block: {gate, up} x 2 K halves, 16 FFN rows
+constexpr int kGuThreads = 64 * kGuWaves;
+constexpr int kDnWaves = 16;       // down block: waves share the expert list
+constexpr int kMaxOctPerWave = 8;  // d_model <= 4096 on the decode path (16 octets / 2 halves)
 constexpr int kMaxDecodeFOct = 2;  // d_ff, d_ff_shared <= 512 on the decode path
+
+// Activation modes of the gate/up kernel.
+constexpr int kXBf16 = 0;  // bf16 input, used as is
+constexpr int kXF32 = 1;   // fp32 input, as bf16 hi + bf16 lo (two MFMAs)
+constexpr int kXRms = 2;   // input normalised to bf16(x / sqrt(mean(x^2) + 1e-6))
 
 __host__ __device__ inline size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
@@ -49,10 +56,8 @@ size_t decode_ws_bytes(int T, int D, int F, int Fs, int E, int k) {
   b += 256;                                           // nwork
   b += align256(4 * (size_t)Wmax);                    // work_ref
   b += align256(16 * (size_t)Wmax);                   // work_gate
-  b += align256(2 * (size_t)T * D) * 2;               // xa_hi, xa_lo
-  b += align256(8 * (size_t)T * (D / 32));            // xs
   b += align256(2 * (size_t)Wmax * T * Fp) * 2;       // hh, hl
-  b += align256(8 * (size_t)Wmax * T * (Fp / 32));    // hs
+  b += align256(16 * (size_t)Wmax * T * (Fp / 32));   // hs
   return b;
 }
 
@@ -67,142 +72,129 @@ DecodeWs decode_ws_carve(void* ws, int T, int D, int F, int Fs, int E, int k) {
   w.nwork = (int32_t*)take(4);
   w.work_ref = (int32_t*)take(4 * (size_t)w.Wmax);
   w.work_gate = (float*)take(16 * (size_t)w.Wmax);
-  w.xa_hi = (uint16_t*)take(2 * (size_t)T * D);
-  w.xa_lo = (uint16_t*)take(2 * (size_t)T * D);
-  w.xs = (float2*)take(8 * (size_t)T * (D / 32));
   w.hh = (uint16_t*)take(2 * (size_t)w.Wmax * T * w.Fp);
   w.hl = (uint16_t*)take(2 * (size_t)w.Wmax * T * w.Fp);
-  w.hs = (float2*)take(8 * (size_t)w.Wmax * T * (w.Fp / 32));
+  w.hs = (float2*)take(16 * (size_t)w.Wmax * T * (w.Fp / 32));
   return w;
 }
 
 // ----------------------------------------------------------------------------
-// decode_prep: one block of 256 threads.
+// Routing inside a decode block.  Waves 0..T-1 route one token each; then
+// wave 0 builds the list of distinct resident experts in (token, rank) order
+// of first occurrence with their per-token gates, and the miss list.  Every
+// block computes the same list; block 0 also publishes it (and the misses).
+struct RouteLds {
+  key64* scr;  // T regions of topk_scratch_bytes(E, k) in dynamic LDS
+  int32_t e[kDecodeMaxT * kMaxTopK];
+  float g[kDecodeMaxT * kMaxTopK];
+  int32_t ref[kDecodeMaxT * kMaxTopK + 1];
+  float wg[(kDecodeMaxT * kMaxTopK + 1) * 4];
+  int32_t nu;
+};
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ void decode_route_token(const DecodeArgs& a, RouteLds& R, int t,
+                                                   int lane) {
+  int my_e;
+  float my_l;
+  wave_topk_any(a.logits + (size_t)t * a.E, a.E, a.k, lane, my_e, my_l,
+                R.scr + t * (topk_scratch_bytes(a.E, a.k) / 8));
+  const float g = wave_gate(my_l, a.k, lane);
+  if (lane < a.k) {
+    // never let an id outside 0..E-1 become an address (cannot happen for
+    // finite logits; the clamp keeps a fault out of the weight streams)
+    R.e[t * a.k + lane] = my_e < 0 ? 0 : (my_e >= a.E ? a.E - 1 : my_e);
+    R.g[t * a.k + lane] = g;
+  }
+}
+
+// Slot of expert e, or -1 when not resident (a slot outside 0..n_slots-1 in
+// the caller's map counts as not resident, so it is never dereferenced).
+__device__ __forceinline__ int resident_ref(const DecodeArgs& a, int e) {
+  if (a.slot_of == nullptr) return e;
+  const int s = a.slot_of[e];
+  return (s >= 0 && s < a.n_slots) ? s : -1;
+}
+
+// Wave 0 only, after every token's routing is visible in LDS.
 template <int T>
-__global__ __launch_bounds__(256) void decode_prep_kernel(DecodeArgs a, DecodeWs w) {
-  __shared__ int32_t s_e[kDecodeMaxT * kMaxTopK];
-  __shared__ float s_g[kDecodeMaxT * kMaxTopK];
-  __shared__ int32_t s_first[kDecodeMaxT * kMaxTopK];
-  __shared__ int32_t s_u[kDecodeMaxT * kMaxTopK];
-  __shared__ int32_t s_cnt[4];
-  __shared__ float s_rinv[kDecodeMaxT];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int k = a.k, P = T * k, D = a.D;
-
-  // 1. routing of token wv; RMS factor of its activations.
-  if (wv < T) {
-    int my_e;
-    float my_l;
-    wave_topk(a.logits + (size_t)wv * a.E, a.E, k, lane, my_e, my_l);
-    const float g = wave_gate(my_l, k, lane);
-    if (lane < k) {
-      s_e[wv * k + lane] = my_e;
-      s_g[wv * k + lane] = g;
-      w.idx[wv * k + lane] = my_e;
-      w.gate[wv * k + lane] = g;
-    }
-    if (a.rmsnorm) {
-      float ss = 0.f;
-      for (int i = lane; i < D; i += 64) {
-        const float v = a.x_bf16 ? bf16_to_f32(((const uint16_t*)a.x)[(size_t)wv * D + i])
-                                 : ((const float*)a.x)[(size_t)wv * D + i];
-        ss += v * v;
+__device__ __forceinline__ void decode_build_list(const DecodeArgs& a, const DecodeWs& w,
+                                                  RouteLds& R, int lane, bool publish) {
+  const int k = a.k, P = T * k;  // P <= 128: lane handles pairs lane, lane + 64
+  int first[2];
+  bool valid[2], hit[2];
+  unsigned long long bf[2], bm[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int p = lane + 64 * h;
+    valid[h] = p < P;
+    first[h] = -1;
+    hit[h] = false;
+    if (valid[h]) {
+      const int e = R.e[p];
+      hit[h] = resident_ref(a, e) >= 0;
+      if (hit[h]) {
+        first[h] = p;
+        for (int p2 = 0; p2 < p; ++p2)
+          if (R.e[p2] == e) {
+            first[h] = p2;
+            break;
+          }
       }
-      ss = wave_sum(ss);
-      if (lane == 0) s_rinv[wv] = 1.0f / sqrtf(ss / (float)D + 1e-6f);
     }
+    bf[h] = __ballot(valid[h] && first[h] == p);
+    bm[h] = __ballot(valid[h] && !hit[h]);
   }
-  for (int i = tid; i < w.Wmax * 4; i += 256) w.work_gate[i] = 0.f;
-  __syncthreads();
-
-  // 2. distinct resident experts in (token, rank) order of first occurrence.
-  if (tid < P) {
-    const int e = s_e[tid];
-    const bool hit = a.slot_of == nullptr || a.slot_of[e] >= 0;
-    int first = -1;
-    if (hit) {
-      first = tid;
-      for (int p2 = 0; p2 < tid; ++p2)
-        if (s_e[p2] == e) {
-          first = p2;
-          break;
-        }
-    }
-    s_first[tid] = first;
+  const int nf0 = __popcll(bf[0]), nm0 = __popcll(bm[0]);
+  const int U = nf0 + __popcll(bf[1]);
+  const int M = nm0 + __popcll(bm[1]);
+  const bool has_sh = a.shared != nullptr;
+  const int nu = U + (has_sh ? 1 : 0);
+  for (int i = lane; i < nu * 4; i += 64) R.wg[i] = 0.f;
+  wave_lds_sync();
+  auto list_index = [&](int fp) {  // list index of the pair that first named an expert
+    const int hh = fp >> 6;
+    return (hh ? nf0 : 0) + __popcll(bf[hh] & ((1ull << (fp & 63)) - 1ull));
+  };
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int p = lane + 64 * h;
+    if (valid[h] && first[h] == p) R.ref[list_index(p)] = resident_ref(a, R.e[p]);
+    if (valid[h] && first[h] >= 0) R.wg[list_index(first[h]) * 4 + p / k] = R.g[p];
   }
-  __syncthreads();
-  unsigned long long bf = 0, bm = 0;
-  if (wv < 2) {
-    const int p = tid;
-    const bool isf = p < P && s_first[p] == p;
-    const bool ism = p < P && s_first[p] < 0;
-    bf = __ballot(isf);
-    bm = __ballot(ism);
-    if (lane == 0) {
-      s_cnt[wv] = __popcll(bf);
-      s_cnt[2 + wv] = __popcll(bm);
-    }
+  if (lane == 0) {
+    R.nu = nu;
+    if (has_sh) R.ref[U] = -1;
   }
-  __syncthreads();
-  const int U = s_cnt[0] + s_cnt[1];
-  const int M = s_cnt[2] + s_cnt[3];
-  if (tid < P) {
-    const unsigned long long lt = (1ull << lane) - 1ull;
-    const int t = tid / k, j = tid % k, e = s_e[tid];
-    if (s_first[tid] == tid) {
-      const int u = (wv == 1 ? s_cnt[0] : 0) + __popcll(bf & lt);
-      s_u[tid] = u;
-      w.work_ref[u] = a.slot_of ? a.slot_of[e] : e;
-    } else if (s_first[tid] < 0) {
-      const int mi = (wv == 1 ? s_cnt[2] : 0) + __popcll(bm & lt);
-      MissRec r;
-      r.token = t;
-      r.rank = j;
-      r.expert = e;
-      r.gate = s_g[tid];
-      a.miss[mi] = r;
-    }
+  if (has_sh && lane < T) R.wg[U * 4 + lane] = 1.0f;
+  wave_lds_sync();
+  if (!publish) return;
+  for (int i = lane; i < nu; i += 64) w.work_ref[i] = R.ref[i];
+  for (int i = lane; i < nu * 4; i += 64) w.work_gate[i] = R.wg[i];
+  for (int i = lane; i < P; i += 64) {
+    w.idx[i] = R.e[i];
+    w.gate[i] = R.g[i];
   }
-  __syncthreads();
-  if (tid < P && s_first[tid] >= 0) {
-    const int u = s_u[s_first[tid]];
-    w.work_gate[u * 4 + tid / k] = s_g[tid];
-  }
-  if (tid == 0) {
-    const int has_sh = a.shared != nullptr;
-    *w.nwork = U + has_sh;
-    if (has_sh) {
-      w.work_ref[U] = -1;
-      for (int t = 0; t < T; ++t) w.work_gate[U * 4 + t] = 1.0f;
-    }
+  if (lane == 0) {
+    *w.nwork = nu;
     if (a.miss_count) *a.miss_count = M;
   }
-
-  // 3. activation operand (bf16 hi [+ lo]) and per-block sums (X, X').
-  const int nb = D / 32;
-  for (int i = tid; i < T * nb; i += 256) {
-    const int t = i / nb, b = i % nb;
-    float X = 0.f, Xc = 0.f;
-    for (int kk = 0; kk < 32; ++kk) {
-      const size_t ei = (size_t)t * D + 32 * b + kk;
-      uint16_t hi, lo = 0;
-      if (a.rmsnorm) {
-        const float v = a.x_bf16 ? bf16_to_f32(((const uint16_t*)a.x)[ei]) : ((const float*)a.x)[ei];
-        hi = f32_to_bf16(v * s_rinv[t]);
-      } else if (a.x_bf16) {
-        hi = ((const uint16_t*)a.x)[ei];
-      } else {
-        const float v = ((const float*)a.x)[ei];
-        hi = f32_to_bf16(v);
-        lo = f32_to_bf16(v - bf16_to_f32(hi));
-      }
-      w.xa_hi[ei] = hi;
-      w.xa_lo[ei] = lo;
-      const float v = bf16_to_f32(hi) + bf16_to_f32(lo);
-      X += v;
-      Xc += dq_offset(b & 1, (kk & 7) >> 1) * v;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int p = lane + 64 * h;
+    if (valid[h] && !hit[h]) {
+      MissRec r;
+      r.token = p / k;
+      r.rank = p % k;
+      r.expert = R.e[p];
+      r.gate = R.g[p];
+      a.miss[(h ? nm0 : 0) + __popcll(bm[h] & ((1ull << lane) - 1ull))] = r;
     }
-    w.xs[(size_t)t * nb + b] = make_float2(X, Xc);
   }
 }
 
@@ -305,41 +297,136 @@ __device__ __forceinline__ void load_record(const uint8_t* rec, int lane, uint4&
 }
 
 // ----------------------------------------------------------------------------
-// decode_gateup.  Grid: (routed capacity x F/32) + Fs/32 blocks of 512 threads.
-// Wave w: h-group hs = w/4 (16 FFN rows), matrix = (w/2)%2 (gate, up), K half
-// = w%2 (octets o = half, half+2, ...).
-template <int T, int FMT, bool HAS_LO>
-__global__ __launch_bounds__(512) void decode_gateup_kernel(DecodeArgs a, DecodeWs w) {
+// decode_gateup.  Grid: (routed capacity x F/16) + Fs/16 blocks of 256
+// threads, two blocks per CU.  Every thread first issues its share of the
+// activation loads, then waves 0..T-1 route; after the list is known, wave w
+// computes matrix w/2 (gate, up) over the K octets o = w%2, w%2 + 2, ... of
+// one 16-row h-group.
+template <int T, int FMT, int XM>
+__global__ __launch_bounds__(kGuThreads, 2) void decode_gateup_kernel(DecodeArgs a, DecodeWs w) {
   extern __shared__ uint4 s_dyn[];
+  __shared__ RouteLds R;
   __shared__ float s_red[kGuWaves][kDecodeMaxT][16];
+  __shared__ float s_ss[kGuWaves][kDecodeMaxT];
+  constexpr bool HAS_LO = XM == kXF32;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int D = a.D, oD = octets(D), nbD = D / 32;
+  const int D = a.D, oD = octets(D), nbD = D / 32, D8 = D / 8;
+  uint4* s_xhi = s_dyn;                                            // [T][D/8]
+  uint4* s_xlo = s_dyn + T * D8;                                   // [T][D/8]
+  float2* s_xs = reinterpret_cast<float2*>(s_dyn + (HAS_LO ? 2 : 1) * T * D8);   // [T][D/32]
+  float* s_raw = reinterpret_cast<float*>(s_xs + T * nbD);         // [T][D] (XM == kXRms)
+  if (tid == 0)
+    R.scr = reinterpret_cast<key64*>(reinterpret_cast<uint8_t*>(s_raw) +
+                                     (XM == kXRms ? (size_t)T * D * 4 : 0));
+  __syncthreads();
+
+  // 0. Activation loads in flight before routing (16-byte pieces of the input).
+  const bool in_bf16 = XM == kXBf16 || a.x_bf16;
+  const int nin = in_bf16 ? T * D8 : 2 * T * D8;          // 16-byte pieces of x
+  constexpr int XJ = (XM == kXBf16 ? 2 : 4) * T;          // pieces per thread, D <= 4096
+  uint4 xr[XJ];
+#pragma unroll
+  for (int j = 0; j < XJ; ++j) {
+    const int i = tid + kGuThreads * j;
+    if (i < nin) xr[j] = reinterpret_cast<const uint4*>(a.x)[i];
+  }
+  // 1. Routing of token wv (waves 0..T-1).
+  if (wv < T) decode_route_token(a, R, wv, lane);
+  // 2. Activations to LDS: the bf16 operand (hi, and lo for fp32 input), or
+  // fp32 values and per-token sums of squares for the normalised mode.
+  float ss[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) ss[t] = 0.f;
+#pragma unroll
+  for (int j = 0; j < XJ; ++j) {
+    const int i = tid + kGuThreads * j;
+    if (i >= nin) continue;
+    if (XM == kXBf16) {
+      s_xhi[i] = xr[j];
+    } else if (XM == kXF32) {  // piece i = fp32 elements 4i..4i+3
+      const float v[4] = {__uint_as_float(xr[j].x), __uint_as_float(xr[j].y),
+                          __uint_as_float(xr[j].z), __uint_as_float(xr[j].w)};
+      uint32_t hi[2], lo[2];
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2) {
+        const uint16_t h0 = f32_to_bf16(v[2 * q2]), h1 = f32_to_bf16(v[2 * q2 + 1]);
+        hi[q2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        lo[q2] = pack_bf16x2(v[2 * q2] - bf16_to_f32(h0), v[2 * q2 + 1] - bf16_to_f32(h1));
+      }
+      reinterpret_cast<uint2*>(s_xhi)[i] = make_uint2(hi[0], hi[1]);
+      reinterpret_cast<uint2*>(s_xlo)[i] = make_uint2(lo[0], lo[1]);
+    } else {  // kXRms
+      float q2 = 0.f;
+      int t;
+      if (in_bf16) {  // piece i = bf16 elements 8i..8i+7
+        const uint32_t qq[4] = {xr[j].x, xr[j].y, xr[j].z, xr[j].w};
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const float v0 = bf16_lo(qq[e2]), v1 = bf16_hi(qq[e2]);
+          s_raw[8 * i + 2 * e2] = v0;
+          s_raw[8 * i + 2 * e2 + 1] = v1;
+          q2 += v0 * v0 + v1 * v1;
+        }
+        t = i / D8;
+      } else {        // piece i = fp32 elements 4i..4i+3
+        const float v[4] = {__uint_as_float(xr[j].x), __uint_as_float(xr[j].y),
+                            __uint_as_float(xr[j].z), __uint_as_float(xr[j].w)};
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          s_raw[4 * i + e2] = v[e2];
+          q2 += v[e2] * v[e2];
+        }
+        t = i / (2 * D8);
+      }
+#pragma unroll
+      for (int tt = 0; tt < T; ++tt) ss[tt] += tt == t ? q2 : 0.f;
+    }
+  }
+  if (XM == kXRms) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const float r = wave_sum(ss[t]);
+      if (lane == 0) s_ss[wv][t] = r;
+    }
+  }
+  __syncthreads();
+  if (XM == kXRms) {
+    for (int i = tid; i < T * D8; i += kGuThreads) {
+      const int t = i / D8;
+      float ssum = 0.f;
+#pragma unroll
+      for (int w2 = 0; w2 < kGuWaves; ++w2) ssum += s_ss[w2][t];
+      const float rinv = 1.0f / sqrtf(ssum / (float)D + 1e-6f);
+      uint32_t hi[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        hi[j] = pack_bf16x2(s_raw[8 * i + 2 * j] * rinv, s_raw[8 * i + 2 * j + 1] * rinv);
+      s_xhi[i] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    }
+  }
+  if (wv == 0) decode_build_list<T>(a, w, R, lane, blockIdx.x == 0);
+  __syncthreads();
+
+  // 3. This block's work item.
   const int has_sh = a.shared != nullptr;
-  const int nwork = *w.nwork;
-  const int U = nwork - has_sh;
-  const int Wr = w.Wmax - 1;
-  const int gpr = a.F / 32;
-  int u, g, Fi;
+  const int U = R.nu - has_sh;
+  const int Wr = w.Wmax - 1, gpr = a.F / 16;
+  int u, g;
   const uint8_t* base;
   if ((int)blockIdx.x < Wr * gpr) {
     u = blockIdx.x / gpr;
     g = blockIdx.x % gpr;
     if (u >= U) return;
-    Fi = a.F;
-    base = a.routed + (size_t)w.work_ref[u] * a.stride;
+    base = a.routed + (size_t)R.ref[u] * a.stride;
   } else {
     if (!has_sh) return;
     g = blockIdx.x - Wr * gpr;
     u = U;
-    Fi = a.Fs;
     base = a.shared;
   }
-  (void)Fi;
-  const int hs = wv >> 2, mat = (wv >> 1) & 1, kh = wv & 1;
+  const int mat = wv >> 1, kh = wv & 1;
   const int n = lane & 15, q = lane >> 4;
-  const uint8_t* tile = base + (size_t)((2 * g + hs) * 2 + mat) * oD * rec_bytes(FMT);
-
-  // Issue every weight load of this wave first.
+  const uint8_t* tile = base + (size_t)(g * 2 + mat) * oD * rec_bytes(FMT);
   uint4 cw[kMaxOctPerWave], pa[kMaxOctPerWave], pb[kMaxOctPerWave];
   uint2 hw[kMaxOctPerWave];
 #pragma unroll
@@ -347,18 +434,27 @@ __global__ __launch_bounds__(512) void decode_gateup_kernel(DecodeArgs a, Decode
     const int o = kh + 2 * i;
     if (o < oD) load_record<FMT>(tile + (size_t)o * rec_bytes(FMT), lane, cw[i], hw[i], pa[i], pb[i]);
   }
-
-  // Stage the activation operand and its block sums in LDS.
-  uint4* s_xhi = s_dyn;
-  uint4* s_xlo = s_dyn + T * D / 8;
-  float2* s_xs = reinterpret_cast<float2*>(s_dyn + (HAS_LO ? 2 : 1) * T * D / 8);
-  for (int i = tid; i < T * D / 8; i += 512) {
-    s_xhi[i] = reinterpret_cast<const uint4*>(w.xa_hi)[i];
-    if (HAS_LO) s_xlo[i] = reinterpret_cast<const uint4*>(w.xa_lo)[i];
+  // Per-block activation sums X = sum x and X' = sum c x (while the weights arrive).
+  for (int i = tid; i < T * nbD; i += kGuThreads) {
+    const int t = i / nbD, b = i % nbD;
+    float X = 0.f, Xc = 0.f;
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const uint4 vh = s_xhi[t * D8 + 4 * b + qq];
+      const uint4 vl = HAS_LO ? s_xlo[t * D8 + 4 * b + qq] : make_uint4(0, 0, 0, 0);
+      const uint32_t hh[4] = {vh.x, vh.y, vh.z, vh.w}, ll[4] = {vl.x, vl.y, vl.z, vl.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float v = bf16_lo(hh[j]) + bf16_lo(ll[j]) + bf16_hi(hh[j]) + bf16_hi(ll[j]);
+        X += v;
+        Xc += dq_offset(b & 1, j) * v;
+      }
+    }
+    s_xs[i] = make_float2(X, Xc);
   }
-  for (int i = tid; i < T * nbD; i += 512) s_xs[i] = w.xs[i];
   __syncthreads();
 
+  // 4. Dequantising MFMA GEMV over this wave's octets.
   const DqConsts kc = dq_consts();
   float acc[T], mt[T];
 #pragma unroll
@@ -369,7 +465,7 @@ __global__ __launch_bounds__(512) void decode_gateup_kernel(DecodeArgs a, Decode
     if (o < oD) {
       auto xfrag = [&](int beta, bool lo) -> uint4 {
         if (n >= T) return make_uint4(0, 0, 0, 0);
-        const int idx = (n * D + 32 * (8 * o + beta) + 8 * q) / 8;
+        const int idx = n * D8 + 4 * (8 * o + beta) + q;
         return lo ? s_xlo[idx] : s_xhi[idx];
       };
       auto xsum = [&](int beta, int t) -> float2 { return s_xs[t * nbD + 8 * o + beta]; };
@@ -387,25 +483,26 @@ __global__ __launch_bounds__(512) void decode_gateup_kernel(DecodeArgs a, Decode
   }
   __syncthreads();
 
-  // SwiGLU over 32 FFN rows x T tokens; h in bf16 hi + lo; block sums of h.
-  if (tid < 32 * T) {
-    const int t = tid >> 5, f = tid & 31, hq = f >> 4, nn = f & 15;
-    const float ga = s_red[hq * 4 + 0][t][nn] + s_red[hq * 4 + 1][t][nn];
-    const float ub = s_red[hq * 4 + 2][t][nn] + s_red[hq * 4 + 3][t][nn];
+  // 5. SwiGLU over 16 FFN rows x T tokens; h in bf16 hi + lo; half-block sums.
+  if (tid < 16 * T) {
+    const int t = tid >> 4, nn = tid & 15;
+    const float ga = s_red[0][t][nn] + s_red[1][t][nn];
+    const float ub = s_red[2][t][nn] + s_red[3][t][nn];
     const float h = silu(ga) * ub;
     const uint16_t hi = f32_to_bf16(h);
     const uint16_t lo = f32_to_bf16(h - bf16_to_f32(hi));
-    const size_t hidx = ((size_t)u * T + t) * w.Fp + 32 * g + f;
+    const size_t hidx = ((size_t)u * T + t) * w.Fp + 16 * g + nn;
     w.hh[hidx] = hi;
     w.hl[hidx] = lo;
     const float v = bf16_to_f32(hi) + bf16_to_f32(lo);
-    float X = v, Xc = dq_offset(g & 1, (f & 7) >> 1) * v;
+    const int kl = 16 * (g & 1) + nn;  // position inside the 32-row down block
+    float X = v, Xc = dq_offset((g >> 1) & 1, (kl & 7) >> 1) * v;
 #pragma unroll
-    for (int o2 = 16; o2 >= 1; o2 >>= 1) {
+    for (int o2 = 8; o2 >= 1; o2 >>= 1) {
       X += __shfl_xor(X, o2, 64);
       Xc += __shfl_xor(Xc, o2, 64);
     }
-    if (f == 0) w.hs[((size_t)u * T + t) * (w.Fp / 32) + g] = make_float2(X, Xc);
+    if (nn == 0) w.hs[(((size_t)u * T + t) * (w.Fp / 32) + (g >> 1)) * 2 + (g & 1)] = make_float2(X, Xc);
   }
 }
 
@@ -477,7 +574,9 @@ __global__ __launch_bounds__(1024) void decode_down_kernel(DecodeArgs a, DecodeW
           return s_hw[(n * 2 + (lo ? 1 : 0)) * hrow + (32 * (8 * o + beta) + 8 * q) / 8];
         };
         auto xsum = [&](int beta, int t) -> float2 {
-          return w.hs[((size_t)u * T + t) * (Fp / 32) + 8 * o + beta];
+          const size_t hi = (((size_t)u * T + t) * (Fp / 32) + 8 * o + beta) * 2;
+          const float2 h0 = w.hs[hi], h1 = w.hs[hi + 1];
+          return make_float2(h0.x + h1.x, h0.y + h1.y);
         };
         record_gemv<T, FMT, true>(cw[o], hw[o], pa[o], pb[o], nvalid, kc, xfrag, xsum, acc, mt, q);
       }
@@ -520,32 +619,32 @@ static hipError_t allow_lds(K kernel, size_t bytes, size_t& cur) {
   return e;
 }
 
-template <int T, int FMT>
-static hipError_t launch_decode_t(const DecodeArgs& a, const DecodeWs& w, hipStream_t st) {
-  static size_t lds_gu_lo = 0, lds_gu = 0, lds_dn = 0;
-  const bool has_lo = !a.x_bf16 && !a.rmsnorm;
-  const size_t lds = (size_t)T * a.D * 2 * (has_lo ? 2 : 1) + (size_t)T * (a.D / 32) * 8;
+template <int T, int FMT, int XM>
+static hipError_t launch_decode_x(const DecodeArgs& a, const DecodeWs& w, hipStream_t st) {
+  static size_t lds_gu = 0, lds_dn = 0;
+  const int D8 = a.D / 8, nbD = a.D / 32;
+  const size_t lds = (size_t)T * D8 * 16 * (XM == kXF32 ? 2 : 1) + (size_t)T * nbD * 8 +
+                     (XM == kXRms ? (size_t)T * a.D * 4 : 0) + T * topk_scratch_bytes(a.E, a.k);
   const size_t lds_down = (size_t)kDnWaves * T * 2 * w.Fp * 2;
   hipError_t e;
-  if (has_lo) {
-    if ((e = allow_lds(decode_gateup_kernel<T, FMT, true>, lds, lds_gu_lo)) != hipSuccess) return e;
-  } else {
-    if ((e = allow_lds(decode_gateup_kernel<T, FMT, false>, lds, lds_gu)) != hipSuccess) return e;
-  }
+  if ((e = allow_lds(decode_gateup_kernel<T, FMT, XM>, lds, lds_gu)) != hipSuccess) return e;
   if ((e = allow_lds(decode_down_kernel<T, FMT>, lds_down, lds_dn)) != hipSuccess) return e;
-  decode_prep_kernel<T><<<1, 256, 0, st>>>(a, w);
   const int Wr = w.Wmax - 1;
-  const int nblk = Wr * (a.F / 32) + (a.shared ? a.Fs / 32 : 0);
+  const int nblk = Wr * (a.F / 16) + (a.shared ? a.Fs / 16 : 0);
   KernelTimer& tm = kernel_timer();
   if ((e = record_timer_event(tm.before, st)) != hipSuccess) return e;
-  if (has_lo)
-    decode_gateup_kernel<T, FMT, true><<<nblk, 512, lds, st>>>(a, w);
-  else
-    decode_gateup_kernel<T, FMT, false><<<nblk, 512, lds, st>>>(a, w);
+  decode_gateup_kernel<T, FMT, XM><<<nblk, kGuThreads, lds, st>>>(a, w);
   if ((e = record_timer_event(tm.after, st)) != hipSuccess) return e;
   tm.before = tm.after = nullptr;
   decode_down_kernel<T, FMT><<<a.D / 16, 1024, lds_down, st>>>(a, w);
   return hipGetLastError();
+}
+
+template <int T, int FMT>
+static hipError_t launch_decode_t(const DecodeArgs& a, const DecodeWs& w, hipStream_t st) {
+  if (a.rmsnorm) return launch_decode_x<T, FMT, kXRms>(a, w, st);
+  if (a.x_bf16) return launch_decode_x<T, FMT, kXBf16>(a, w, st);
+  return launch_decode_x<T, FMT, kXF32>(a, w, st);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, const DecodeWs& w, hipStream_t st) {

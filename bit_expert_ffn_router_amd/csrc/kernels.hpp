@@ -46,17 +46,14 @@ hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offs
 constexpr int kDecodeMaxT = 4;
 
 struct DecodeWs {
-  int32_t* idx;        // [T*k]
+  int32_t* idx;        // [T*k] routing of the call (written by block 0)
   float* gate;         // [T*k]
-  int32_t* nwork;      // [1]
+  int32_t* nwork;      // [1] listed experts (distinct resident + shared)
   int32_t* work_ref;   // [Wmax] routed index (expert or slot) or -1 = shared
-  float* work_gate;    // [Wmax][4]
-  uint16_t* xa_hi;     // [T][D] bf16 operand
-  uint16_t* xa_lo;     // [T][D] bf16 residual (fp32 inputs)
-  float2* xs;          // [T][D/32] block sums (X, X')
+  float* work_gate;    // [Wmax][4] gate of each token for each listed expert
   uint16_t* hh;        // [Wmax][T][Fp] bf16 hi of h
   uint16_t* hl;        // [Wmax][T][Fp] bf16 lo of h
-  float2* hs;          // [Wmax][T][Fp/32] block sums of h
+  float2* hs;          // [Wmax][T][Fp/32][2] block sums of h, per 16-row half
   int Wmax;            // routed work capacity + 1 (shared)
   int Fp;              // padded FFN width of the h rows
 };
@@ -70,6 +67,7 @@ struct DecodeArgs {
   const uint8_t* routed;
   size_t stride;
   const int32_t* slot_of;  // NULL = all resident
+  int n_slots;             // slots behind `routed` when slot_of != NULL
   const uint8_t* shared;   // NULL = no shared expert
   void* out;
   int out_bf16;

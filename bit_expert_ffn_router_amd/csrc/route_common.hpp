@@ -21,50 +21,105 @@ __device__ __forceinline__ float ord_key_inv(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-// Top-k of row[0..E) by one wave.  Expert e lives in lane e % 64, slot e / 64.
+// 64-bit composite key (value key << 32 | ~expert id): larger wins, so equal
+// values resolve to the lower expert id; 0 marks an empty or taken slot
+// (every real key has a nonzero value half).
+typedef unsigned long long key64;
+
+__device__ __forceinline__ key64 make_key(uint32_t vk, int e) {
+  return ((key64)vk << 32) | (key64)(0xFFFFFFFFu - (uint32_t)e);
+}
+
+// LDS entries of wave_topk's scratch for a given slot count and k, and the
+// slot count used for E experts.
+__host__ __device__ constexpr int topk_scratch(int vpl, int k) { return 64 + k * vpl + k; }
+__host__ __device__ constexpr int topk_vpl(int E) { return E <= 512 ? 8 : (E <= 1024 ? 16 : 32); }
+__host__ __device__ constexpr size_t topk_scratch_bytes(int E, int k) {
+  return (size_t)topk_scratch(topk_vpl(E), k) * 8;
+}
+
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Top-k of row[0..E) by one wave (E <= 64 * VPL), exact.  Expert e lives in
+// lane e % 64, slot e / 64; every key is the composite (value, ~id), so all
+// keys are distinct and order = value descending, id ascending.
+//  1. Each lane takes the maximum of its keys; the lane maxima are ranked
+//     against each other through LDS.  The k-th largest lane maximum L is a
+//     lower bound of the k-th largest key (at least k keys are >= L), so
+//     every top-k key is >= L.  (Fewer than k non-empty lanes: L = 0.)
+//  2. The keys >= L -- at most k lanes contribute, so at most k*VPL -- are
+//     compacted into LDS and ranked against each other; those of rank < k
+//     are stored at their rank.
 // Afterwards lane j < k holds the j-th selected expert and its (canonical)
-// logit.  Composite 64-bit key: (value key << 32) | ~e, so equal values
-// resolve to the lower expert id.
+// logit.  `scratch`: topk_scratch(VPL, k) LDS entries private to the wave.
+template <int VPL>
 __device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, int k, int lane,
-                                          int& my_e, float& my_l) {
-  constexpr int VPL = kMaxExperts / 64;
-  uint32_t key[VPL];
-  uint32_t taken = 0;
-  const int nv = (E + 63) / 64;
+                                          int& my_e, float& my_l, key64* scratch) {
+  key64 key[VPL];
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     const int e = i * 64 + lane;
-    if (i < nv && e < E) {
-      key[i] = ord_key(row[e]);
-    } else {
-      key[i] = 0u;
-      taken |= 1u << i;
-    }
+    key[i] = e < E ? make_key(ord_key(row[e]), e) : 0ull;
   }
+  key64 m = key[0];
+#pragma unroll
+  for (int i = 1; i < VPL; ++i) m = key[i] > m ? key[i] : m;
+  scratch[lane] = m;
+  wave_lds_fence();
+  int r = 0;
+#pragma unroll 8
+  for (int j = 0; j < 64; ++j) r += scratch[j] > m ? 1 : 0;
+  const unsigned long long nonempty = __ballot(m != 0ull);
+  key64 L = 0ull;
+  if (__popcll(nonempty) >= k) {
+    const unsigned long long at = __ballot(m != 0ull && r == k - 1);
+    const int src = __builtin_ctzll(at);
+    // readlane returns int: widen through uint32_t (no sign extension)
+    L = ((key64)(uint32_t)__builtin_amdgcn_readlane((uint32_t)(m >> 32), src) << 32) |
+        (key64)(uint32_t)__builtin_amdgcn_readlane((uint32_t)m, src);
+  }
+  key64* cand = scratch + 64;
+  key64* out = scratch + 64 + k * VPL;
+  int C = 0;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const bool c = key[i] != 0ull && key[i] >= L;
+    const unsigned long long mc = __ballot(c);
+    const int pos = C + __builtin_amdgcn_mbcnt_hi((uint32_t)(mc >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)mc, 0u));
+    if (c) cand[pos] = key[i];
+    C += __popcll(mc);
+  }
+  wave_lds_fence();
+  for (int j = lane; j < C; j += 64) {
+    const key64 c = cand[j];
+    int rank = 0;
+    for (int i = 0; i < C; ++i) rank += cand[i] > c ? 1 : 0;
+    if (rank < k) out[rank] = c;
+  }
+  wave_lds_fence();
   my_e = 0;
   my_l = 0.f;
-  for (int r = 0; r < k; ++r) {
-    unsigned long long best = 0ull;
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      if (i < nv && !((taken >> i) & 1u)) {
-        const unsigned long long c = ((unsigned long long)key[i] << 32) |
-                                     (unsigned long long)(0xFFFFFFFFu - (uint32_t)(i * 64 + lane));
-        best = c > best ? c : best;
-      }
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const unsigned long long y = __shfl_xor(best, o, 64);
-      best = y > best ? y : best;
-    }
-    const int e = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull));
-    if ((e & 63) == lane) taken |= 1u << (e >> 6);
-    if (lane == r) {
-      my_e = e;
-      my_l = ord_key_inv((uint32_t)(best >> 32));
-    }
+  if (lane < k) {
+    const key64 o = out[lane];
+    my_e = (int)(0xFFFFFFFFu - (uint32_t)o);
+    my_l = ord_key_inv((uint32_t)(o >> 32));
   }
+}
+
+// Dispatch on the number of experts.
+__device__ __forceinline__ void wave_topk_any(const float* __restrict__ row, int E, int k, int lane,
+                                              int& my_e, float& my_l, key64* scratch) {
+  if (E <= 512)
+    wave_topk<8>(row, E, k, lane, my_e, my_l, scratch);
+  else if (E <= 1024)
+    wave_topk<16>(row, E, k, lane, my_e, my_l, scratch);
+  else
+    wave_topk<32>(row, E, k, lane, my_e, my_l, scratch);
 }
 
 // Gate of lane j < k: exp(l_j - l_0) / sum_i exp(l_i - l_0) (0 for other lanes).
