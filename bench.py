@@ -272,6 +272,36 @@ def bench_chain(ctx, stack, K, W, use_graph, T, slot=None):
     return res
 
 
+def bench_prefill(ctx, stack, K, W, use_graph, n_layers=4):
+    """8192 tokens through one layer per step, rotating over n_layers layers."""
+    torch, moe, synth = ctx.torch, ctx.moe, ctx.synth
+    w = synth.WORKLOADS["prefill_8192"]
+    _, shape, layers = stack
+    L, T, D = min(n_layers, len(layers)), w["tokens"], w["d_model"]
+    logits = [ctx.dev_f32(synth.router_logits(0, l, T, w["n_experts"], zipf_s=w["zipf_s"],
+                                              alpha=w["alpha"])) for l in range(L)]
+    xs = [ctx.dev_u16(synth.activations_bf16(0, l, T, D)) for l in range(L)]
+    wsb = moe.moe_workspace_bytes(shape, T)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=ctx.dev)
+    out = torch.empty(T * D, dtype=torch.int16, device=ctx.dev)
+    tables = [layers[l].table() for l in range(L)]
+
+    def launch(i):
+        l = i % L
+        moe.moe_layer_forward(shape, T, xs[l], moe.MOE_BF16, 0, logits[l], tables[l], out,
+                              moe.MOE_BF16, None, 0, None, ws, wsb)
+
+    launch(0)
+    torch.cuda.synchronize()
+    dt, kms = run_steps(ctx, launch, K, W, use_graph, timer_events=True)
+    rows = T * w["top_k"] + T                       # routed pairs + shared-expert rows
+    flops_gu = 2.0 * rows * D * 2 * w["d_ff"]       # gate/up grouped GEMM
+    flops_layer = flops_gu + 2.0 * rows * w["d_ff"] * D
+    kavg = sum(kms) / len(kms) * 1e-3
+    return dict(tokens=K * T, seconds=dt, kernel_s=kavg, flops_per_launch=flops_gu,
+                flops_layer=flops_layer)
+
+
 def build_slot_stack(ctx, name):
     torch, moe, synth, np = ctx.torch, ctx.moe, ctx.synth, ctx.np
     w = synth.WORKLOADS[name]
@@ -371,6 +401,25 @@ def main():
             config="4 tokens x 48 chained layers (RMS input rule), Q2SM, 43.6 GB resident")
         print("mtp_verify_t4_48l: %.3f ms/step" % (r["seconds"] / Kc * 1e3), file=sys.stderr,
               flush=True)
+    if "prefill_8192" in wl:
+        if stack is None:
+            stack = decode_stack(ctx, "prefill_8192", 4)
+        Kp = max(2, K // 48)
+        r = bench_prefill(ctx, stack, Kp, 2, use_graph)
+        sps = r["seconds"] / Kp
+        achieved = r["flops_per_launch"] / r["kernel_s"] / 1e12
+        results["prefill_8192"] = dict(
+            value=r["tokens"] / r["seconds"], unit="tokens/s", steps=Kp, ms_per_step=sps * 1e3,
+            config="8192 tokens x 1 layer (rotated over 4 resident layers), Q2SM, bf16 in/out",
+            layer_mfma_frac=r["flops_layer"] / sps / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            roofline={"bound": "mfma",
+                      "kernel": "pf_gemm_kernel<0> (gate/up grouped GEMM + SwiGLU)",
+                      "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                      "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                      "flops_per_launch": r["flops_per_launch"],
+                      "kernel_us": r["kernel_s"] * 1e6})
+        print("prefill_8192: %.3f ms/step, gate/up kernel %.1f us (%.1f TFLOP/s)" %
+              (sps * 1e3, r["kernel_s"] * 1e6, achieved), file=sys.stderr, flush=True)
     if stack is not None:
         del stack
         torch.cuda.empty_cache()
@@ -386,9 +435,6 @@ def main():
               file=sys.stderr, flush=True)
         del keep, tables, sstack
         torch.cuda.empty_cache()
-    if "prefill_8192" in wl:
-        results["prefill_8192"] = dict(value=None, unit="tokens/s",
-                                       note="prefill path not built in this version")
 
     line = {
         "metric": METRIC, "value": None, "unit": "tokens/s", "n_gpus": 1, "steps": K,

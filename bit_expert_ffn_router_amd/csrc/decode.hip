@@ -85,7 +85,7 @@ DecodeWs decode_ws_carve(void* ws, int T, int D, int F, int Fs, int E, int k) {
 // block computes the same list; block 0 also publishes it (and the misses).
 struct RouteLds {
   key64* scr;  // T regions of topk_scratch_bytes(E, k) in dynamic LDS
-  int32_t e[kDecodeMaxT * kMaxTopK];
+  alignas(16) int32_t e[kDecodeMaxT * kMaxTopK];
   float g[kDecodeMaxT * kMaxTopK];
   int32_t ref[kDecodeMaxT * kMaxTopK + 1];
   float wg[(kDecodeMaxT * kMaxTopK + 1) * 4];
@@ -139,12 +139,22 @@ __device__ __forceinline__ void decode_build_list(const DecodeArgs& a, const Dec
       const int e = R.e[p];
       hit[h] = resident_ref(a, e) >= 0;
       if (hit[h]) {
+        // first (token, rank) pair naming the same expert; one token's ids
+        // are distinct, so only pairs of earlier tokens can match
         first[h] = p;
-        for (int p2 = 0; p2 < p; ++p2)
-          if (R.e[p2] == e) {
-            first[h] = p2;
-            break;
+        if (T > 1) {
+          const int4* e4 = reinterpret_cast<const int4*>(R.e);
+          const int nq = (p / k) * k;  // pairs of earlier tokens
+          for (int c = 0; c < (nq + 3) / 4; ++c) {
+            const int4 v = e4[c];
+            const int ids[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int q2 = 0; q2 < 4; ++q2) {
+              const int idx = 4 * c + q2;
+              if (idx < nq && ids[q2] == e && first[h] == p) first[h] = idx;
+            }
           }
+        }
       }
     }
     bf[h] = __ballot(valid[h] && first[h] == p);

@@ -32,7 +32,11 @@ __device__ __forceinline__ key64 make_key(uint32_t vk, int e) {
 
 // LDS entries of wave_topk's scratch for a given slot count and k, and the
 // slot count used for E experts.
-__host__ __device__ constexpr int topk_scratch(int vpl, int k) { return 64 + k * vpl + k; }
+// (64 lane maxima, up to k*VPL candidates + 2 pad, k ranked outputs; even
+// so that consecutive regions stay 16-byte aligned)
+__host__ __device__ constexpr int topk_scratch(int vpl, int k) {
+  return (64 + (k * vpl + 2) + k + 1) / 2 * 2;
+}
 __host__ __device__ constexpr int topk_vpl(int E) { return E <= 512 ? 8 : (E <= 1024 ? 16 : 32); }
 __host__ __device__ constexpr size_t topk_scratch_bytes(int E, int k) {
   return (size_t)topk_scratch(topk_vpl(E), k) * 8;
@@ -71,8 +75,17 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, 
   scratch[lane] = m;
   wave_lds_fence();
   int r = 0;
-#pragma unroll 8
-  for (int j = 0; j < 64; ++j) r += scratch[j] > m ? 1 : 0;
+  {
+    const uint4* s4 = reinterpret_cast<const uint4*>(scratch);  // 2 keys per read
+    uint4 v[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) v[j] = s4[j];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const key64 a0 = ((key64)v[j].y << 32) | v[j].x, a1 = ((key64)v[j].w << 32) | v[j].z;
+      r += (a0 > m ? 1 : 0) + (a1 > m ? 1 : 0);
+    }
+  }
   const unsigned long long nonempty = __ballot(m != 0ull);
   key64 L = 0ull;
   if (__popcll(nonempty) >= k) {
@@ -83,7 +96,7 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, 
         (key64)(uint32_t)__builtin_amdgcn_readlane((uint32_t)m, src);
   }
   key64* cand = scratch + 64;
-  key64* out = scratch + 64 + k * VPL;
+  key64* out = scratch + 64 + k * VPL + 2;
   int C = 0;
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
@@ -95,10 +108,17 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, 
     C += __popcll(mc);
   }
   wave_lds_fence();
+  if (C & 1) cand[C] = 0ull;  // pad to an even count (a 0 key never outranks)
+  wave_lds_fence();
   for (int j = lane; j < C; j += 64) {
     const key64 c = cand[j];
     int rank = 0;
-    for (int i = 0; i < C; ++i) rank += cand[i] > c ? 1 : 0;
+    const uint4* c4 = reinterpret_cast<const uint4*>(cand);
+    for (int i = 0; i < (C + 1) / 2; ++i) {
+      const uint4 v = c4[i];
+      const key64 a0 = ((key64)v.y << 32) | v.x, a1 = ((key64)v.w << 32) | v.z;
+      rank += (a0 > c ? 1 : 0) + (a1 > c ? 1 : 0);
+    }
     if (rank < k) out[rank] = c;
   }
   wave_lds_fence();

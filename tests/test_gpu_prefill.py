@@ -1,0 +1,155 @@
+"""GPU parity of the prefill path (more than 4 tokens) against the fp64 oracle.
+
+Routing is checked bit-exactly elsewhere (moe_route, moe_permute); here the
+layer output is compared by relative L2 error (bar 5e-3): in full for sizes
+the oracle finishes in seconds (several row tiles, ragged tails, the
+smallest prefill batch), and on sampled tokens for the 8192-token chunk.
+"""
+import numpy as np
+import pytest
+
+import synth
+from oracle import moe_oracle as O
+from helpers import RTOL_L2, OracleWeights, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def g():
+    import gpu_common
+    return gpu_common
+
+
+def _shape(g, w):
+    return g.moe.MoeShape(w["d_model"], w["d_ff"], w["n_experts"], w["top_k"], w["d_ff_shared"],
+                          w["fmt"])
+
+
+@pytest.fixture(scope="module")
+def tiny(g):
+    w = synth.WORKLOADS["tiny"]
+    shape = _shape(g, w)
+    return w, shape, g.build_layer(shape, 0, 0, g.DEV)
+
+
+@pytest.mark.parametrize("T", [5, 64, 131, 300])
+@pytest.mark.parametrize("x_f32", [False, True])
+def test_tiny_prefill(g, tiny, T, x_f32):
+    w, shape, L = tiny
+    D, E = w["d_model"], w["n_experts"]
+    logits = synth.router_logits(0, 7, T, E, min_gap=1e-3)
+    if x_f32:
+        xf = synth.activations_f32(0, 7, T, D)
+        x_dev, x64, xdt = g.f32_to_dev(xf), O.bf16_to_f64(synth.bf16_bits_from_f32(xf)), g.moe.MOE_F32
+    else:
+        xb = synth.activations_bf16(0, 7, T, D)
+        x_dev, x64, xdt = g.u16_to_dev(xb), O.bf16_to_f64(xb), g.moe.MOE_BF16
+    run = g.LayerRun(shape, T)
+    out = run(L.table(), x_dev, xdt, g.f32_to_dev(logits), g.moe.MOE_F32)
+    got = g.out_to_f64(out, False).reshape(T, D)
+    ow = OracleWeights(0, 0, D, w["d_ff"], w["d_ff_shared"], E, w["fmt"])
+    # fp32 activations enter the prefill MFMA path rounded to bf16 (documented);
+    # the oracle gets the exact fp32 input, so the bar covers that rounding too
+    ref, _, _ = O.layer_forward(x64 if not x_f32 else xf.astype(np.float64), logits, w["top_k"],
+                                ow, ow.shared)
+    err = rel_l2(got, ref)
+    print("tiny prefill T=%d x_f32=%s rel_l2=%.3g" % (T, x_f32, err))
+    assert err <= RTOL_L2
+
+
+@pytest.fixture(scope="module")
+def full(g):
+    w = synth.WORKLOADS["prefill_8192"]
+    shape = _shape(g, w)
+    return w, shape, g.build_layer(shape, 0, 0, g.DEV)
+
+
+def test_full_width_prefill_256_tokens(g, full):
+    w, shape, L = full
+    T, D, E = 256, w["d_model"], w["n_experts"]
+    logits = synth.router_logits(0, 3, T, E, zipf_s=1.1, alpha=1.0)
+    xb = synth.activations_bf16(0, 3, T, D)
+    run = g.LayerRun(shape, T)
+    out = run(L.table(), g.u16_to_dev(xb), g.moe.MOE_BF16, g.f32_to_dev(logits), g.moe.MOE_BF16)
+    got = g.out_to_f64(out, True).reshape(T, D)
+    ow = OracleWeights(0, 0, D, w["d_ff"], w["d_ff_shared"], E, w["fmt"])
+    ref, _, _ = O.layer_forward(O.bf16_to_f64(xb), logits, w["top_k"], ow, ow.shared)
+    err = rel_l2(got, ref)
+    print("full-width prefill T=256 rel_l2=%.3g" % err)
+    assert err <= RTOL_L2
+
+
+def test_full_chunk_8192_sampled_tokens(g, full):
+    """The 8192-token chunk at full size: 12 sampled tokens checked one by one."""
+    w, shape, L = full
+    T, D, E, k = w["tokens"], w["d_model"], w["n_experts"], w["top_k"]
+    logits = synth.router_logits(0, 0, T, E, zipf_s=w["zipf_s"], alpha=w["alpha"])
+    xb = synth.activations_bf16(0, 0, T, D)
+    run = g.LayerRun(shape, T)
+    out = run(L.table(), g.u16_to_dev(xb), g.moe.MOE_BF16, g.f32_to_dev(logits), g.moe.MOE_BF16)
+    out2 = run(L.table(), g.u16_to_dev(xb), g.moe.MOE_BF16, g.f32_to_dev(logits), g.moe.MOE_BF16)
+    assert np.array_equal(out.cpu().numpy(), out2.cpu().numpy())   # deterministic
+    got = g.out_to_f64(out, True).reshape(T, D)
+    sample = [0, 1, 127, 128, 4095, 8191] + list(np.random.default_rng(0).choice(T, 6, replace=False))
+    ow = OracleWeights(0, 0, D, w["d_ff"], w["d_ff_shared"], E, w["fmt"])
+    x64 = O.bf16_to_f64(xb)
+    errs = []
+    for t in sample:
+        ref, _, _ = O.layer_forward(x64[t:t + 1], logits[t:t + 1], k, ow, ow.shared)
+        errs.append(rel_l2(got[t:t + 1], ref))
+    print("8192-chunk sampled rel_l2 max=%.3g" % max(errs))
+    assert max(errs) <= RTOL_L2
+
+
+def test_prefill_rmsnorm_input(g, full):
+    w, shape, L = full
+    T, D, E = 40, w["d_model"], w["n_experts"]
+    y = synth.activations_f32(0, 77, T, D) * 3.0
+    logits = synth.router_logits(0, 4, T, E, zipf_s=1.1, alpha=1.0)
+    run = g.LayerRun(shape, T)
+    out = run(L.table(), g.f32_to_dev(y), g.moe.MOE_F32, g.f32_to_dev(logits), g.moe.MOE_F32,
+              flags=g.moe.MOE_FLAG_RMSNORM_INPUT)
+    got = g.out_to_f64(out, False).reshape(T, D)
+    ow = OracleWeights(0, 0, D, w["d_ff"], w["d_ff_shared"], E, w["fmt"])
+    x64 = O.bf16_to_f64(O.rms_chain(y.astype(np.float64)))
+    ref, _, _ = O.layer_forward(x64, logits, w["top_k"], ow, ow.shared)
+    assert rel_l2(got, ref) <= RTOL_L2
+
+
+def test_identical_experts_prefill_equals_dense_swiglu(g):
+    """All routed experts identical: the layer is one dense SwiGLU plus the shared expert."""
+    import torch
+    from synth.device import fill_expert_weights
+    moe = g.moe
+    D, F, E, k, T = 512, 128, 32, 4, 96
+    shape = moe.MoeShape(D, F, E, k, F, moe.MOE_Q2SM32)
+    stride = (moe.moe_packed_expert_bytes(shape, F) + 255) // 256 * 256
+    per = 3 * F * D
+    codes = torch.empty(per, dtype=torch.uint8, device=g.DEV)
+    scale = torch.empty(per // 32, dtype=torch.int16, device=g.DEV)
+    mins = torch.empty_like(scale)
+    fill_expert_weights(0, 9, 3, 1, D, F, 1, codes, scale, mins)
+    one = torch.empty(stride, dtype=torch.uint8, device=g.DEV)
+    moe.moe_pack_weights(shape, 1, F, codes, scale, mins, one, stride)
+    routed = one.repeat(E)
+    sh_c = torch.empty_like(codes); sh_s = torch.empty_like(scale); sh_m = torch.empty_like(mins)
+    fill_expert_weights(0, 9, E, 1, D, F, 1, sh_c, sh_s, sh_m)
+    shared = torch.empty(stride, dtype=torch.uint8, device=g.DEV)
+    moe.moe_pack_weights(shape, 1, F, sh_c, sh_s, sh_m, shared, stride)
+    table = moe.MoeExpertTable(routed.data_ptr(), stride, None, 0, shared.data_ptr())
+    xb = synth.activations_bf16(0, 9, T, D)
+    logits = synth.router_logits(0, 9, T, E)
+    run = g.LayerRun(shape, T)
+    out = run(table, g.u16_to_dev(xb), moe.MOE_BF16, g.f32_to_dev(logits), moe.MOE_F32)
+    got = g.out_to_f64(out, False).reshape(T, D)
+    c, s, m = synth.expert_weights(0, 9, 3, D, F, 1)
+    wg, wu, wd = O.expert_matrices(c, s, m, D, F, 1)
+    c2, s2, m2 = synth.expert_weights(0, 9, E, D, F, 1)
+    sg, su, sd = O.expert_matrices(c2, s2, m2, D, F, 1)
+    x = O.bf16_to_f64(xb)
+    a, b = x @ wg.T, x @ wu.T
+    dense = (a / (1 + np.exp(-a)) * b) @ wd.T
+    a2, b2 = x @ sg.T, x @ su.T
+    dense += (a2 / (1 + np.exp(-a2)) * b2) @ sd.T
+    assert rel_l2(got, dense) <= RTOL_L2
