@@ -37,6 +37,15 @@ if not os.path.exists(LIB_PATH):
         "libmoe.so is not built (%s); run `python bit_expert_ffn_router_amd/build.py` "
         "(hipcc, gfx950)" % LIB_PATH)
 
+# One HIP runtime per process.  torch ships its own libamdhip64 (soname
+# libamdhip64.so.7) and HSA runtime; when torch is loaded first, this
+# library's dependency on libamdhip64.so.7 binds to that copy.  Loaded the
+# other way round, the process would hold two HIP/HSA runtimes side by side,
+# whose kernel launches then fail.  So torch, when installed, goes first.
+try:
+    import torch  # noqa: F401
+except ImportError:
+    pass
 _lib = ctypes.CDLL(LIB_PATH)
 
 

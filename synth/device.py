@@ -16,6 +16,15 @@ from . import tables, FMT_Q2SM
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_synth.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError("libmoe_synth.so is not built; run `python bit_expert_ffn_router_amd/build.py`")
+# One HIP runtime per process.  torch ships its own libamdhip64 (soname
+# libamdhip64.so.7) and HSA runtime; when torch is loaded first, this
+# library's dependency on libamdhip64.so.7 binds to that copy.  Loaded the
+# other way round, the process would hold two HIP/HSA runtimes side by side,
+# whose kernel launches then fail.  So torch, when installed, goes first.
+try:
+    import torch  # noqa: F401
+except ImportError:
+    pass
 _lib = ctypes.CDLL(LIB_PATH)
 _lib.synth_fill_expert_weights.restype = ctypes.c_int
 _lib.synth_fill_expert_weights.argtypes = [
