@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--workloads", default="decode_t1,mtp_verify_t4_48l,prefill_8192,slot_q3s_t1_48l")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-graph", action="store_true", help="launch steps eagerly")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy 4 times (the reference kernel that "
+                         "scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
     return ap.parse_args()
 
 
@@ -366,12 +369,27 @@ def cpu_baseline_decode(budget_s=15.0):
 
 
 # ----------------------------------------------------------------------------
+def copy_calibration():
+    """A plain device-to-device copy of known size: 1 GiB read + 1 GiB written per launch."""
+    import torch
+    n = 1 << 30
+    a = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(4):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": n, "launches": 4}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     wl = [s for s in args.workloads.split(",") if s]
     use_graph = not args.no_graph
     ctx = Ctx()
@@ -415,7 +433,9 @@ def main():
             roofline={"bound": "mfma",
                       "kernel": "pf_gemm_kernel<0> (gate/up grouped GEMM + SwiGLU)",
                       "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                      "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                      "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+                      "traffic": traffic_from_profile("prefill_gateup_8192",
+                                                      ["prefill.hip", "common.hpp", "kernels.hpp"], None),
                       "flops_per_launch": r["flops_per_launch"],
                       "kernel_us": r["kernel_s"] * 1e6})
         print("prefill_8192: %.3f ms/step, gate/up kernel %.1f us (%.1f TFLOP/s)" %
@@ -454,8 +474,9 @@ def main():
             "bound": "hbm", "kernel": "decode_gateup_kernel (dequantising MFMA GEMV + SwiGLU)",
             "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": traffic_from_profile("decode_gateup_t1", ["decode.hip", "common.hpp"],
-                                            prim["bytes_per_launch"]),
+            "traffic": traffic_from_profile(
+                "decode_gateup_t1", ["decode.hip", "common.hpp", "route_common.hpp", "kernels.hpp"],
+                prim["bytes_per_launch"]),
             "bytes_per_launch": prim["bytes_per_launch"],
             "kernel_us": prim["kernel_s"] * 1e6,
         }

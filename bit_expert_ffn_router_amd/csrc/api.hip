@@ -71,16 +71,6 @@ KernelTimer& kernel_timer() {
   return t;
 }
 
-hipError_t record_timer_event(hipEvent_t ev, hipStream_t st) {
-  if (!ev) return hipSuccess;
-  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-  hipError_t e = hipStreamIsCapturing(st, &cs);
-  if (e != hipSuccess) return e;
-  return hipEventRecordWithFlags(ev, st,
-                                 cs == hipStreamCaptureStatusActive ? hipEventRecordExternal
-                                                                    : hipEventRecordDefault);
-}
-
 }  // namespace moe
 
 extern "C" {

@@ -168,8 +168,8 @@ __device__ __forceinline__ void decode_build_list(const DecodeArgs& a, const Dec
   for (int i = lane; i < nu * 4; i += 64) R.wg[i] = 0.f;
   wave_lds_sync();
   auto list_index = [&](int fp) {  // list index of the pair that first named an expert
-    const int hh = fp >> 6;
-    return (hh ? nf0 : 0) + __popcll(bf[hh] & ((1ull << (fp & 63)) - 1ull));
+    const unsigned long long b = fp >= 64 ? bf[1] : bf[0];   // no run-time array index
+    return (fp >= 64 ? nf0 : 0) + __popcll(b & ((1ull << (fp & 63)) - 1ull));
   };
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -338,7 +338,9 @@ __global__ __launch_bounds__(kGuThreads, 2) void decode_gateup_kernel(DecodeArgs
 #pragma unroll
   for (int j = 0; j < XJ; ++j) {
     const int i = tid + kGuThreads * j;
-    if (i < nin) xr[j] = reinterpret_cast<const uint4*>(a.x)[i];
+    // clamped index + select: every element defined, so the array stays in VGPRs
+    const uint4 v = reinterpret_cast<const uint4*>(a.x)[i < nin ? i : 0];
+    xr[j] = i < nin ? v : make_uint4(0, 0, 0, 0);
   }
   // 1. Routing of token wv (waves 0..T-1).
   if (wv < T) decode_route_token(a, R, wv, lane);
@@ -557,11 +559,11 @@ __global__ __launch_bounds__(1024) void decode_down_kernel(DecodeArgs a, DecodeW
       uint4 hv[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int i = j0 + lane + 64 * j;  // i over [T][2][hrow]
-        if (i < nh) {
-          const int t = i / (2 * hrow), rem = i % (2 * hrow);
-          hv[j] = rem < hrow ? gh[t * hrow + rem] : gl[t * hrow + rem - hrow];
-        }
+        const int i0 = j0 + lane + 64 * j;  // i over [T][2][hrow]
+        const int i = i0 < nh ? i0 : 0;     // clamped: all four loads issue unconditionally
+        const int t = i / (2 * hrow), rem = i % (2 * hrow);
+        const uint4* src = rem < hrow ? gh + t * hrow + rem : gl + t * hrow + rem - hrow;
+        hv[j] = *src;
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -641,11 +643,9 @@ static hipError_t launch_decode_x(const DecodeArgs& a, const DecodeWs& w, hipStr
   if ((e = allow_lds(decode_down_kernel<T, FMT>, lds_down, lds_dn)) != hipSuccess) return e;
   const int Wr = w.Wmax - 1;
   const int nblk = Wr * (a.F / 16) + (a.shared ? a.Fs / 16 : 0);
-  KernelTimer& tm = kernel_timer();
-  if ((e = record_timer_event(tm.before, st)) != hipSuccess) return e;
-  decode_gateup_kernel<T, FMT, XM><<<nblk, kGuThreads, lds, st>>>(a, w);
-  if ((e = record_timer_event(tm.after, st)) != hipSuccess) return e;
-  tm.before = tm.after = nullptr;
+  if ((e = launch_timed(decode_gateup_kernel<T, FMT, XM>, dim3(nblk), dim3(kGuThreads),
+                        (uint32_t)lds, st, a, w)) != hipSuccess)
+    return e;
   decode_down_kernel<T, FMT><<<a.D / 16, 1024, lds_down, st>>>(a, w);
   return hipGetLastError();
 }

@@ -1,6 +1,8 @@
 // Internal launch interface between the C ABI (api.hip) and the kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
+
 #include "common.hpp"
 
 namespace moe {
@@ -17,8 +19,30 @@ struct KernelTimer {
   hipEvent_t before = nullptr, after = nullptr;
 };
 KernelTimer& kernel_timer();
-// Record ev on st (as an external node when st is capturing); no-op for NULL.
-hipError_t record_timer_event(hipEvent_t ev, hipStream_t st);
+
+// Launch `kernel` on st.  When the calling thread has armed the kernel timer,
+// the launch carries its two events (hipExtLaunchKernel), which then take the
+// kernel's own start and end timestamps, and the timer is disarmed.  A timed
+// launch is refused while st is capturing a graph.
+template <typename... P, typename... A>
+hipError_t launch_timed(void (*kernel)(P...), dim3 grid, dim3 block, uint32_t lds, hipStream_t st,
+                        A... args) {
+  static_assert(sizeof...(P) == sizeof...(A), "argument count");
+  KernelTimer& tm = kernel_timer();
+  if (tm.before == nullptr) {
+    kernel<<<grid, block, lds, st>>>(args...);
+    return hipGetLastError();
+  }
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(st, &cs);
+  if (e != hipSuccess) return e;
+  if (cs != hipStreamCaptureStatusNone) return hipErrorStreamCaptureUnsupported;
+  void* argv[] = {(void*)&args...};
+  e = hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, lds, st,
+                         tm.before, tm.after, 0);
+  tm.before = tm.after = nullptr;
+  return e;
+}
 
 // ---------------------------------------------------------------- packing
 hipError_t launch_pack(int fmt, int D, int F, int n, const void* codes, const uint16_t* scale,

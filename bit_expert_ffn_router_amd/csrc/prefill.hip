@@ -433,12 +433,10 @@ hipError_t launch_prefill(const PrefillArgs& pa, void* ws, hipStream_t st) {
   a.out_bf16 = pa.out_bf16;
   const int nN_gu = (2 * w.Fmax + kBN - 1) / kBN;
   const int nN_dn = (D + kBN - 1) / kBN;
-  KernelTimer& tm = kernel_timer();
-  if ((e = record_timer_event(tm.before, st)) != hipSuccess) return e;
   const int nw_gu = w.max_tiles * nN_gu, nw_dn = w.max_tiles * nN_dn;
-  pf_gemm_kernel<0><<<(nw_gu + 7) / 8 * 8, kPfThreads, 0, st>>>(a, nN_gu, nw_gu);
-  if ((e = record_timer_event(tm.after, st)) != hipSuccess) return e;
-  tm.before = tm.after = nullptr;
+  if ((e = launch_timed(pf_gemm_kernel<0>, dim3((nw_gu + 7) / 8 * 8), dim3(kPfThreads), 0u, st, a,
+                        nN_gu, nw_gu)) != hipSuccess)
+    return e;
   pf_gemm_kernel<1><<<(nw_dn + 7) / 8 * 8, kPfThreads, 0, st>>>(a, nN_dn, nw_dn);
   pf_combine_kernel<<<T, 256, 0, st>>>(a, has_sh);
   return hipGetLastError();

@@ -258,12 +258,13 @@ moe_status moe_permute(const int32_t* idx, int32_t tokens, int32_t top_k, int32_
 
 /* Profiling aid: time the dominant kernel of the calling thread's next
  * moe_layer_forward call.  `before` and `after` are hipEvent_t handles
- * created by the caller with timing enabled; the call records `before` on
- * its stream just before launching the dominant kernel (decode path: the
- * gate/up GEMV; prefill path: the gate/up grouped GEMM) and `after` just
- * after it, then forgets both.  Under stream capture the records become
- * external event nodes of the graph.  NULL, NULL clears a pending pair.
- * Thread-local; no device work is done by this call itself. */
+ * created by the caller with timing enabled.  The forward call attaches both
+ * to the launch of its dominant kernel (decode path: the gate/up GEMV;
+ * prefill path: the gate/up grouped GEMM) through hipExtLaunchKernel, so
+ * they take that kernel's own start and end timestamps, then forgets both.
+ * A forward call on a stream that is capturing a graph fails while a pair is
+ * armed (MOE_EHIP: stream capture unsupported).  NULL, NULL clears a pending
+ * pair.  Thread-local; no device work is done by this call itself. */
 moe_status moe_set_kernel_timer(void* before, void* after);
 
 /* The calling thread's message for its last failed call ("" if none). */
