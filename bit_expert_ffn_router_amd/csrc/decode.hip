@@ -11,16 +11,23 @@
 // "命中率七成，代价是答案会变").  So the kernels stream each distinct selected
 // expert's packed bytes exactly once for all tokens that chose it.
 //
+// The list of experts a call computes holds the shared expert first (index
+// 0, when there is one), then the distinct resident routed experts in order
+// of first occurrence over (token, rank).
+//
 // Two launches:
-//   decode_gateup:  one block per (listed expert, 16 FFN rows).  Every block
-//                   first routes the tokens itself (top-k + gates, the list of
-//                   distinct resident experts in first-occurrence order, the
-//                   miss list) while its other waves stage the activations in
-//                   LDS; block 0 publishes the list for the second kernel.
-//                   Then: dequantising MFMA GEMV of W_gate and W_up, SwiGLU,
-//                   h in bf16 hi + lo with per-block sums.
+//   decode_gateup:  blocks [0, d_ff_shared/16) compute 16 FFN rows of the
+//                   shared expert each and stream its weights at once.  The
+//                   other blocks are (routed list entry, 16 FFN rows); they
+//                   route the tokens themselves first.  With one token every
+//                   wave routes it, so each wave knows its expert without
+//                   waiting for another; with 2..4 tokens wave t routes token
+//                   t and wave 0 builds the list and the miss list.  The
+//                   first routed block publishes the list for the second
+//                   kernel.  Then: dequantising MFMA GEMV of W_gate and W_up,
+//                   SwiGLU, h in bf16 hi + lo with per-block sums.
 //   decode_down:    one block per 16 output rows: W_down GEMV of every listed
-//                   expert, gate-weighted sum in a fixed order, output write.
+//                   expert, gate-weighted sum in list order, output write.
 //
 // Dequantisation (see DqConsts): a code word is turned into bf16 operands
 // (c + u) with one VALU op per pair of weights plus shared shifts and no
@@ -42,7 +49,8 @@ constexpr int kMaxDecodeFOct = 2;  // d_ff, d_ff_shared <= 512 on the decode pat
 // Activation modes of the gate/up kernel.
 constexpr int kXBf16 = 0;  // bf16 input, used as is
 constexpr int kXF32 = 1;   // fp32 input, as bf16 hi + bf16 lo (two MFMAs)
-constexpr int kXRms = 2;   // input normalised to bf16(x / sqrt(mean(x^2) + 1e-6))
+constexpr int kXRms = 2;     // bf16 input normalised to bf16(x / sqrt(mean(x^2) + 1e-6))
+constexpr int kXRmsF32 = 3;  // fp32 input, same rule
 
 __host__ __device__ inline size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
@@ -79,13 +87,11 @@ DecodeWs decode_ws_carve(void* ws, int T, int D, int F, int Fs, int E, int k) {
 }
 
 // ----------------------------------------------------------------------------
-// Routing inside a decode block.  Waves 0..T-1 route one token each; then
-// wave 0 builds the list of distinct resident experts in (token, rank) order
-// of first occurrence with their per-token gates, and the miss list.  Every
-// block computes the same list; block 0 also publishes it (and the misses).
+// Routing inside a decode block.
+
+// Routing results of 2..4 tokens and the list built from them.
 struct RouteLds {
-  key64* scr;  // T regions of topk_scratch_bytes(E, k) in dynamic LDS
-  alignas(16) int32_t e[kDecodeMaxT * kMaxTopK];
+  int32_t e[kDecodeMaxT * kMaxTopK];
   float g[kDecodeMaxT * kMaxTopK];
   int32_t ref[kDecodeMaxT * kMaxTopK + 1];
   float wg[(kDecodeMaxT * kMaxTopK + 1) * 4];
@@ -98,19 +104,15 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__device__ __forceinline__ void decode_route_token(const DecodeArgs& a, RouteLds& R, int t,
-                                                   int lane) {
-  int my_e;
-  float my_l;
-  wave_topk_any(a.logits + (size_t)t * a.E, a.E, a.k, lane, my_e, my_l,
-                R.scr + t * (topk_scratch_bytes(a.E, a.k) / 8));
-  const float g = wave_gate(my_l, a.k, lane);
-  if (lane < a.k) {
-    // never let an id outside 0..E-1 become an address (cannot happen for
-    // finite logits; the clamp keeps a fault out of the weight streams)
-    R.e[t * a.k + lane] = my_e < 0 ? 0 : (my_e >= a.E ? a.E - 1 : my_e);
-    R.g[t * a.k + lane] = g;
-  }
+// Top-k of token t by the calling wave: lane j < k gets the j-th expert and
+// its gate.  The id is clamped into 0..E-1 (it always is for finite logits;
+// the clamp keeps a wild id out of the weight addresses).
+__device__ __forceinline__ void route_token(const DecodeArgs& a, int t, int lane, int& e,
+                                            float& g) {
+  float l;
+  wave_topk_any(a.logits + (size_t)t * a.E, a.E, a.k, lane, e, l);
+  g = wave_gate(l, a.k, lane);
+  e = e < 0 ? 0 : (e >= a.E ? a.E - 1 : e);
 }
 
 // Slot of expert e, or -1 when not resident (a slot outside 0..n_slots-1 in
@@ -121,67 +123,96 @@ __device__ __forceinline__ int resident_ref(const DecodeArgs& a, int e) {
   return (s >= 0 && s < a.n_slots) ? s : -1;
 }
 
-// Wave 0 only, after every token's routing is visible in LDS.
+// One token: lane j < k holds expert e, gate g and residency ref (-1 = miss);
+// `hits` has bit j set for resident ranks.  Hit i (in rank order) is list
+// entry base + i.  Writes the list, the routing and the miss list.
+__device__ __forceinline__ void publish_t1(const DecodeArgs& a, const DecodeWs& w, int lane, int e,
+                                           float g, int ref, unsigned long long hits, int base) {
+  const int k = a.k;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  const unsigned long long kmask = (1ull << k) - 1ull;  // k <= 32
+  if (lane < k) {
+    w.idx[lane] = e;
+    w.gate[lane] = g;
+    if ((hits >> lane) & 1ull) {
+      const int i = base + __popcll(hits & below);
+      w.work_ref[i] = ref;
+      w.work_gate[4 * i] = g;
+    } else {
+      MissRec r;
+      r.token = 0;
+      r.rank = lane;
+      r.expert = e;
+      r.gate = g;
+      a.miss[__popcll(~hits & kmask & below)] = r;
+    }
+  }
+  if (lane == 0) {
+    if (base) {
+      w.work_ref[0] = -1;
+      w.work_gate[0] = 1.0f;
+    }
+    *w.nwork = base + __popcll(hits);
+    if (a.miss_count) *a.miss_count = k - __popcll(hits);
+  }
+}
+
+// 2..4 tokens, wave 0, once every token's routing is in R.e / R.g.  The
+// first occurrence of each resident expert comes from a table in LDS indexed
+// by expert (only the entries of named experts are touched): every pair
+// stores INT_MAX, then each hit takes the atomic minimum of its pair index.
+// Builds R.ref / R.wg / R.nu (shared entry first when base = 1); `publish`
+// also writes them, the routing and the miss list to the workspace.
 template <int T>
-__device__ __forceinline__ void decode_build_list(const DecodeArgs& a, const DecodeWs& w,
-                                                  RouteLds& R, int lane, bool publish) {
+__device__ __forceinline__ void build_list(const DecodeArgs& a, const DecodeWs& w, RouteLds& R,
+                                           int32_t* s_first, int lane, bool publish, int base) {
   const int k = a.k, P = T * k;  // P <= 128: lane handles pairs lane, lane + 64
-  int first[2];
+  int e[2], ref[2], tok[2], first[2];
   bool valid[2], hit[2];
-  unsigned long long bf[2], bm[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int p = lane + 64 * h;
     valid[h] = p < P;
-    first[h] = -1;
-    hit[h] = false;
-    if (valid[h]) {
-      const int e = R.e[p];
-      hit[h] = resident_ref(a, e) >= 0;
-      if (hit[h]) {
-        // first (token, rank) pair naming the same expert; one token's ids
-        // are distinct, so only pairs of earlier tokens can match
-        first[h] = p;
-        if (T > 1) {
-          const int4* e4 = reinterpret_cast<const int4*>(R.e);
-          const int nq = (p / k) * k;  // pairs of earlier tokens
-          for (int c = 0; c < (nq + 3) / 4; ++c) {
-            const int4 v = e4[c];
-            const int ids[4] = {v.x, v.y, v.z, v.w};
+    e[h] = valid[h] ? R.e[p] : 0;
+    ref[h] = valid[h] ? resident_ref(a, e[h]) : -1;
+    hit[h] = valid[h] && ref[h] >= 0;
+    tok[h] = (p >= k ? 1 : 0) + (p >= 2 * k ? 1 : 0) + (p >= 3 * k ? 1 : 0);
+    if (valid[h]) s_first[e[h]] = 0x7FFFFFFF;
+  }
+  wave_lds_sync();
 #pragma unroll
-            for (int q2 = 0; q2 < 4; ++q2) {
-              const int idx = 4 * c + q2;
-              if (idx < nq && ids[q2] == e && first[h] == p) first[h] = idx;
-            }
-          }
-        }
-      }
-    }
-    bf[h] = __ballot(valid[h] && first[h] == p);
+  for (int h = 0; h < 2; ++h)
+    if (hit[h]) atomicMin(&s_first[e[h]], lane + 64 * h);
+  wave_lds_sync();
+  unsigned long long bf[2], bm[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int p = lane + 64 * h;
+    first[h] = hit[h] ? s_first[e[h]] : -1;
+    bf[h] = __ballot(hit[h] && first[h] == p);
     bm[h] = __ballot(valid[h] && !hit[h]);
   }
   const int nf0 = __popcll(bf[0]), nm0 = __popcll(bm[0]);
   const int U = nf0 + __popcll(bf[1]);
   const int M = nm0 + __popcll(bm[1]);
-  const bool has_sh = a.shared != nullptr;
-  const int nu = U + (has_sh ? 1 : 0);
+  const int nu = base + U;
   for (int i = lane; i < nu * 4; i += 64) R.wg[i] = 0.f;
   wave_lds_sync();
-  auto list_index = [&](int fp) {  // list index of the pair that first named an expert
-    const unsigned long long b = fp >= 64 ? bf[1] : bf[0];   // no run-time array index
-    return (fp >= 64 ? nf0 : 0) + __popcll(b & ((1ull << (fp & 63)) - 1ull));
+  auto list_index = [&](int fp) {  // list entry of the pair that first named an expert
+    const unsigned long long m = fp >= 64 ? bf[1] : bf[0];
+    return base + (fp >= 64 ? nf0 : 0) + __popcll(m & ((1ull << (fp & 63)) - 1ull));
   };
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int p = lane + 64 * h;
-    if (valid[h] && first[h] == p) R.ref[list_index(p)] = resident_ref(a, R.e[p]);
-    if (valid[h] && first[h] >= 0) R.wg[list_index(first[h]) * 4 + p / k] = R.g[p];
+    if (hit[h] && first[h] == p) R.ref[list_index(p)] = ref[h];
+    if (hit[h]) R.wg[list_index(first[h]) * 4 + tok[h]] = R.g[p];
   }
   if (lane == 0) {
     R.nu = nu;
-    if (has_sh) R.ref[U] = -1;
+    if (base) R.ref[0] = -1;
   }
-  if (has_sh && lane < T) R.wg[U * 4 + lane] = 1.0f;
+  if (base && lane < T) R.wg[lane] = 1.0f;
   wave_lds_sync();
   if (!publish) return;
   for (int i = lane; i < nu; i += 64) w.work_ref[i] = R.ref[i];
@@ -199,9 +230,9 @@ __device__ __forceinline__ void decode_build_list(const DecodeArgs& a, const Dec
     const int p = lane + 64 * h;
     if (valid[h] && !hit[h]) {
       MissRec r;
-      r.token = p / k;
-      r.rank = p % k;
-      r.expert = R.e[p];
+      r.token = tok[h];
+      r.rank = p - tok[h] * k;
+      r.expert = e[h];
       r.gate = R.g[p];
       a.miss[(h ? nm0 : 0) + __popcll(bm[h] & ((1ull << lane) - 1ull))] = r;
     }
@@ -306,12 +337,26 @@ __device__ __forceinline__ void load_record(const uint8_t* rec, int lane, uint4&
   }
 }
 
+// Sums over groups of 4 / 8 consecutive lanes (DPP quad swaps, half-row
+// mirror); every lane of the group gets the group sum.
+__device__ __forceinline__ float dpp_add(float v, uint32_t other) { return v + __uint_as_float(other); }
+__device__ __forceinline__ float quad_sum(float v) {
+  v = dpp_add(v, dpp_u32<kDppQuadSwap1, 0xF>(0u, __float_as_uint(v)));
+  return dpp_add(v, dpp_u32<kDppQuadSwap2, 0xF>(0u, __float_as_uint(v)));
+}
+__device__ __forceinline__ float oct_sum(float v) {
+  v = quad_sum(v);
+  return dpp_add(v, dpp_u32<kDppRowHalfMirror, 0xF>(0u, __float_as_uint(v)));
+}
+
 // ----------------------------------------------------------------------------
-// decode_gateup.  Grid: (routed capacity x F/16) + Fs/16 blocks of 256
-// threads, two blocks per CU.  Every thread first issues its share of the
-// activation loads, then waves 0..T-1 route; after the list is known, wave w
-// computes matrix w/2 (gate, up) over the K octets o = w%2, w%2 + 2, ... of
-// one 16-row h-group.
+// decode_gateup.  Grid: d_ff_shared/16 shared-expert blocks, then
+// (routed list capacity x d_ff/16) blocks, of 256 threads, two blocks per
+// CU.  A routed block first routes (see above) and drops out when its list
+// entry is not used.  Then every block issues its weight loads -- wave w
+// holds matrix w/2 (gate, up) over the K octets o = w%2, w%2 + 2, ... of one
+// 16-row h-group -- and, while they are in flight, the activation loads, the
+// input rule, the bf16 operand(s) in LDS and the per-32-block activation sums.
 template <int T, int FMT, int XM>
 __global__ __launch_bounds__(kGuThreads, 2) void decode_gateup_kernel(DecodeArgs a, DecodeWs w) {
   extern __shared__ uint4 s_dyn[];
@@ -321,124 +366,62 @@ __global__ __launch_bounds__(kGuThreads, 2) void decode_gateup_kernel(DecodeArgs
   constexpr bool HAS_LO = XM == kXF32;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int D = a.D, oD = octets(D), nbD = D / 32, D8 = D / 8;
-  uint4* s_xhi = s_dyn;                                            // [T][D/8]
-  uint4* s_xlo = s_dyn + T * D8;                                   // [T][D/8]
-  float2* s_xs = reinterpret_cast<float2*>(s_dyn + (HAS_LO ? 2 : 1) * T * D8);   // [T][D/32]
-  float* s_raw = reinterpret_cast<float*>(s_xs + T * nbD);         // [T][D] (XM == kXRms)
-  if (tid == 0)
-    R.scr = reinterpret_cast<key64*>(reinterpret_cast<uint8_t*>(s_raw) +
-                                     (XM == kXRms ? (size_t)T * D * 4 : 0));
-  __syncthreads();
+  uint4* s_xhi = s_dyn;                                                         // [T][D/8]
+  uint4* s_xlo = s_dyn + T * D8;                                                // [T][D/8]
+  float2* s_xs = reinterpret_cast<float2*>(s_dyn + (HAS_LO ? 2 : 1) * T * D8);  // [T][D/32]
+  int32_t* s_first = reinterpret_cast<int32_t*>(s_xs + T * nbD);                // [E], T > 1
 
-  // 0. Activation loads in flight before routing (16-byte pieces of the input).
-  const bool in_bf16 = XM == kXBf16 || a.x_bf16;
-  const int nin = in_bf16 ? T * D8 : 2 * T * D8;          // 16-byte pieces of x
-  constexpr int XJ = (XM == kXBf16 ? 2 : 4) * T;          // pieces per thread, D <= 4096
-  uint4 xr[XJ];
-#pragma unroll
-  for (int j = 0; j < XJ; ++j) {
-    const int i = tid + kGuThreads * j;
-    // clamped index + select: every element defined, so the array stays in VGPRs
-    const uint4 v = reinterpret_cast<const uint4*>(a.x)[i < nin ? i : 0];
-    xr[j] = i < nin ? v : make_uint4(0, 0, 0, 0);
-  }
-  // 1. Routing of token wv (waves 0..T-1).
-  if (wv < T) decode_route_token(a, R, wv, lane);
-  // 2. Activations to LDS: the bf16 operand (hi, and lo for fp32 input), or
-  // fp32 values and per-token sums of squares for the normalised mode.
-  float ss[T];
-#pragma unroll
-  for (int t = 0; t < T; ++t) ss[t] = 0.f;
-#pragma unroll
-  for (int j = 0; j < XJ; ++j) {
-    const int i = tid + kGuThreads * j;
-    if (i >= nin) continue;
-    if (XM == kXBf16) {
-      s_xhi[i] = xr[j];
-    } else if (XM == kXF32) {  // piece i = fp32 elements 4i..4i+3
-      const float v[4] = {__uint_as_float(xr[j].x), __uint_as_float(xr[j].y),
-                          __uint_as_float(xr[j].z), __uint_as_float(xr[j].w)};
-      uint32_t hi[2], lo[2];
-#pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2) {
-        const uint16_t h0 = f32_to_bf16(v[2 * q2]), h1 = f32_to_bf16(v[2 * q2 + 1]);
-        hi[q2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-        lo[q2] = pack_bf16x2(v[2 * q2] - bf16_to_f32(h0), v[2 * q2 + 1] - bf16_to_f32(h1));
-      }
-      reinterpret_cast<uint2*>(s_xhi)[i] = make_uint2(hi[0], hi[1]);
-      reinterpret_cast<uint2*>(s_xlo)[i] = make_uint2(lo[0], lo[1]);
-    } else {  // kXRms
-      float q2 = 0.f;
-      int t;
-      if (in_bf16) {  // piece i = bf16 elements 8i..8i+7
-        const uint32_t qq[4] = {xr[j].x, xr[j].y, xr[j].z, xr[j].w};
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          const float v0 = bf16_lo(qq[e2]), v1 = bf16_hi(qq[e2]);
-          s_raw[8 * i + 2 * e2] = v0;
-          s_raw[8 * i + 2 * e2 + 1] = v1;
-          q2 += v0 * v0 + v1 * v1;
-        }
-        t = i / D8;
-      } else {        // piece i = fp32 elements 4i..4i+3
-        const float v[4] = {__uint_as_float(xr[j].x), __uint_as_float(xr[j].y),
-                            __uint_as_float(xr[j].z), __uint_as_float(xr[j].w)};
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          s_raw[4 * i + e2] = v[e2];
-          q2 += v[e2] * v[e2];
-        }
-        t = i / (2 * D8);
-      }
-#pragma unroll
-      for (int tt = 0; tt < T; ++tt) ss[tt] += tt == t ? q2 : 0.f;
-    }
-  }
-  if (XM == kXRms) {
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-      const float r = wave_sum(ss[t]);
-      if (lane == 0) s_ss[wv][t] = r;
-    }
-  }
-  __syncthreads();
-  if (XM == kXRms) {
-    for (int i = tid; i < T * D8; i += kGuThreads) {
-      const int t = i / D8;
-      float ssum = 0.f;
-#pragma unroll
-      for (int w2 = 0; w2 < kGuWaves; ++w2) ssum += s_ss[w2][t];
-      const float rinv = 1.0f / sqrtf(ssum / (float)D + 1e-6f);
-      uint32_t hi[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        hi[j] = pack_bf16x2(s_raw[8 * i + 2 * j] * rinv, s_raw[8 * i + 2 * j + 1] * rinv);
-      s_xhi[i] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-    }
-  }
-  if (wv == 0) decode_build_list<T>(a, w, R, lane, blockIdx.x == 0);
-  __syncthreads();
-
-  // 3. This block's work item.
+  // 0. This block's work: shared-expert rows, or a routed list entry.
   const int has_sh = a.shared != nullptr;
-  const int U = R.nu - has_sh;
-  const int Wr = w.Wmax - 1, gpr = a.F / 16;
+  const int nsh = has_sh ? a.Fs / 16 : 0;
+  const int gpr = a.F / 16;
   int u, g;
-  const uint8_t* base;
-  if ((int)blockIdx.x < Wr * gpr) {
-    u = blockIdx.x / gpr;
-    g = blockIdx.x % gpr;
-    if (u >= U) return;
-    base = a.routed + (size_t)R.ref[u] * a.stride;
+  const uint8_t* eb;
+  if ((int)blockIdx.x < nsh) {
+    u = 0;
+    g = blockIdx.x;
+    eb = a.shared;
   } else {
-    if (!has_sh) return;
-    g = blockIdx.x - Wr * gpr;
-    u = U;
-    base = a.shared;
+    const int rb = (int)blockIdx.x - nsh;
+    const int ui = rb / gpr;
+    g = rb % gpr;
+    int ref;
+    if (T == 1) {
+      int e;
+      float gt;
+      route_token(a, 0, lane, e, gt);
+      const int rl = lane < a.k ? resident_ref(a, e) : -1;
+      const unsigned long long hits = __ballot(lane < a.k && rl >= 0);
+      if (rb == 0 && wv == 0) publish_t1(a, w, lane, e, gt, rl, hits, has_sh);
+      if (ui >= __popcll(hits)) return;  // same in every wave of the block
+      const unsigned long long below = (1ull << lane) - 1ull;
+      const unsigned long long pick =
+          __ballot(((hits >> lane) & 1ull) && __popcll(hits & below) == ui);
+      ref = __builtin_amdgcn_readlane(rl, __builtin_ctzll(pick));
+    } else {
+      if (wv < T) {
+        int e;
+        float gt;
+        route_token(a, wv, lane, e, gt);
+        if (lane < a.k) {
+          R.e[wv * a.k + lane] = e;
+          R.g[wv * a.k + lane] = gt;
+        }
+      }
+      __syncthreads();
+      if (wv == 0) build_list<T>(a, w, R, s_first, lane, rb == 0, has_sh);
+      __syncthreads();
+      if (has_sh + ui >= R.nu) return;
+      ref = R.ref[has_sh + ui];
+    }
+    u = has_sh + ui;
+    eb = a.routed + (size_t)ref * a.stride;
   }
+
+  // 1. Weight loads of this wave.
   const int mat = wv >> 1, kh = wv & 1;
   const int n = lane & 15, q = lane >> 4;
-  const uint8_t* tile = base + (size_t)(g * 2 + mat) * oD * rec_bytes(FMT);
+  const uint8_t* tile = eb + (size_t)(g * 2 + mat) * oD * rec_bytes(FMT);
   uint4 cw[kMaxOctPerWave], pa[kMaxOctPerWave], pb[kMaxOctPerWave];
   uint2 hw[kMaxOctPerWave];
 #pragma unroll
@@ -446,27 +429,123 @@ __global__ __launch_bounds__(kGuThreads, 2) void decode_gateup_kernel(DecodeArgs
     const int o = kh + 2 * i;
     if (o < oD) load_record<FMT>(tile + (size_t)o * rec_bytes(FMT), lane, cw[i], hw[i], pa[i], pb[i]);
   }
-  // Per-block activation sums X = sum x and X' = sum c x (while the weights arrive).
-  for (int i = tid; i < T * nbD; i += kGuThreads) {
-    const int t = i / nbD, b = i % nbD;
-    float X = 0.f, Xc = 0.f;
+
+  // 2. Activations (16-byte pieces; every element defined, so the array
+  // stays in registers).
+  constexpr bool in_bf16 = XM == kXBf16 || XM == kXRms;
+  constexpr bool RMS = XM == kXRms || XM == kXRmsF32;
+  const int nin = in_bf16 ? T * D8 : 2 * T * D8;
+  constexpr int XJ = (in_bf16 ? 2 : 4) * T;  // pieces per thread, D <= 4096
+  uint4 xr[XJ];
 #pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
-      const uint4 vh = s_xhi[t * D8 + 4 * b + qq];
-      const uint4 vl = HAS_LO ? s_xlo[t * D8 + 4 * b + qq] : make_uint4(0, 0, 0, 0);
-      const uint32_t hh[4] = {vh.x, vh.y, vh.z, vh.w}, ll[4] = {vl.x, vl.y, vl.z, vl.w};
+  for (int j = 0; j < XJ; ++j) {
+    const int i = tid + kGuThreads * j;
+    const uint4 v = reinterpret_cast<const uint4*>(a.x)[i < nin ? i : 0];
+    xr[j] = i < nin ? v : make_uint4(0, 0, 0, 0);
+  }
+  float rinv[T];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float v = bf16_lo(hh[j]) + bf16_lo(ll[j]) + bf16_hi(hh[j]) + bf16_hi(ll[j]);
-        X += v;
-        Xc += dq_offset(b & 1, j) * v;
+  for (int t = 0; t < T; ++t) rinv[t] = 1.f;
+  if (RMS) {
+    float ss[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) ss[t] = 0.f;
+#pragma unroll
+    for (int j = 0; j < XJ; ++j) {
+      const int i = tid + kGuThreads * j;
+      const int t = in_bf16 ? i / D8 : i / (2 * D8);
+      const uint32_t qq[4] = {xr[j].x, xr[j].y, xr[j].z, xr[j].w};
+      float q2 = 0.f;
+      if (in_bf16) {
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) q2 += bf16_lo(qq[e2]) * bf16_lo(qq[e2]) + bf16_hi(qq[e2]) * bf16_hi(qq[e2]);
+      } else {
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) q2 += __uint_as_float(qq[e2]) * __uint_as_float(qq[e2]);
       }
+#pragma unroll
+      for (int tt = 0; tt < T; ++tt) ss[tt] += tt == t ? q2 : 0.f;  // invalid pieces are 0
     }
-    s_xs[i] = make_float2(X, Xc);
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const float r = wave_sum_f32(ss[t]);
+      if (lane == 0) s_ss[wv][t] = r;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      float ssum = 0.f;
+#pragma unroll
+      for (int w2 = 0; w2 < kGuWaves; ++w2) ssum += s_ss[w2][t];
+      rinv[t] = 1.0f / sqrtf(ssum / (float)D + 1e-6f);
+    }
+  }
+  // bf16 operand(s) to LDS, and per-block sums X = sum x, X' = sum c x of the
+  // operand values (lanes holding the pieces of one block combine by DPP).
+#pragma unroll
+  for (int j = 0; j < XJ; ++j) {
+    const int i = tid + kGuThreads * j;
+    const bool ok = i < nin;
+    float X = 0.f, Xc = 0.f;
+    if (in_bf16) {  // piece i = bf16 elements 8(i % D8) .. +7 of token i / D8
+      const int t = i / D8, pc = i % D8, b = pc >> 2;
+      const uint32_t qq[4] = {xr[j].x, xr[j].y, xr[j].z, xr[j].w};
+      uint32_t hi[4];
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        if (RMS) {
+          const float r = rinv[0] * (t == 0) + (T > 1 ? rinv[T > 1 ? 1 : 0] * (t == 1) : 0.f) +
+                          (T > 2 ? rinv[T > 2 ? 2 : 0] * (t == 2) : 0.f) +
+                          (T > 3 ? rinv[T > 3 ? 3 : 0] * (t == 3) : 0.f);
+          hi[e2] = pack_bf16x2(bf16_lo(qq[e2]) * r, bf16_hi(qq[e2]) * r);
+        } else {
+          hi[e2] = qq[e2];
+        }
+        const float v = bf16_lo(hi[e2]) + bf16_hi(hi[e2]);
+        X += v;
+        Xc += dq_offset(b & 1, e2) * v;
+      }
+      if (ok) s_xhi[i] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      X = quad_sum(X);
+      Xc = quad_sum(Xc);
+      if (ok && (pc & 3) == 0) s_xs[t * nbD + b] = make_float2(X, Xc);
+    } else {  // piece i = fp32 elements 4(i % 2D8) .. +3 of token i / (2 D8)
+      const int t = i / (2 * D8), pc = i % (2 * D8), b = pc >> 3, j0 = 2 * (pc & 1);
+      const float v4[4] = {__uint_as_float(xr[j].x), __uint_as_float(xr[j].y),
+                           __uint_as_float(xr[j].z), __uint_as_float(xr[j].w)};
+      uint32_t hi[2], lo[2];
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2) {
+        float v0 = v4[2 * q2], v1 = v4[2 * q2 + 1];
+        if (RMS) {
+          const float r = rinv[0] * (t == 0) + (T > 1 ? rinv[T > 1 ? 1 : 0] * (t == 1) : 0.f) +
+                          (T > 2 ? rinv[T > 2 ? 2 : 0] * (t == 2) : 0.f) +
+                          (T > 3 ? rinv[T > 3 ? 3 : 0] * (t == 3) : 0.f);
+          v0 *= r;
+          v1 *= r;
+        }
+        const uint16_t h0 = f32_to_bf16(v0), h1 = f32_to_bf16(v1);
+        hi[q2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        float s = bf16_to_f32(h0) + bf16_to_f32(h1);
+        if (HAS_LO) {
+          lo[q2] = pack_bf16x2(v0 - bf16_to_f32(h0), v1 - bf16_to_f32(h1));
+          s += bf16_lo(lo[q2]) + bf16_hi(lo[q2]);
+        }
+        X += s;
+        Xc += dq_offset(b & 1, j0 + q2) * s;
+      }
+      if (ok) {
+        reinterpret_cast<uint2*>(s_xhi)[i] = make_uint2(hi[0], hi[1]);
+        if (HAS_LO) reinterpret_cast<uint2*>(s_xlo)[i] = make_uint2(lo[0], lo[1]);
+      }
+      X = oct_sum(X);
+      Xc = oct_sum(Xc);
+      if (ok && (pc & 7) == 0) s_xs[t * nbD + b] = make_float2(X, Xc);
+    }
   }
   __syncthreads();
 
-  // 4. Dequantising MFMA GEMV over this wave's octets.
+  // 3. Dequantising MFMA GEMV over this wave's octets.
   const DqConsts kc = dq_consts();
   float acc[T], mt[T];
 #pragma unroll
@@ -495,7 +574,7 @@ __global__ __launch_bounds__(kGuThreads, 2) void decode_gateup_kernel(DecodeArgs
   }
   __syncthreads();
 
-  // 5. SwiGLU over 16 FFN rows x T tokens; h in bf16 hi + lo; half-block sums.
+  // 4. SwiGLU over 16 FFN rows x T tokens; h in bf16 hi + lo; half-block sums.
   if (tid < 16 * T) {
     const int t = tid >> 4, nn = tid & 15;
     const float ga = s_red[0][t][nn] + s_red[1][t][nn];
@@ -519,10 +598,13 @@ __global__ __launch_bounds__(kGuThreads, 2) void decode_gateup_kernel(DecodeArgs
 }
 
 // ----------------------------------------------------------------------------
-// decode_down.  Grid: D/16 blocks of 1024 threads; wave w handles the listed
-// experts u = w, w + 16, ...; outputs are summed over waves in a fixed order.
-// Each wave stages its expert's h rows (bf16 hi and lo) in a private LDS
-// region, so the weight loads of all its octets are in flight together.
+// decode_down.  Grid: D/16 blocks of 1024 threads; wave w handles list
+// entries u = w, w + 16, ...; outputs are summed over waves in a fixed order.
+// The h rows (bf16 hi and lo) and block sums of entry u sit at a place that
+// does not depend on the list, so each wave issues those of its first entry
+// together with the list loads; its weight loads follow as soon as the
+// entry's expert is known.  h and sums are staged in a wave-private LDS
+// region for the MFMA operands.
 template <int T, int FMT>
 __global__ __launch_bounds__(1024) void decode_down_kernel(DecodeArgs a, DecodeWs w) {
   extern __shared__ uint4 s_dyn[];
@@ -530,16 +612,59 @@ __global__ __launch_bounds__(1024) void decode_down_kernel(DecodeArgs a, DecodeW
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int rt = blockIdx.x, D = a.D;
   const int n = lane & 15, q = lane >> 4;
-  const int nwork = *w.nwork;
-  const int Fp = w.Fp;
-  const int hrow = Fp / 8;                 // uint4 per h row
-  uint4* s_hw = s_dyn + (size_t)wv * T * 2 * hrow;   // [T][hi row, lo row]
+  const int Fp = w.Fp, hrow = Fp / 8, nbF = Fp / 32;
+  const int nh = T * 2 * hrow;  // uint4 of h per entry: [T][hi row, lo row]
+  const int nsum = T * nbF;     // uint4 of sums per entry: both halves of one block each
+  uint4* s_hw = s_dyn + (size_t)wv * (nh + nsum / 2);
+  float2* s_hs = reinterpret_cast<float2*>(s_hw + nh);  // [T][Fp/32], halves combined
   const DqConsts kc = dq_consts();
+
+  // h of one entry is staged in chunks of 64 * HV uint4 per wave; the first
+  // chunk (all of it for up to two tokens at d_ff <= 512) is prefetched.
+  constexpr int HV = T <= 2 ? 2 * T : 4;
+  uint4 hv[HV], sv;
+  auto load_h = [&](int u, int c0) {
+    const uint4* gh = reinterpret_cast<const uint4*>(w.hh) + (size_t)u * T * hrow;
+    const uint4* gl = reinterpret_cast<const uint4*>(w.hl) + (size_t)u * T * hrow;
+#pragma unroll
+    for (int j = 0; j < HV; ++j) {
+      const int i0 = c0 + lane + 64 * j;
+      const int i = i0 < nh ? i0 : 0;
+      const int t = i / (2 * hrow), rem = i % (2 * hrow);
+      const uint4 v = rem < hrow ? gh[t * hrow + rem] : gl[t * hrow + rem - hrow];
+      hv[j] = i0 < nh ? v : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store_h = [&](int c0) {
+#pragma unroll
+    for (int j = 0; j < HV; ++j)
+      if (c0 + lane + 64 * j < nh) s_hw[c0 + lane + 64 * j] = hv[j];
+  };
+  auto load_s = [&](int u) {
+    const uint4* gs = reinterpret_cast<const uint4*>(w.hs) + (size_t)u * nsum;
+    const uint4 v = gs[lane < nsum ? lane : 0];
+    sv = lane < nsum ? v : make_uint4(0, 0, 0, 0);
+  };
+
+  const int nwork = *w.nwork;
+  int ref = 0;
+  float4 gt = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (wv < w.Wmax) {
+    ref = w.work_ref[wv];
+    gt = reinterpret_cast<const float4*>(w.work_gate)[wv];
+    load_h(wv, 0);
+    load_s(wv);
+  }
   float oacc[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) oacc[t] = 0.f;
   for (int u = wv; u < nwork; u += kDnWaves) {
-    const int ref = w.work_ref[u];
+    if (u != wv) {
+      ref = w.work_ref[u];
+      gt = reinterpret_cast<const float4*>(w.work_gate)[u];
+      load_h(u, 0);
+      load_s(u);
+    }
     const bool sh = ref < 0;
     const int Fu = sh ? a.Fs : a.F;
     const int oF = octets(Fu), nb = Fu / 32;
@@ -550,30 +675,16 @@ __global__ __launch_bounds__(1024) void decode_down_kernel(DecodeArgs a, DecodeW
 #pragma unroll
     for (int o = 0; o < kMaxDecodeFOct; ++o)
       if (o < oF) load_record<FMT>(base + (size_t)o * rec_bytes(FMT), lane, cw[o], hw[o], pa[o], pb[o]);
-    // h rows of this expert -> LDS (T rows of hi then lo, each Fp bf16), in
-    // chunks of four 16-byte loads per lane to bound register use.
-    const uint4* gh = reinterpret_cast<const uint4*>(w.hh) + (size_t)u * T * hrow;
-    const uint4* gl = reinterpret_cast<const uint4*>(w.hl) + (size_t)u * T * hrow;
-    const int nh = T * 2 * hrow;
-    for (int j0 = 0; j0 < nh; j0 += 4 * 64) {
-      uint4 hv[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i0 = j0 + lane + 64 * j;  // i over [T][2][hrow]
-        const int i = i0 < nh ? i0 : 0;     // clamped: all four loads issue unconditionally
-        const int t = i / (2 * hrow), rem = i % (2 * hrow);
-        const uint4* src = rem < hrow ? gh + t * hrow + rem : gl + t * hrow + rem - hrow;
-        hv[j] = *src;
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = j0 + lane + 64 * j;
-        if (i < nh) s_hw[i] = hv[j];
-      }
+    // h and sums to this wave's LDS region
+    store_h(0);
+    for (int c0 = 64 * HV; c0 < nh; c0 += 64 * HV) {
+      load_h(u, c0);
+      store_h(c0);
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (lane < nsum)
+      s_hs[lane] = make_float2(__uint_as_float(sv.x) + __uint_as_float(sv.z),
+                               __uint_as_float(sv.y) + __uint_as_float(sv.w));
+    wave_lds_sync();
     float acc[T], mt[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) acc[t] = mt[t] = 0.f;
@@ -585,21 +696,18 @@ __global__ __launch_bounds__(1024) void decode_down_kernel(DecodeArgs a, DecodeW
           if (n >= T) return make_uint4(0, 0, 0, 0);
           return s_hw[(n * 2 + (lo ? 1 : 0)) * hrow + (32 * (8 * o + beta) + 8 * q) / 8];
         };
-        auto xsum = [&](int beta, int t) -> float2 {
-          const size_t hi = (((size_t)u * T + t) * (Fp / 32) + 8 * o + beta) * 2;
-          const float2 h0 = w.hs[hi], h1 = w.hs[hi + 1];
-          return make_float2(h0.x + h1.x, h0.y + h1.y);
-        };
+        auto xsum = [&](int beta, int t) -> float2 { return s_hs[t * nbF + 8 * o + beta]; };
         record_gemv<T, FMT, true>(cw[o], hw[o], pa[o], pb[o], nvalid, kc, xfrag, xsum, acc, mt, q);
       }
     }
+    const float gg[4] = {gt.x, gt.y, gt.z, gt.w};
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       mt[t] += __shfl_xor(mt[t], 16, 64);
       mt[t] += __shfl_xor(mt[t], 32, 64);
-      oacc[t] += w.work_gate[u * 4 + t] * (acc[t] + mt[t]);
+      oacc[t] += gg[t] * (acc[t] + mt[t]);
     }
-    __builtin_amdgcn_wave_barrier();   // LDS region reused by the next expert
+    wave_lds_sync();  // LDS region reused by the next entry
   }
   if (lane < 16) {
 #pragma unroll
@@ -636,13 +744,13 @@ static hipError_t launch_decode_x(const DecodeArgs& a, const DecodeWs& w, hipStr
   static size_t lds_gu = 0, lds_dn = 0;
   const int D8 = a.D / 8, nbD = a.D / 32;
   const size_t lds = (size_t)T * D8 * 16 * (XM == kXF32 ? 2 : 1) + (size_t)T * nbD * 8 +
-                     (XM == kXRms ? (size_t)T * a.D * 4 : 0) + T * topk_scratch_bytes(a.E, a.k);
-  const size_t lds_down = (size_t)kDnWaves * T * 2 * w.Fp * 2;
+                     (T > 1 ? (size_t)a.E * 4 : 0);
+  const size_t lds_down =
+      (size_t)kDnWaves * ((size_t)T * 2 * (w.Fp / 8) + (size_t)T * (w.Fp / 32) / 2) * 16;
   hipError_t e;
   if ((e = allow_lds(decode_gateup_kernel<T, FMT, XM>, lds, lds_gu)) != hipSuccess) return e;
   if ((e = allow_lds(decode_down_kernel<T, FMT>, lds_down, lds_dn)) != hipSuccess) return e;
-  const int Wr = w.Wmax - 1;
-  const int nblk = Wr * (a.F / 16) + (a.shared ? a.Fs / 16 : 0);
+  const int nblk = (a.shared ? a.Fs / 16 : 0) + (w.Wmax - 1) * (a.F / 16);
   if ((e = launch_timed(decode_gateup_kernel<T, FMT, XM>, dim3(nblk), dim3(kGuThreads),
                         (uint32_t)lds, st, a, w)) != hipSuccess)
     return e;
@@ -652,7 +760,8 @@ static hipError_t launch_decode_x(const DecodeArgs& a, const DecodeWs& w, hipStr
 
 template <int T, int FMT>
 static hipError_t launch_decode_t(const DecodeArgs& a, const DecodeWs& w, hipStream_t st) {
-  if (a.rmsnorm) return launch_decode_x<T, FMT, kXRms>(a, w, st);
+  if (a.rmsnorm) return a.x_bf16 ? launch_decode_x<T, FMT, kXRms>(a, w, st)
+                                 : launch_decode_x<T, FMT, kXRmsF32>(a, w, st);
   if (a.x_bf16) return launch_decode_x<T, FMT, kXBf16>(a, w, st);
   return launch_decode_x<T, FMT, kXF32>(a, w, st);
 }

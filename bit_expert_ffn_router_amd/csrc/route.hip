@@ -21,14 +21,12 @@ __global__ void fill_i32_kernel(int32_t* p, int n, int32_t v) {
 __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int T, int E,
                                                    int k, int32_t* __restrict__ idx,
                                                    float* __restrict__ gate) {
-  extern __shared__ key64 s_scr[];  // 4 waves x topk_scratch entries
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   int my_e;
   float my_l;
-  wave_topk_any(logits + (size_t)t * E, E, k, lane, my_e, my_l,
-                s_scr + (threadIdx.x >> 6) * (topk_scratch_bytes(E, k) / 8));
+  wave_topk_any(logits + (size_t)t * E, E, k, lane, my_e, my_l);
   const float g = wave_gate(my_l, k, lane);
   if (lane < k) {
     idx[(size_t)t * k + lane] = my_e;
@@ -39,7 +37,7 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* idx, float* gate,
                         hipStream_t st) {
   if (T == 0) return hipSuccess;
-  route_kernel<<<(T + 3) / 4, 256, 4 * topk_scratch_bytes(E, k), st>>>(logits, T, E, k, idx, gate);
+  route_kernel<<<(T + 3) / 4, 256, 0, st>>>(logits, T, E, k, idx, gate);
   return hipGetLastError();
 }
 
