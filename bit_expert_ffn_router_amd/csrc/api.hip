@@ -176,8 +176,8 @@ moe_status moe_layer_forward(const moe_shape* shape, int32_t tokens, const void*
   if (T == 0) return ok();
   if (!x || !router_logits || !out || !ws) return fail(MOE_EINVAL, "x, router_logits, out, ws are required");
   if (!aligned256(ws)) return fail(MOE_EINVAL, "ws must be 256-byte aligned");
-  if (((uintptr_t)x & 15u) || ((uintptr_t)router_logits & 3u) || ((uintptr_t)out & 3u))
-    return fail(MOE_EINVAL, "x must be 16-byte aligned, logits and out 4-byte aligned");
+  if (((uintptr_t)x & 15u) || ((uintptr_t)router_logits & 3u) || ((uintptr_t)out & 15u))
+    return fail(MOE_EINVAL, "x and out must be 16-byte aligned, router_logits 4-byte aligned");
   const size_t need_ws = forward_ws_bytes(shape, T);
   if (ws_bytes < need_ws) return fail(MOE_ENOSPACE, "ws_bytes %zu < %zu", ws_bytes, need_ws);
   if (use_decode_path(T)) {

@@ -48,6 +48,14 @@ __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v 
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
 
+// Order this wave's LDS accesses around an exchange between its own lanes
+// (release / acquire fences at wavefront scope around a wave barrier).
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // fp32 -> bf16, round to nearest, ties to even (finite inputs).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   uint32_t b = __float_as_uint(f);

@@ -98,12 +98,6 @@ struct RouteLds {
   int32_t nu;
 };
 
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 // Top-k of token t by the calling wave: lane j < k gets the j-th expert and
 // its gate.  The id is clamped into 0..E-1 (it always is for finite logits;
 // the clamp keeps a wild id out of the weight addresses).
@@ -179,11 +173,11 @@ __device__ __forceinline__ void build_list(const DecodeArgs& a, const DecodeWs& 
     tok[h] = (p >= k ? 1 : 0) + (p >= 2 * k ? 1 : 0) + (p >= 3 * k ? 1 : 0);
     if (valid[h]) s_first[e[h]] = 0x7FFFFFFF;
   }
-  wave_lds_sync();
+  wave_lds_fence();
 #pragma unroll
   for (int h = 0; h < 2; ++h)
     if (hit[h]) atomicMin(&s_first[e[h]], lane + 64 * h);
-  wave_lds_sync();
+  wave_lds_fence();
   unsigned long long bf[2], bm[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -197,7 +191,7 @@ __device__ __forceinline__ void build_list(const DecodeArgs& a, const DecodeWs& 
   const int M = nm0 + __popcll(bm[1]);
   const int nu = base + U;
   for (int i = lane; i < nu * 4; i += 64) R.wg[i] = 0.f;
-  wave_lds_sync();
+  wave_lds_fence();
   auto list_index = [&](int fp) {  // list entry of the pair that first named an expert
     const unsigned long long m = fp >= 64 ? bf[1] : bf[0];
     return base + (fp >= 64 ? nf0 : 0) + __popcll(m & ((1ull << (fp & 63)) - 1ull));
@@ -213,7 +207,7 @@ __device__ __forceinline__ void build_list(const DecodeArgs& a, const DecodeWs& 
     if (base) R.ref[0] = -1;
   }
   if (base && lane < T) R.wg[lane] = 1.0f;
-  wave_lds_sync();
+  wave_lds_fence();
   if (!publish) return;
   for (int i = lane; i < nu; i += 64) w.work_ref[i] = R.ref[i];
   for (int i = lane; i < nu * 4; i += 64) w.work_gate[i] = R.wg[i];
@@ -684,7 +678,7 @@ __global__ __launch_bounds__(1024) void decode_down_kernel(DecodeArgs a, DecodeW
     if (lane < nsum)
       s_hs[lane] = make_float2(__uint_as_float(sv.x) + __uint_as_float(sv.z),
                                __uint_as_float(sv.y) + __uint_as_float(sv.w));
-    wave_lds_sync();
+    wave_lds_fence();
     float acc[T], mt[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) acc[t] = mt[t] = 0.f;
@@ -707,7 +701,7 @@ __global__ __launch_bounds__(1024) void decode_down_kernel(DecodeArgs a, DecodeW
       mt[t] += __shfl_xor(mt[t], 32, 64);
       oacc[t] += gg[t] * (acc[t] + mt[t]);
     }
-    wave_lds_sync();  // LDS region reused by the next entry
+    wave_lds_fence();  // LDS region reused by the next entry
   }
   if (lane < 16) {
 #pragma unroll

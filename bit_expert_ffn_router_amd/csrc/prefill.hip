@@ -17,13 +17,20 @@
 //                (fixed order, no atomics)
 //
 // The grouped GEMM is the one dense contraction of the layer.  It runs on
-// bf16 MFMA (16x16x32) with fp32 accumulation.  Weights stay packed in HBM;
-// each pipeline step dequantises one 32-column block of 256 weight rows into
-// LDS (one weight row per thread: a 4-entry bf16 table s*u + m built from the
-// block's fp16 scale and min, then v_perm byte selects expand the 2-bit codes),
-// while the waves run the MFMAs of the previous step.  Row tiles of
-// activations are gathered through the permutation into LDS in the MFMA
-// operand order.
+// bf16 MFMA (16x16x32) with fp32 accumulation.  A block of 8 waves computes
+// 128 rows of one row tile x 512 weight rows; wave w owns weight rows
+// 64w .. 64w+63 (four 16-row column tiles) over all 128 rows, so the
+// activation tile in LDS serves 512 weight rows.  Operands reach LDS by
+// direct global-to-LDS loads of 16 bytes per lane: the 128 gathered
+// activation rows (through the permutation) in a ring of four stages of two
+// 32-column k-steps, issued three stages ahead; and each wave's own column
+// tiles, a whole 256-column octet of packed code words and (scale, min)
+// pairs at a time, double-buffered and issued one octet ahead.  Each wave
+// dequantises its tiles in registers -- per (row, block) a 4-entry bf16
+// table s*u + m and v_perm byte selects, two weights per select -- straight
+// into MFMA B fragments, so every weight is dequantised once per block.
+#include <type_traits>
+
 #include "route_common.hpp"
 
 namespace moe {
@@ -31,9 +38,9 @@ namespace moe {
 namespace {
 
 constexpr int kBM = 128;             // rows (permuted pairs) per tile
-constexpr int kBN = 256;             // weight rows per block: 16 MFMA column tiles
-constexpr int kPfThreads = 256;      // 4 waves, 2 x 2 over (rows, weight rows)
-constexpr int kNT = kBN / 16;        // column tiles per block
+constexpr int kBN = 512;             // weight rows per block: 32 MFMA column tiles
+constexpr int kPfWaves = 8;          // wave w: column tiles 4w .. 4w+3, all rows
+constexpr int kPfThreads = 64 * kPfWaves;
 constexpr int kRG = kBM / 16;        // row groups per tile
 
 __host__ __device__ inline size_t al256(size_t v) { return (v + 255) / 256 * 256; }
@@ -162,27 +169,58 @@ __global__ __launch_bounds__(1024) void pf_tiles_kernel(const int32_t* __restric
 }
 
 // ----------------------------------------------------------------------------
-// Dequantisation of one 32-column block of one weight row into the MFMA B
-// layout.  Q2SM: w = s*u + m as bf16 via a 4-entry table and byte permutes.
-// codes[q] = the record's code word of lane 16q + n covering this block.
-__device__ __forceinline__ void dq_row_block_q2(const uint32_t (&codes)[4], int beta,
-                                                uint32_t sm, uint4 (&frag)[4]) {
+// Q2SM dequantisation into MFMA B fragments.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};  // round to nearest even
+  return __builtin_bit_cast(uint32_t, v);
+}
+// The four values s*u + m (u = 0..3) of one block as bf16, in two words:
+// bytes 0..3 (u = 0, 1) and 4..7 (u = 2, 3) of the byte-select source.
+__device__ __forceinline__ void q2_table(uint32_t sm, uint32_t& lo, uint32_t& hi) {
   const float s = f16_to_f32((uint16_t)(sm & 0xFFFFu));
   const float m = f16_to_f32((uint16_t)(sm >> 16));
-  const uint32_t lut_lo = pack_bf16x2(m, s + m);                 // u = 0, 1
-  const uint32_t lut_hi = pack_bf16x2(fmaf(2.f, s, m), fmaf(3.f, s, m));  // u = 2, 3
-  const int sh = 8 * (beta & 1);  // slots 4*(beta%2) .. +3 -> bits 2*slot
+  lo = cvt_pk_bf16(m, s + m);
+  hi = cvt_pk_bf16(fmaf(2.f, s, m), fmaf(3.f, s, m));
+}
+// Eight consecutive weights (k = 8q .. 8q+7 of one block) of one weight row:
+// code word W of lane (q, n), block half sh / 8; slot j of the half holds the
+// codes of columns 2j (bits sh+2j) and 2j+1 (bits 16+sh+2j).
+__device__ __forceinline__ uint4 q2_frag(uint32_t W, int sh, uint32_t lo, uint32_t hi) {
+  uint32_t v[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    uint32_t v[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t t = (codes[q] >> (sh + 2 * j)) & 0x00030003u;   // u0 | u1 << 16
-      const uint32_t sel = t * 0x202u + 0x01000100u;                 // bytes 2u0,2u0+1,2u1,2u1+1
-      v[j] = __builtin_amdgcn_perm(lut_hi, lut_lo, sel);
-    }
-    frag[q] = make_uint4(v[0], v[1], v[2], v[3]);
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t t = (W >> (sh + 2 * j)) & 0x00030003u;  // u0 | u1 << 16
+    const uint32_t sel = t * 0x202u + 0x01000100u;          // bytes 2u0, 2u0+1, 2u1, 2u1+1
+    v[j] = __builtin_amdgcn_perm(hi, lo, sel);
   }
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// ----------------------------------------------------------------------------
+// Pipeline plumbing.
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Direct global -> LDS load: lane l's 16 bytes land at lds + 16 l; `lds` is
+// the same for the whole wave.  Counts in vmcnt.
+__device__ __forceinline__ void dma16(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)lds, 16, 0, 0);
+}
+// Wait until at most N vector-memory operations of this wave are in flight
+// (gfx9 s_waitcnt: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt not waited).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// Workgroup barrier without the release/acquire fences of __syncthreads (which
+// would also drain the loads in flight for later stages); the ordering it needs
+// comes from wait_vm before it and from the compiler barriers around it.
+__device__ __forceinline__ void block_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 struct PfArgs {
@@ -196,15 +234,28 @@ struct PfArgs {
   int out_bf16;
 };
 
+// LDS of the grouped GEMM: 4 x 16 KB activation stages + 2 x 48 KB weight
+// octets = 160 KB, the whole LDS of a CU (one block per CU).
+struct PfA {
+  uint4 a[2][kRG * 4 * 16];  // [k-step][row group][quarter q][row m]: A fragments
+};
+struct PfB {
+  uint4 code[kPfWaves][4][64];  // [wave][tile][lane]: the lane's 4 code words of the octet
+  uint4 sm[kPfWaves][2][64];    // [wave][tile pair][...]: (scale, min) of rows x 8 blocks
+};
+// direct loads per wave: activations per stage, weights per octet
+constexpr int kPfDmaA = 2;
+constexpr int kPfDmaB = 6;
+
 // Grouped GEMM tile.  MODE 0: gate/up (A = gathered activations, K = D, B =
 // the expert's gate/up rows, SwiGLU epilogue into H).  MODE 1: down (A = H
 // rows, K = F, B = W_down rows, epilogue into Y).
 template <int MODE>
-__global__ __launch_bounds__(kPfThreads, 2) void pf_gemm_kernel(PfArgs a, int nN, int nwork) {
-  __shared__ uint4 s_a[2][kRG * 4 * 16];   // [stage][row group][q][m]     2 x 8 KB
-  __shared__ uint4 s_b[2][kNT * 4 * 16];   // [stage][col tile][q][n]      2 x 16 KB
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int wm = wv >> 1, wn = wv & 1;
+__global__ __launch_bounds__(kPfThreads, 1) void pf_gemm_kernel(PfArgs a, int nN, int nwork) {
+  __shared__ PfA sa0, sa1, sa2, sa3;
+  __shared__ PfB sb0, sb1;
+  // wave index as a uniform (scalar) value: the weight addresses stay in SGPRs
+  const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   // XCD-aware order: blocks are dispatched round-robin over the 8 XCDs, so
   // block i runs on XCD i % 8; give each XCD a contiguous range of work items
   // (the grid is a multiple of 8, which makes this a bijection).
@@ -220,138 +271,229 @@ __global__ __launch_bounds__(kPfThreads, 2) void pf_gemm_kernel(PfArgs a, int nN
   const int F = sh ? a.Fs : a.F;
   const uint8_t* base = sh ? a.shared : a.routed + (size_t)e * a.stride;
   const int K = MODE == 0 ? a.D : F;
-  const int nkb = K / 32;
+  const int nkb = K / 32, nst = (nkb + 1) / 2;
   const int oK = octets(K);
-  const int NW = MODE == 0 ? 2 * F : a.D;   // weight rows of this GEMM
+  const int NW = MODE == 0 ? 2 * F : a.D;  // weight rows of this GEMM
   if (nb * kBN >= NW) return;
 
-  // A rows of this thread: chunks c = tid, tid + 256 -> (row c/4, quarter c%4)
-  const uint16_t* arow[2];
-  bool avalid[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int c = tid + kPfThreads * h, r = c >> 2;
-    avalid[h] = r < rows;
+  // A: this lane's 16-byte piece (row 16 wv + lane % 16, quarter lane / 16) of
+  // the wave's row group; rows past the tile read row 0 (masked later).
+  const uint16_t* arow;
+  {
+    const int r = 16 * wv + (lane & 15);
     const int pos = row0 + (r < rows ? r : 0);
     if (MODE == 0) {
       const int tok = pos < P ? a.w.sorted[pos] / a.k : pos - P;
-      arow[h] = a.x + (size_t)tok * a.D;
+      arow = a.x + (size_t)tok * a.D + 8 * (lane >> 4);
     } else {
-      arow[h] = a.w.H + (size_t)pos * a.w.Fmax;
+      arow = a.w.H + (size_t)pos * a.w.Fmax + 8 * (lane >> 4);
     }
   }
-  // B row of this thread: column tile tau = tid / 16, row n = tid % 16.
-  const int tau = tid >> 4, n = tid & 15;
-  const int wrow = nb * kBN + tau * 16;   // first weight row of the tile
-  const bool bvalid = wrow < NW;
-  const uint8_t* brec = nullptr;          // record of (tile, octet 0)
-  if (bvalid) {
-    if (MODE == 0) {
-      const int hg = wrow / 32, mat = (wrow / 16) & 1;  // h-group, gate/up
-      brec = base + (size_t)(hg * 2 + mat) * oK * kRecQ2;
-    } else {
-      brec = base + down_offset(a.D, F, kQ2) + (size_t)(wrow / 16) * oK * kRecQ2;
-    }
+  // B: record row of each of the wave's column tiles (uniform).  Tiles past
+  // the matrix read the pair's first tile or tile 0 (masked in the epilogue).
+  const uint8_t* trec[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    int w0 = nb * kBN + (4 * wv + j) * 16;
+    if (w0 >= NW) w0 = (j & 1) ? nb * kBN + (4 * wv + j - 1) * 16 : 0;
+    if (w0 >= NW) w0 = 0;
+    trec[j] = base + (MODE == 0 ? 0 : down_offset(a.D, F, kQ2)) + (size_t)(w0 / 16) * oK * kRecQ2;
   }
-  auto load_a = [&](int kb, uint4 (&ra)[2]) {
+  // (scale, min) pieces: lanes 0..31 / 32..63 take tile 2i / 2i+1 of pair i,
+  // 16 bytes each: row lane % 16, blocks 4 h .. 4 h + 3 with h = (lane / 16) % 2
+  // (in LDS: [tile of pair][h][row], so a k-step's reads conflict at most 2-way)
+  const uint8_t* smp[2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int q = (tid + kPfThreads * h) & 3;
-      ra[h] = avalid[h] ? *reinterpret_cast<const uint4*>(arow[h] + 32 * kb + 8 * q)
-                        : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto load_b = [&](int kb, uint32_t (&rc)[4], uint32_t& rsm) {
-    if (bvalid) {
-      const uint8_t* rec = brec + (size_t)(kb >> 3) * kRecQ2;
-      const int beta = kb & 7;
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        rc[q] = *reinterpret_cast<const uint32_t*>(rec + 16 * (16 * q + n) + 4 * (beta >> 1));
-      rsm = *reinterpret_cast<const uint32_t*>(rec + 1024 + 4 * (8 * n + beta));
-    } else {
-      rc[0] = rc[1] = rc[2] = rc[3] = 0u;
-      rsm = 0u;
-    }
-  };
-  auto store_stage = [&](int st, int kb, const uint4 (&ra)[2], const uint32_t (&rc)[4],
-                         uint32_t rsm) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int c = tid + kPfThreads * h, r = c >> 2, q = c & 3;
-      s_a[st][((r >> 4) * 4 + q) * 16 + (r & 15)] = ra[h];
-    }
-    uint4 frag[4];
-    dq_row_block_q2(rc, kb & 7, rsm, frag);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) s_b[st][(tau * 4 + q) * 16 + n] = frag[q];
-  };
-
-  f32x4_t acc[4][8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  uint4 ra[2];
-  uint32_t rc[4], rsm;
-  load_a(0, ra);
-  load_b(0, rc, rsm);
-  store_stage(0, 0, ra, rc, rsm);
-  __syncthreads();
-  const int m = lane & 15, q = lane >> 4;
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int st = kb & 1;
-    const bool more = kb + 1 < nkb;
-    if (more) {
-      load_a(kb + 1, ra);
-      load_b(kb + 1, rc, rsm);
-    }
-    uint4 af[4], bf[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) af[i] = s_a[st][((4 * wm + i) * 4 + q) * 16 + m];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) bf[j] = s_b[st][((8 * wn + j) * 4 + q) * 16 + m];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc[i][j] = mfma16(af[i], bf[j], acc[i][j]);
-    if (more) store_stage(st ^ 1, kb + 1, ra, rc, rsm);
-    __syncthreads();
+  for (int i = 0; i < 2; ++i) {
+    const ptrdiff_t d = trec[2 * i + 1] - trec[2 * i];  // uniform; no indexed pointer array
+    smp[i] = trec[2 * i] + (lane >= 32 ? d : 0) + 1024 + 32 * (lane & 15) + 16 * ((lane >> 4) & 1);
   }
+  const int n = lane & 15, q = lane >> 4;
 
-  // Epilogue.  Lane holds D[4*(lane/16) + r][lane % 16] of each 16x16 tile.
-  const int rq = 4 * (lane >> 4), cn = lane & 15;
-  if (MODE == 0) {
-    // tiles 8wn + 2jj (gate) and 8wn + 2jj + 1 (up) belong to h-group
-    // (nb*kBN + (8wn + 2jj)*16) / 32 = nb*8 + 4wn + jj
+  // Loads of activation stage s and weight octet o (past the end: reload
+  // stage / octet 0, so every step issues the same loads).
+  auto issue_a = [&](PfA& A, int s0) __attribute__((always_inline)) {
+    const int s = s0 < nst ? s0 : 0;
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int hg = nb * (kBN / 32) + 4 * wn + jj;
-      if (hg * 16 >= F) continue;
+    for (int kk = 0; kk < 2; ++kk) {
+      const int kb = 2 * s + kk;
+      dma16(arow + (kb < nkb ? 32 * kb : 0), &A.a[kk][wv * 64]);
+    }
+  };
+  auto issue_b = [&](PfB& B, int o0) __attribute__((always_inline)) {
+    const size_t ro = (size_t)(o0 < oK ? o0 : 0) * kRecQ2;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 4; ++j)
+      dma16(reinterpret_cast<const uint4*>(trec[j] + ro) + lane, &B.code[wv][j][0]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = 64 * wm + 16 * i + rq + r;
-          if (row < rows) {
-            const float h = silu(acc[i][2 * jj][r]) * acc[i][2 * jj + 1][r];
-            a.w.H[(size_t)(row0 + row) * a.w.Fmax + 16 * hg + cn] = f32_to_bf16(h);
-          }
-        }
+    for (int i = 0; i < 2; ++i) dma16(smp[i] + ro, &B.sm[wv][i][0]);
+  };
+
+  f32x4_t acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // Software pipeline of the dequantisation: while the MFMAs of one k-step
+  // run, the B fragments of the next k-step are built (VALU work that the
+  // MFMAs hide).  cwo holds the octet's code words (one 16-byte LDS read per
+  // tile per octet); bfa / bfb the fragments of k-steps 2s and 2s+1.
+  uint4 cwo[4], bfa[4], bfb[4];
+  auto load_codes = [&](const PfB& B) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) cwo[j] = B.code[wv][j][lane];
+  };
+  // fragments of block b = 2 wd + kk (wd, kk compile-time) of the octet in B
+  auto dequant = [&](const PfB& B, auto WD, auto KK, uint4 (&bf)[4]) __attribute__((always_inline)) {
+    constexpr int wd = decltype(WD)::value, kk = decltype(KK)::value, b = 2 * wd + kk;
+    const uint32_t* smw = reinterpret_cast<const uint32_t*>(&B.sm[wv][0][0]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t w = wd == 0 ? cwo[j].x : (wd == 1 ? cwo[j].y : (wd == 2 ? cwo[j].z : cwo[j].w));
+      uint32_t lo, hi;
+      q2_table(smw[(j >> 1) * 256 + ((j & 1) * 32 + (b >> 2) * 16 + n) * 4 + (b & 3)], lo, hi);
+      bf[j] = q2_frag(w, 8 * kk, lo, hi);
+    }
+  };
+  auto mfmas = [&](const PfA& A, int kk, const uint4 (&bf)[4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint4 af = A.a[kk][(i * 4 + q) * 16 + n];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(af, bf[j], acc[i][j]);
+    }
+  };
+
+  // Step s = 8 t + I.  Stage s sits in activation buffer s % 4 and octet s / 4
+  // in weight buffer (s / 4) % 2.  Loads are issued in the order: prologue
+  // B(0), A(0), A(1), A(2); then in step s, after its barrier and its compute
+  // (so that the compute's LDS reads never sit behind newer loads), A(s + 3)
+  // and, when s % 4 == 0, B(s / 4 + 1).  So when step s waits, the loads
+  // issued after A(s) are A(s+1), A(s+2) and -- unless s % 4 == 0 -- one
+  // octet B.  Waiting down to 2 kPfDmaA also completes that octet, which the
+  // last stage of an octet needs (it prepares the first fragments of the
+  // next octet).  Every wave waits for its own loads, then the barrier makes
+  // all of them visible and frees buffer (s + 3) % 4.
+  auto abuf = [&](int i) __attribute__((always_inline)) -> PfA& {
+    return i == 0 ? sa0 : (i == 1 ? sa1 : (i == 2 ? sa2 : sa3));
+  };
+  auto step = [&](auto I, int s) __attribute__((always_inline)) {
+    constexpr int i = decltype(I)::value;
+    constexpr int wd = i % 4;
+    if constexpr (wd == 0 || wd == 3)
+      wait_vm<2 * kPfDmaA>();
+    else
+      wait_vm<2 * kPfDmaA + kPfDmaB>();
+    block_barrier();
+    PfB& bc = (i / 4) % 2 == 0 ? sb0 : sb1;  // this octet
+    PfB& bn = (i / 4) % 2 == 0 ? sb1 : sb0;  // the next one
+    if (s < nst) {
+      const PfA& A = abuf(i % 4);
+      // k-step 2s (fragments in bfa) || fragments of k-step 2s+1
+      dequant(bc, std::integral_constant<int, wd>(), std::integral_constant<int, 1>(), bfb);
+      mfmas(A, 0, bfa);
+      {  // odd number of k-steps: the last one is empty (a mask, not a branch)
+        const uint32_t keep = 2 * s + 1 < nkb ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          bfb[j] = make_uint4(bfb[j].x & keep, bfb[j].y & keep, bfb[j].z & keep, bfb[j].w & keep);
       }
+      // k-step 2s+1 (bfb) || fragments of k-step 2s+2 (next stage, maybe next octet)
+      uint4 bfn[4];
+      if constexpr (wd == 3) {
+        load_codes(bn);
+        dequant(bn, std::integral_constant<int, 0>(), std::integral_constant<int, 0>(), bfn);
+      } else {
+        dequant(bc, std::integral_constant<int, wd + 1>(), std::integral_constant<int, 0>(), bfn);
+      }
+      mfmas(A, 1, bfb);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bfa[j] = bfn[j];
+      // Instruction order for the scheduler: the LDS reads first, then each
+      // MFMA followed by three VALU instructions of the other k-step's
+      // dequantisation, which thereby run in the MFMAs' shadow.
+      __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);  // DS reads: A (k-step 2s), tables
+#pragma unroll
+      for (int t = 0; t < 32; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);  // DS reads: A (k-step 2s+1), tables
+#pragma unroll
+      for (int t = 0; t < 32; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+      }
+    }
+    issue_a(abuf((i + 3) % 4), s + 3);
+    if constexpr (wd == 0) issue_b(bn, s / 4 + 1);
+  };
+  issue_b(sb0, 0);
+  issue_a(sa0, 0);
+  issue_a(sa1, 1);
+  issue_a(sa2, 2);
+  wait_vm<3 * kPfDmaA>();  // B(0) has landed (this wave's own weight buffer)
+  load_codes(sb0);
+  dequant(sb0, std::integral_constant<int, 0>(), std::integral_constant<int, 0>(), bfa);
+#pragma unroll 1
+  for (int s = 0; s < nst; s += 8) {  // one exit: the register allocator keeps acc in place
+    step(std::integral_constant<int, 0>(), s);
+    step(std::integral_constant<int, 1>(), s + 1);
+    step(std::integral_constant<int, 2>(), s + 2);
+    step(std::integral_constant<int, 3>(), s + 3);
+    step(std::integral_constant<int, 4>(), s + 4);
+    step(std::integral_constant<int, 5>(), s + 5);
+    step(std::integral_constant<int, 6>(), s + 6);
+    step(std::integral_constant<int, 7>(), s + 7);
+  }
+  wait_vm<0>();  // the trailing (unused) loads land before the LDS is reused
+
+  // Epilogue through a wave-private 2 KB LDS patch (the stage buffers are
+  // free once every wave is past its last stage): per 16-row group the lane's
+  // D[4q + r][n] values go in as bf16, and come out as whole row segments,
+  // so each lane stores 16 contiguous bytes.
+  block_barrier();
+  uint16_t* ep = reinterpret_cast<uint16_t*>(&sa0.a[0][0]) + wv * 1024;
+  const int rl = lane >> 2;     // row of the group this lane stores
+  const int cb = 8 * (lane & 3);
+  if (MODE == 0) {
+    // tiles 4wv + 2jj (gate) and 4wv + 2jj + 1 (up) form h-group nb*16 + 2wv + jj
+    const int hg = nb * (kBN / 32) + 2 * wv + (cb >> 4);
+    const bool colok = hg * 16 < F;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          ep[(4 * q + r) * 32 + 16 * jj + n] =
+              f32_to_bf16(silu(acc[i][2 * jj][r]) * acc[i][2 * jj + 1][r]);
+      wave_lds_fence();
+      const uint4 v = *reinterpret_cast<const uint4*>(ep + rl * 32 + cb);
+      const int row = 16 * i + rl;
+      if (row < rows && colok)
+        *reinterpret_cast<uint4*>(a.w.H + (size_t)(row0 + row) * a.w.Fmax + nb * (kBN / 2) +
+                                  32 * wv + cb) = v;
+      wave_lds_fence();
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int col = nb * kBN + (8 * wn + j) * 16 + cn;
+    for (int jj = 0; jj < 2; ++jj) {
+      const int col = nb * kBN + 64 * wv + 32 * jj + cb;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 8; ++i) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = 64 * wm + 16 * i + rq + r;
-          if (row < rows) a.w.Y[(size_t)(row0 + row) * a.D + col] = f32_to_bf16(acc[i][j][r]);
-        }
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            ep[(4 * q + r) * 32 + 16 * t2 + n] = f32_to_bf16(acc[i][2 * jj + t2][r]);
+        wave_lds_fence();
+        const uint4 v = *reinterpret_cast<const uint4*>(ep + rl * 32 + cb);
+        const int row = 16 * i + rl;
+        if (row < rows && col < a.D)
+          *reinterpret_cast<uint4*>(a.w.Y + (size_t)(row0 + row) * a.D + col) = v;
+        wave_lds_fence();
       }
     }
   }

@@ -179,11 +179,13 @@ size_t moe_workspace_bytes(const moe_shape* shape, int32_t tokens);
 /* One MoE FFN layer.
  *   tokens:        T >= 0 (T == 0: nothing is launched, *miss_count is not
  *                  touched).
- *   x:             device [T][d_model], dtype x_dtype (MOE_BF16 or MOE_F32).
+ *   x:             device [T][d_model], dtype x_dtype (MOE_BF16 or MOE_F32),
+ *                  16-byte aligned.
  *   flags:         0 or MOE_FLAG_RMSNORM_INPUT.
- *   router_logits: device fp32 [T][n_experts]; must be finite.
+ *   router_logits: device fp32 [T][n_experts], 4-byte aligned; must be finite.
  *   table:         where the experts are (see moe_expert_table).
- *   out:           device [T][d_model], dtype out_dtype.  Written in full.
+ *   out:           device [T][d_model], dtype out_dtype, 16-byte aligned.
+ *                  Written in full.
  *                  Without a slot table: the layer output.  With one: the
  *                  partial output -- the shared expert plus every pair whose
  *                  expert is resident, weighted by the full top-k gates.
@@ -195,6 +197,7 @@ size_t moe_workspace_bytes(const moe_shape* shape, int32_t tokens);
  *                  of gate * FFN_expert(x_token) is the whole layer.
  *   ws, ws_bytes:  device workspace, ws_bytes >= moe_workspace_bytes(shape,
  *                  T), 256-byte aligned.
+ * Misaligned pointers are rejected with MOE_EINVAL before any launch.
  * Paths: T <= 4 runs the decode path (dequantising MFMA GEMV that streams
  * each distinct selected expert once); larger T runs the prefill path
  * (routing, stable token permutation, grouped MFMA GEMM, combine).  The
