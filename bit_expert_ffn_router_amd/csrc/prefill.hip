@@ -206,6 +206,14 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 __device__ __forceinline__ void dma16(const void* src, void* lds) {
   __builtin_amdgcn_global_load_lds(src, (lds_void_t*)lds, 16, 0, 0);
 }
+// One 16-byte LDS read as a single native-vector load (a uint4 copy is done
+// member by member, and the merged read can lose the LDS variable's alias
+// scope; without it the compiler drains every direct load in flight first).
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 lds128(const uint4* p) {
+  const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 // Wait until at most N vector-memory operations of this wave are in flight
 // (gfx9 s_waitcnt: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt not waited).
 template <int N>
@@ -257,13 +265,17 @@ __global__ __launch_bounds__(kPfThreads, 1) void pf_gemm_kernel(PfArgs a, int nN
   // wave index as a uniform (scalar) value: the weight addresses stay in SGPRs
   const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   // XCD-aware order: blocks are dispatched round-robin over the 8 XCDs, so
-  // block i runs on XCD i % 8; give each XCD a contiguous range of work items
-  // (the grid is a multiple of 8, which makes this a bijection).
-  const int per_xcd = gridDim.x / 8;
-  const int bid = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-  if (bid >= nwork) return;
+  // block i runs on XCD i % 8.  Each XCD gets a contiguous eighth of the
+  // work items that exist (ntiles * nN, known only here; the grid is sized
+  // for the most tiles the routing can make, nwork, and is a multiple of 8),
+  // so the column blocks of one tile and the tiles of one expert share an L2
+  // and every XCD has work.  Blocks past an XCD's share exit.
+  const int nreal = *a.w.ntiles * nN;
+  const int per_xcd = (nreal + 7) / 8;
+  const int jx = blockIdx.x / 8;
+  const int bid = (blockIdx.x % 8) * per_xcd + jx;
+  if (jx >= per_xcd || bid >= nreal || bid >= nwork) return;
   const int ti = bid / nN, nb = bid % nN;
-  if (ti >= *a.w.ntiles) return;
   const int4 tile = a.w.tiles[ti];
   const int e = tile.x, row0 = tile.y, rows = tile.z;
   const int P = a.T * a.k;
@@ -342,7 +354,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void pf_gemm_kernel(PfArgs a, int nN
   uint4 cwo[4], bfa[4], bfb[4];
   auto load_codes = [&](const PfB& B) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) cwo[j] = B.code[wv][j][lane];
+    for (int j = 0; j < 4; ++j) cwo[j] = lds128(&B.code[wv][j][lane]);
   };
   // fragments of block b = 2 wd + kk (wd, kk compile-time) of the octet in B
   auto dequant = [&](const PfB& B, auto WD, auto KK, uint4 (&bf)[4]) __attribute__((always_inline)) {
@@ -359,7 +371,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void pf_gemm_kernel(PfArgs a, int nN
   auto mfmas = [&](const PfA& A, int kk, const uint4 (&bf)[4]) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const uint4 af = A.a[kk][(i * 4 + q) * 16 + n];
+      const uint4 af = lds128(&A.a[kk][(i * 4 + q) * 16 + n]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(af, bf[j], acc[i][j]);
     }
