@@ -101,10 +101,10 @@ struct RouteLds {
 // Top-k of token t by the calling wave: lane j < k gets the j-th expert and
 // its gate.  The id is clamped into 0..E-1 (it always is for finite logits;
 // the clamp keeps a wild id out of the weight addresses).
-__device__ __forceinline__ void route_token(const DecodeArgs& a, int t, int lane, int& e,
-                                            float& g) {
+__device__ __forceinline__ void route_token(const DecodeArgs& a, int t, int lane, TopkScratch& S,
+                                            int& e, float& g) {
   float l;
-  wave_topk_any(a.logits + (size_t)t * a.E, a.E, a.k, lane, e, l);
+  wave_topk_any(a.logits + (size_t)t * a.E, a.E, a.k, lane, S, e, l);
   g = wave_gate(l, a.k, lane);
   e = e < 0 ? 0 : (e >= a.E ? a.E - 1 : e);
 }
@@ -355,6 +355,7 @@ template <int T, int FMT, int XM>
 __global__ __launch_bounds__(kGuThreads, 2) void decode_gateup_kernel(DecodeArgs a, DecodeWs w) {
   extern __shared__ uint4 s_dyn[];
   __shared__ RouteLds R;
+  __shared__ TopkScratch s_topk[kGuWaves];
   __shared__ float s_red[kGuWaves][kDecodeMaxT][16];
   __shared__ float s_ss[kGuWaves][kDecodeMaxT];
   constexpr bool HAS_LO = XM == kXF32;
@@ -383,7 +384,7 @@ __global__ __launch_bounds__(kGuThreads, 2) void decode_gateup_kernel(DecodeArgs
     if (T == 1) {
       int e;
       float gt;
-      route_token(a, 0, lane, e, gt);
+      route_token(a, 0, lane, s_topk[wv], e, gt);
       const int rl = lane < a.k ? resident_ref(a, e) : -1;
       const unsigned long long hits = __ballot(lane < a.k && rl >= 0);
       if (rb == 0 && wv == 0) publish_t1(a, w, lane, e, gt, rl, hits, has_sh);
@@ -396,7 +397,7 @@ __global__ __launch_bounds__(kGuThreads, 2) void decode_gateup_kernel(DecodeArgs
       if (wv < T) {
         int e;
         float gt;
-        route_token(a, wv, lane, e, gt);
+        route_token(a, wv, lane, s_topk[wv], e, gt);
         if (lane < a.k) {
           R.e[wv * a.k + lane] = e;
           R.g[wv * a.k + lane] = gt;

@@ -21,12 +21,13 @@ __global__ void fill_i32_kernel(int32_t* p, int n, int32_t v) {
 __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int T, int E,
                                                    int k, int32_t* __restrict__ idx,
                                                    float* __restrict__ gate) {
+  __shared__ TopkScratch s_topk[4];
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   int my_e;
   float my_l;
-  wave_topk_any(logits + (size_t)t * E, E, k, lane, my_e, my_l);
+  wave_topk_any(logits + (size_t)t * E, E, k, lane, s_topk[threadIdx.x >> 6], my_e, my_l);
   const float g = wave_gate(my_l, k, lane);
   if (lane < k) {
     idx[(size_t)t * k + lane] = my_e;

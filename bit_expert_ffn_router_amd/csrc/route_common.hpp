@@ -71,23 +71,27 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
   return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), 63));
 }
 
-// Top-k of row[0..E) by one wave (E <= 64 * VPL), exact, in registers.
-// Expert e lives in lane e % 64, slot e / 64, as its order key (0 = empty;
-// no finite logit maps to 0).  Each lane keeps its head: its largest key,
-// the lowest slot on equal keys.  Round r takes the wave maximum of the
-// heads; equal maxima in several lanes go to the lowest expert id (lowest
-// slot, then lowest lane).  The winning lane drops that key and recomputes
-// its head.  After k rounds lane j < k holds the j-th expert and its
-// (canonical) logit: larger logits first, equal logits by ascending id.
+// Order keys of row[0..E) for one wave: expert e lives in lane e % 64, slot
+// e / 64 (0 = empty; no finite logit maps to 0).
 template <int VPL>
-__device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, int k, int lane,
-                                          int& my_e, float& my_l) {
-  uint32_t key[VPL];
+__device__ __forceinline__ void load_keys(const float* __restrict__ row, int E, int lane,
+                                          uint32_t (&key)[VPL]) {
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     const int e = i * 64 + lane;
     key[i] = e < E ? ord_key(row[e]) : 0u;
   }
+}
+
+// Exact top-k by a tournament (any k <= 64): each lane keeps its head, its
+// largest key (lowest slot on equal keys).  Round r takes the wave maximum of
+// the heads; equal maxima in several lanes go to the lowest expert id (lowest
+// slot, then lowest lane).  The winning lane drops that key and recomputes its
+// head.  After k rounds lane j < k holds the j-th expert and its (canonical)
+// logit: larger logits first, equal logits by ascending id.  Consumes `key`.
+template <int VPL>
+__device__ __forceinline__ void topk_tournament(uint32_t (&key)[VPL], int k, int lane, int& my_e,
+                                                float& my_l) {
   uint32_t hv;
   int hs;
   auto head = [&]() {
@@ -126,15 +130,112 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, 
   }
 }
 
-// Dispatch on the number of experts.
+// LDS scratch of one wave for topk_threshold.
+struct __attribute__((aligned(16))) TopkScratch {
+  uint32_t g[16];  // maxima of the 16 lane quads
+  uint2 cand[64];  // candidates as {~id, key}
+  uint2 top[16];   // {id, key} of ranks 0..15
+};
+
+// Exact top-k (k <= 16) in a fixed number of steps instead of k dependent
+// rounds.  tau = the k-th largest of the 16 lane-quad maxima: those k maxima
+// are k distinct keys >= tau, so the top k all have key >= tau, and only the
+// keys >= tau (usually a few more than k) stay candidates.  Candidates are
+// packed into LDS; each one's rank is the number of candidates before it in
+// the order (key descending, id ascending), i.e. of larger 64-bit values
+// key << 32 | ~id.  Lane j < k then gets the candidate of rank j, which is the
+// tournament's result.  Returns false (nothing decided) when more than 64
+// keys pass tau.  Does not change `key`.
+template <int VPL>
+__device__ __forceinline__ bool topk_threshold(const uint32_t (&key)[VPL], int k, int lane,
+                                               TopkScratch& S, int& my_e, float& my_l) {
+  uint32_t t[VPL];
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) t[i] = key[i];
+#pragma unroll
+  for (int w = VPL / 2; w >= 1; w /= 2)
+#pragma unroll
+    for (int i = 0; i < w; ++i) t[i] = max(t[i], t[i + w]);
+  uint32_t h = t[0];
+  h = max(h, dpp_u32<kDppQuadSwap1, 0xF>(0u, h));
+  h = max(h, dpp_u32<kDppQuadSwap2, 0xF>(0u, h));
+  if ((lane & 3) == 0) S.g[lane >> 2] = h;
+  wave_lds_fence();
+  uint32_t tc;
+  {
+    const uint4* g4 = reinterpret_cast<const uint4*>(S.g);
+    const uint32_t mine = S.g[lane & 15];
+    int c = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint4 v = g4[j];
+      c += (v.x >= mine) + (v.y >= mine) + (v.z >= mine) + (v.w >= mine);
+    }
+    tc = (lane < 16 && c >= k) ? mine : 0u;
+  }
+  uint32_t tau = wave_max_u32(tc);
+  tau = tau > 0u ? tau : 1u;  // empty slots are never candidates
+  int C = 0;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const bool f = key[i] >= tau;
+    const unsigned long long m = __ballot(f);
+    const int pos = C + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    if (f && pos < 64) S.cand[pos] = make_uint2(~(uint32_t)(i * 64 + lane), key[i]);
+    C += __popcll(m);
+  }
+  if (C > 64) return false;  // uniform
+  wave_lds_fence();
+  const uint2 mc = S.cand[lane];
+  const uint64_t mv = ((uint64_t)mc.y << 32) | mc.x;
+  int r = 0;
+  const uint4* c4 = reinterpret_cast<const uint4*>(S.cand);
+  for (int j0 = 0; j0 < C; j0 += 8) {  // 8 candidates per pass (4 reads in flight)
+    uint4 v[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) v[jj] = c4[j0 / 2 + jj];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const uint64_t a = ((uint64_t)v[jj].y << 32) | v[jj].x;
+      const uint64_t b = ((uint64_t)v[jj].w << 32) | v[jj].z;
+      r += (j0 + 2 * jj < C && a > mv) ? 1 : 0;
+      r += (j0 + 2 * jj + 1 < C && b > mv) ? 1 : 0;
+    }
+  }
+  if (lane < C && r < k) S.top[r] = make_uint2(~mc.x, mc.y);
+  wave_lds_fence();
+  if (lane < k) {
+    const uint2 tp = S.top[lane];
+    my_e = (int)tp.x;
+    my_l = ord_key_inv(tp.y);
+  } else {
+    my_e = 0;
+    my_l = 0.f;
+  }
+  return true;
+}
+
+template <int VPL>
+__device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, int k, int lane,
+                                          TopkScratch& S, int& my_e, float& my_l) {
+  uint32_t key[VPL];
+  load_keys<VPL>(row, E, lane, key);
+  if (k <= 16 && topk_threshold<VPL>(key, k, lane, S, my_e, my_l)) return;
+  topk_tournament<VPL>(key, k, lane, my_e, my_l);
+}
+
+// Top-k of row[0..E) by one wave (E <= kMaxExperts, k <= kMaxTopK): lane j < k
+// gets the j-th expert and its logit, larger logits first, equal logits by
+// ascending id.  S: this wave's LDS scratch.
 __device__ __forceinline__ void wave_topk_any(const float* __restrict__ row, int E, int k, int lane,
-                                              int& my_e, float& my_l) {
+                                              TopkScratch& S, int& my_e, float& my_l) {
   if (E <= 512)
-    wave_topk<8>(row, E, k, lane, my_e, my_l);
+    wave_topk<8>(row, E, k, lane, S, my_e, my_l);
   else if (E <= 1024)
-    wave_topk<16>(row, E, k, lane, my_e, my_l);
+    wave_topk<16>(row, E, k, lane, S, my_e, my_l);
   else
-    wave_topk<32>(row, E, k, lane, my_e, my_l);
+    wave_topk<32>(row, E, k, lane, S, my_e, my_l);
 }
 
 // Gate of lane j < k: exp(l_j - l_0) / sum_i exp(l_i - l_0) (0 for other lanes).

@@ -82,6 +82,9 @@ def _route_gpu(g, logits, k):
     (5, 2048, 32, dict()),
     (3, 64, 1, dict()),
     (3, 7, 7, dict()),
+    (64, 1024, 16, dict(zipf_s=1.1, alpha=1.0)),
+    (64, 512, 17, dict(zipf_s=1.1, alpha=1.0)),
+    (64, 300, 16, dict()),
 ])
 def test_route_matches_oracle(g, T, E, k, kw):
     logits = synth.router_logits(0, 11, T, E, **kw)
@@ -101,6 +104,31 @@ def test_route_ties_and_signed_zero(g):
     assert idx.tolist() == ridx.tolist()
     assert idx[0].tolist() == [2, 4, 0, 1] and idx[1].tolist() == [0, 1, 2, 3]
     assert idx[2].tolist() == [0, 1, 2, 3]
+    assert np.max(np.abs(gate - rgate)) <= GATE_ATOL
+
+
+def test_route_many_ties_at_the_cut(g):
+    """Ties that cross the k-th place, and more than 64 keys level with the
+    k-th: order by id among equal logits, whichever way the kernel selects."""
+    rng = np.random.default_rng(5)
+    E, k = 512, 10
+    rows = []
+    rows.append(np.full(E, 1.0, np.float32))                 # all 512 equal
+    r = rng.standard_normal(E).astype(np.float32) - 10.0      # 20 tied leaders spread over lanes/slots
+    r[rng.choice(E, 20, replace=False)] = 3.0
+    rows.append(r)
+    r = rng.standard_normal(E).astype(np.float32) - 10.0      # 5 clear leaders, 100 tied behind them
+    r[rng.choice(E, 100, replace=False)] = 2.0
+    r[rng.choice(np.nonzero(r < 0)[0], 5, replace=False)] = 4.0
+    rows.append(r)
+    r = np.full(E, -1.0, np.float32)                          # one quad holds every leader
+    r[[0, 1, 2, 3, 64, 65, 66, 67, 128, 129, 130, 131]] = np.arange(12, dtype=np.float32)
+    rows.append(r)
+    lg = np.stack(rows)
+    idx, gate = _route_gpu(g, lg, k)
+    ridx, rgate = O.route(lg, k)
+    assert idx.tolist() == ridx.tolist()
+    assert idx[0].tolist() == list(range(10))
     assert np.max(np.abs(gate - rgate)) <= GATE_ATOL
 
 
