@@ -260,31 +260,70 @@ __device__ __forceinline__ float blk_min(const uint4& pa, const uint4& pb, int b
 // activation fragments fetched by `xfrag(beta, hi_or_lo)`; accumulates
 // scale * block result into acc (lanes 0..15 hold tokens 0..T-1), and the
 // lane's share of the constant terms (blocks beta = q and q + 4) into mt.
-template <int T, int FMT, bool HAS_LO, typename XFrag, typename XSum>
+// The activation fragments of HB blocks at a time are read first (every read
+// is in range: the staging regions hold whole octets) and their MFMAs follow,
+// so the LDS latencies overlap; HB trades that against registers.  Blocks at
+// or past nvalid (a partial last octet) are computed on whatever the region
+// holds and dropped by selects, not branches.  FULL: nvalid == 8.
+template <int T, int FMT, bool HAS_LO, bool FULL = false, int HB = 8, typename XFrag,
+          typename XSum>
 __device__ __forceinline__ void record_gemv(const uint4& cw, const uint2& hw, const uint4& pa,
                                             const uint4& pb, int nvalid, const DqConsts& kc,
                                             XFrag xfrag, XSum xsum, float (&acc)[T],
                                             float (&mt)[T], int q) {
   const uint32_t words[4] = {cw.x, cw.y, cw.z, cw.w};
   const uint32_t hws[2] = {hw.x, hw.y};
+  static_assert(HB == 1 || HB == 2 || HB == 4 || HB == 8, "blocks per read batch");
+  if constexpr (HB == 1) {  // least registers: each block read where it is used
 #pragma unroll
-  for (int wd = 0; wd < 4; ++wd) {
-    uint4 ea, eb;
-    if (FMT == kQ2)
-      dq_q2(words[wd], kc, ea, eb);
-    else
-      dq_q3(words[wd], hws[wd >> 1], (wd & 1) != 0, kc, ea, eb);
+    for (int wd = 0; wd < 4; ++wd) {
+      uint4 ea, eb;
+      if (FMT == kQ2)
+        dq_q2(words[wd], kc, ea, eb);
+      else
+        dq_q3(words[wd], hws[wd >> 1], (wd & 1) != 0, kc, ea, eb);
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int beta = 2 * wd + half;
-      if (beta < nvalid) {
-        const uint4 bop = half ? eb : ea;
-        f32x4_t d = {0.f, 0.f, 0.f, 0.f};
-        d = mfma16(xfrag(beta, false), bop, d);
-        if (HAS_LO) d = mfma16(xfrag(beta, true), bop, d);
-        const float s = blk_scale<FMT>(pa, pb, beta);
+      for (int half = 0; half < 2; ++half) {
+        const int beta = 2 * wd + half;
+        if (FULL || beta < nvalid) {
+          const uint4 bop = half ? eb : ea;
+          f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+          d = mfma16(xfrag(beta, false), bop, d);
+          if (HAS_LO) d = mfma16(xfrag(beta, true), bop, d);
+          const float s = blk_scale<FMT>(pa, pb, beta);
 #pragma unroll
-        for (int r = 0; r < T; ++r) acc[r] += s * d[r];
+          for (int r = 0; r < T; ++r) acc[r] += s * d[r];
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int b0 = 0; b0 < 8; b0 += HB) {
+      uint4 xh[HB], xl[HB];
+#pragma unroll
+      for (int j = 0; j < HB; ++j) {
+        xh[j] = xfrag(b0 + j, false);
+        xl[j] = HAS_LO ? xfrag(b0 + j, true) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int wd = b0 / 2; wd < (b0 + HB) / 2; ++wd) {
+        uint4 ea, eb;
+        if (FMT == kQ2)
+          dq_q2(words[wd], kc, ea, eb);
+        else
+          dq_q3(words[wd], hws[wd >> 1], (wd & 1) != 0, kc, ea, eb);
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int beta = 2 * wd + half;
+          const uint4 bop = half ? eb : ea;
+          f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+          d = mfma16(xh[beta - b0], bop, d);
+          if (HAS_LO) d = mfma16(xl[beta - b0], bop, d);
+          const float s = blk_scale<FMT>(pa, pb, beta);
+          const bool on = FULL || beta < nvalid;
+#pragma unroll
+          for (int r = 0; r < T; ++r) acc[r] += on ? s * d[r] : 0.f;
+        }
       }
     }
   }
@@ -292,25 +331,22 @@ __device__ __forceinline__ void record_gemv(const uint4& cw, const uint2& hw, co
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb) {
     const int beta = q + 4 * hb;
-    if (beta < nvalid) {
-      float s, m;
-      if (FMT == kQ2) {
-        const uint32_t v = sel4(hb ? pb : pa, q);
-        s = f16_to_f32((uint16_t)(v & 0xFFFFu));
-        m = f16_to_f32((uint16_t)(v >> 16));
-      } else {
-        const uint32_t v = sel4(pa, beta >> 1);
-        s = f16_to_f32((uint16_t)((beta & 1) ? (v >> 16) : (v & 0xFFFFu)));
-        m = 0.f;
-      }
+    const bool on = FULL || beta < nvalid;
+    float s, m;
+    if (FMT == kQ2) {
+      const uint32_t v = sel4(hb ? pb : pa, q);
+      s = f16_to_f32((uint16_t)(v & 0xFFFFu));
+      m = f16_to_f32((uint16_t)(v >> 16));
+    } else {
+      const uint32_t v = sel4(pa, beta >> 1);
+      s = f16_to_f32((uint16_t)((beta & 1) ? (v >> 16) : (v & 0xFFFFu)));
+      m = 0.f;
+    }
 #pragma unroll
-      for (int t = 0; t < T; ++t) {
-        const float2 X = xsum(beta, t);
-        if (FMT == kQ2)
-          mt[t] += m * X.x - s * X.y;
-        else
-          mt[t] -= s * (X.y + 4.0f * X.x);
-      }
+    for (int t = 0; t < T; ++t) {
+      const float2 X = xsum(beta, t);
+      const float c = FMT == kQ2 ? m * X.x - s * X.y : -s * (X.y + 4.0f * X.x);
+      mt[t] += on ? c : 0.f;
     }
   }
 }
@@ -351,13 +387,23 @@ __device__ __forceinline__ float oct_sum(float v) {
 // holds matrix w/2 (gate, up) over the K octets o = w%2, w%2 + 2, ... of one
 // 16-row h-group -- and, while they are in flight, the activation loads, the
 // input rule, the bf16 operand(s) in LDS and the per-32-block activation sums.
+// Static LDS of a gate/up block.
+struct GuLds {
+  RouteLds R;
+  TopkScratch topk[kGuWaves];
+  float red[kGuWaves][kDecodeMaxT][16];
+  float ss[kGuWaves][kDecodeMaxT];
+};
+
+// Gate/up work item vb (the block index of decode_gateup_kernel).  Returns
+// early, with the same decision in every wave, when its list entry is unused.
 template <int T, int FMT, int XM>
-__global__ __launch_bounds__(kGuThreads, 2) void decode_gateup_kernel(DecodeArgs a, DecodeWs w) {
-  extern __shared__ uint4 s_dyn[];
-  __shared__ RouteLds R;
-  __shared__ TopkScratch s_topk[kGuWaves];
-  __shared__ float s_red[kGuWaves][kDecodeMaxT][16];
-  __shared__ float s_ss[kGuWaves][kDecodeMaxT];
+__device__ __forceinline__ void gateup_body(const DecodeArgs& a, const DecodeWs& w, int vb,
+                                            GuLds& L, uint4* s_dyn) {
+  RouteLds& R = L.R;
+  auto& s_topk = L.topk;
+  auto& s_red = L.red;
+  auto& s_ss = L.ss;
   constexpr bool HAS_LO = XM == kXF32;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int D = a.D, oD = octets(D), nbD = D / 32, D8 = D / 8;
@@ -372,12 +418,12 @@ __global__ __launch_bounds__(kGuThreads, 2) void decode_gateup_kernel(DecodeArgs
   const int gpr = a.F / 16;
   int u, g;
   const uint8_t* eb;
-  if ((int)blockIdx.x < nsh) {
+  if (vb < nsh) {
     u = 0;
-    g = blockIdx.x;
+    g = vb;
     eb = a.shared;
   } else {
-    const int rb = (int)blockIdx.x - nsh;
+    const int rb = vb - nsh;
     const int ui = rb / gpr;
     g = rb % gpr;
     int ref;
@@ -549,13 +595,13 @@ __global__ __launch_bounds__(kGuThreads, 2) void decode_gateup_kernel(DecodeArgs
   for (int i = 0; i < kMaxOctPerWave; ++i) {
     const int o = kh + 2 * i;
     if (o < oD) {
-      auto xfrag = [&](int beta, bool lo) -> uint4 {
-        if (n >= T) return make_uint4(0, 0, 0, 0);
-        const int idx = n * D8 + 4 * (8 * o + beta) + q;
-        return lo ? s_xlo[idx] : s_xhi[idx];
+      auto xfrag = [&](int beta, bool lo) -> uint4 {  // rows n >= T are zero (a select)
+        const int idx = (n < T ? n : 0) * D8 + 4 * (8 * o + beta) + q;
+        const uint4 v = lo ? s_xlo[idx] : s_xhi[idx];
+        return n < T ? v : make_uint4(0, 0, 0, 0);
       };
       auto xsum = [&](int beta, int t) -> float2 { return s_xs[t * nbD + 8 * o + beta]; };
-      record_gemv<T, FMT, HAS_LO>(cw[i], hw[i], pa[i], pb[i], 8, kc, xfrag, xsum, acc, mt, q);
+      record_gemv<T, FMT, HAS_LO, true>(cw[i], hw[i], pa[i], pb[i], 8, kc, xfrag, xsum, acc, mt, q);
     }
   }
 #pragma unroll
@@ -590,6 +636,13 @@ __global__ __launch_bounds__(kGuThreads, 2) void decode_gateup_kernel(DecodeArgs
     }
     if (nn == 0) w.hs[(((size_t)u * T + t) * (w.Fp / 32) + (g >> 1)) * 2 + (g & 1)] = make_float2(X, Xc);
   }
+}
+
+template <int T, int FMT, int XM>
+__global__ __launch_bounds__(kGuThreads, 2) void decode_gateup_kernel(DecodeArgs a, DecodeWs w) {
+  extern __shared__ uint4 s_dyn[];
+  __shared__ GuLds L;
+  gateup_body<T, FMT, XM>(a, w, (int)blockIdx.x, L, s_dyn);
 }
 
 // ----------------------------------------------------------------------------
@@ -687,12 +740,13 @@ __global__ __launch_bounds__(1024) void decode_down_kernel(DecodeArgs a, DecodeW
     for (int o = 0; o < kMaxDecodeFOct; ++o) {
       if (o < oF) {
         const int nvalid = nb - 8 * o < 8 ? nb - 8 * o : 8;
-        auto xfrag = [&](int beta, bool lo) -> uint4 {
-          if (n >= T) return make_uint4(0, 0, 0, 0);
-          return s_hw[(n * 2 + (lo ? 1 : 0)) * hrow + (32 * (8 * o + beta) + 8 * q) / 8];
+        auto xfrag = [&](int beta, bool lo) -> uint4 {  // rows n >= T are zero (a select)
+          const uint4 v = s_hw[((n < T ? n : 0) * 2 + (lo ? 1 : 0)) * hrow + (32 * (8 * o + beta) + 8 * q) / 8];
+          return n < T ? v : make_uint4(0, 0, 0, 0);
         };
         auto xsum = [&](int beta, int t) -> float2 { return s_hs[t * nbF + 8 * o + beta]; };
-        record_gemv<T, FMT, true>(cw[o], hw[o], pa[o], pb[o], nvalid, kc, xfrag, xsum, acc, mt, q);
+        record_gemv<T, FMT, true, false, 1>(cw[o], hw[o], pa[o], pb[o], nvalid, kc, xfrag, xsum, acc,
+                                            mt, q);
       }
     }
     const float gg[4] = {gt.x, gt.y, gt.z, gt.w};
