@@ -19,6 +19,8 @@ scale and min, or signed 3-bit blocks with an fp16 scale):
   prefill_8192       8192 tokens x 1 layer
   slot_q3s_t1_48l    1 token x 48 layers, 128 of 512 experts resident per
                      layer (hit rate about 70 %), misses returned
+  decode_q2s_t1      as decode_t1 with scale-only 2-bit blocks (2.5 bits per
+                     weight, 36.3 GB for 48 layers)
 
 Output: one JSON line (see the end of main()).
 """
@@ -45,7 +47,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None, help="timed steps of the primary workload")
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workloads", default="decode_t1,mtp_verify_t4_48l,prefill_8192,slot_q3s_t1_48l")
+    ap.add_argument("--workloads",
+                    default="decode_t1,mtp_verify_t4_48l,prefill_8192,slot_q3s_t1_48l,decode_q2s_t1")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-graph", action="store_true", help="launch steps eagerly")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -186,7 +189,8 @@ def run_steps(ctx, launch, K, W, use_graph, timer_events=False):
 
 # ----------------------------------------------------------------------------
 def decode_stack(ctx, name, layers_needed):
-    """Build the 48-layer Q2SM stack (shared by the decode workloads)."""
+    """Build a stack of packed layers in the workload's format (the 48-layer
+    Q2SM stack is shared by the decode workloads)."""
     w = ctx.synth.WORKLOADS[name]
     shape = ctx.shape(w)
     layers = [ctx.build_layer(shape, 0, l, ctx.dev) for l in range(layers_needed)]
@@ -454,6 +458,24 @@ def main():
         print("slot_q3s_t1_48l: %.3f ms/step hit %.3f" % (r["seconds"] / Kc * 1e3, r["hit_rate"]),
               file=sys.stderr, flush=True)
         del keep, tables, sstack
+        torch.cuda.empty_cache()
+    if "decode_q2s_t1" in wl:
+        qstack = decode_stack(ctx, "decode_q2s_t1", 48)
+        r = bench_decode_t1(ctx, qstack, K, W, use_graph)
+        achieved = r["bytes_per_launch"] / r["kernel_s"] / 1e9
+        results["decode_q2s_t1"] = dict(
+            value=r["tokens"] / r["seconds"], unit="tokens/s", steps=K,
+            ms_per_step=r["seconds"] / K * 1e3,
+            config="1 token x 1 layer rotated over 48 resident layers, Q2S (scale-only 2-bit, "
+                   "2.5 bits/weight, 36.3 GB), bf16 in/out",
+            layer_hbm_frac=r["layer_bytes"] / (r["seconds"] / K) / 1e9 / HBM_PEAK_GBS,
+            roofline={"bound": "hbm", "kernel": "decode_gateup_kernel (Q2S)",
+                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                      "bytes_per_launch": r["bytes_per_launch"], "kernel_us": r["kernel_s"] * 1e6})
+        print("decode_q2s_t1: %.1f us/step, gate/up kernel %.2f us" %
+              (r["seconds"] / K * 1e6, r["kernel_s"] * 1e6), file=sys.stderr, flush=True)
+        del qstack
         torch.cuda.empty_cache()
 
     line = {

@@ -17,7 +17,7 @@ import os
 
 __all__ = [
     "MOE_OK", "MOE_EINVAL", "MOE_EUNSUPPORTED", "MOE_EHIP", "MOE_ENOSPACE",
-    "MOE_Q2SM32", "MOE_Q3S32", "MOE_F32", "MOE_BF16", "MOE_FLAG_RMSNORM_INPUT",
+    "MOE_Q2SM32", "MOE_Q3S32", "MOE_Q2S32", "MOE_F32", "MOE_BF16", "MOE_FLAG_RMSNORM_INPUT",
     "MoeError", "MoeShape", "MoeExpertTable", "MoeMiss", "MoeSlotTable",
     "moe_packed_expert_bytes", "moe_pack_weights", "moe_unpack_weights",
     "moe_workspace_bytes", "moe_layer_forward", "moe_slot_table_init",
@@ -26,7 +26,7 @@ __all__ = [
 ]
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EHIP, MOE_ENOSPACE = 0, -1, -2, -3, -4
-MOE_Q2SM32, MOE_Q3S32 = 1, 2
+MOE_Q2SM32, MOE_Q3S32, MOE_Q2S32 = 1, 2, 3
 MOE_F32, MOE_BF16 = 0, 1
 MOE_FLAG_RMSNORM_INPUT = 1
 

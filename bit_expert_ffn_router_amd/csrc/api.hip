@@ -37,7 +37,7 @@ bool aligned256(const void* p) { return ((uintptr_t)p & 255u) == 0; }
 // Shape checks shared by every entry point.
 moe_status check_shape(const moe_shape* s) {
   if (!s) return fail(MOE_EINVAL, "shape is NULL");
-  if (s->qfmt != MOE_Q2SM32 && s->qfmt != MOE_Q3S32)
+  if (s->qfmt != MOE_Q2SM32 && s->qfmt != MOE_Q3S32 && s->qfmt != MOE_Q2S32)
     return fail(MOE_EINVAL, "unknown qfmt %d", (int)s->qfmt);
   if (s->d_model <= 0 || s->d_model % 256 != 0)
     return fail(MOE_EINVAL, "d_model %d must be a positive multiple of 256", (int)s->d_model);
@@ -208,7 +208,7 @@ moe_status moe_layer_forward(const moe_shape* shape, int32_t tokens, const void*
     return hip_status(moe::launch_decode(a, w, (hipStream_t)stream), "decode launch");
   }
   if (slots) return fail(MOE_EUNSUPPORTED, "slot tables are supported on the decode path (tokens <= 4)");
-  if (shape->qfmt != MOE_Q2SM32) return fail(MOE_EUNSUPPORTED, "prefill path supports Q2SM only");
+  if (shape->qfmt == MOE_Q3S32) return fail(MOE_EUNSUPPORTED, "prefill path supports Q2SM and Q2S only");
   moe::PrefillArgs a;
   a.T = T;
   a.D = shape->d_model;

@@ -10,13 +10,17 @@ namespace moe {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kQ2 = 1;
-constexpr int kQ3 = 2;
+constexpr int kQ2 = 1;   // Q2SM: w = s*u + m
+constexpr int kQ3 = 2;   // Q3S:  w = s*q
+constexpr int kQ2S = 3;  // Q2S:  w = s*(u - 2)
 constexpr int kRecQ2 = 1536;  // bytes of a 16-row x 256-column record
 constexpr int kRecQ3 = 1792;
+constexpr int kRecQ2S = 1280;
 constexpr int kWave = 64;
 
-__host__ __device__ constexpr int rec_bytes(int fmt) { return fmt == kQ2 ? kRecQ2 : kRecQ3; }
+__host__ __device__ constexpr int rec_bytes(int fmt) {
+  return fmt == kQ2 ? kRecQ2 : (fmt == kQ3 ? kRecQ3 : kRecQ2S);
+}
 __host__ __device__ constexpr int octets(int K) { return (K + 255) / 256; }
 
 // Byte offset of the down region inside a packed expert.
@@ -97,7 +101,7 @@ __device__ __forceinline__ DqConsts dq_consts() {
   return k;
 }
 
-// Q2SM code word -> MFMA operands (c + u) for its two blocks.
+// Q2SM / Q2S code word -> MFMA operands (c + u) for its two blocks.
 // Slots 0..3 (block 2w) -> ea.x..ea.w, slots 4..7 (block 2w+1) -> eb.x..eb.w.
 // Offsets c per register: block 2w: 128, 32, 8, 128; block 2w+1: 32, 8, 128, 32.
 __device__ __forceinline__ void dq_q2(uint32_t W, const DqConsts& k, uint4& ea, uint4& eb) {

@@ -235,8 +235,8 @@ __device__ __forceinline__ void build_list(const DecodeArgs& a, const DecodeWs& 
 
 // ----------------------------------------------------------------------------
 // Block parameter helpers.  Q2SM: the two 16-byte parameter loads of a record
-// row hold (scale, min) for blocks 0..3 and 4..7.  Q3S: one 16-byte load holds
-// the 8 scales.
+// row hold (scale, min) for blocks 0..3 and 4..7.  Q3S and Q2S: one 16-byte
+// load holds the 8 scales.
 __device__ __forceinline__ uint32_t sel4(const uint4& v, int i) {
   return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
 }
@@ -278,7 +278,7 @@ __device__ __forceinline__ void record_gemv(const uint4& cw, const uint2& hw, co
 #pragma unroll
     for (int wd = 0; wd < 4; ++wd) {
       uint4 ea, eb;
-      if (FMT == kQ2)
+      if (FMT != kQ3)
         dq_q2(words[wd], kc, ea, eb);
       else
         dq_q3(words[wd], hws[wd >> 1], (wd & 1) != 0, kc, ea, eb);
@@ -308,7 +308,7 @@ __device__ __forceinline__ void record_gemv(const uint4& cw, const uint2& hw, co
 #pragma unroll
       for (int wd = b0 / 2; wd < (b0 + HB) / 2; ++wd) {
         uint4 ea, eb;
-        if (FMT == kQ2)
+        if (FMT != kQ3)
           dq_q2(words[wd], kc, ea, eb);
         else
           dq_q3(words[wd], hws[wd >> 1], (wd & 1) != 0, kc, ea, eb);
@@ -345,7 +345,10 @@ __device__ __forceinline__ void record_gemv(const uint4& cw, const uint2& hw, co
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       const float2 X = xsum(beta, t);
-      const float c = FMT == kQ2 ? m * X.x - s * X.y : -s * (X.y + 4.0f * X.x);
+      // Q2SM: s*(sum (c+u)x - sum cx) + m*sum x; Q3S and Q2S: the code offset
+      // (4 or 2) folds into the same correction.
+      const float c = FMT == kQ2 ? m * X.x - s * X.y
+                                 : -s * (X.y + (FMT == kQ3 ? 4.0f : 2.0f) * X.x);
       mt[t] += on ? c : 0.f;
     }
   }
@@ -360,10 +363,14 @@ __device__ __forceinline__ void load_record(const uint8_t* rec, int lane, uint4&
     pa = *reinterpret_cast<const uint4*>(rec + 1024 + 32 * n);
     pb = *reinterpret_cast<const uint4*>(rec + 1024 + 32 * n + 16);
     hw = make_uint2(0, 0);
-  } else {
+  } else if (FMT == kQ3) {
     hw = *reinterpret_cast<const uint2*>(rec + 1024 + 8 * lane);
     pa = *reinterpret_cast<const uint4*>(rec + 1536 + 16 * n);
     pb = make_uint4(0, 0, 0, 0);
+  } else {
+    pa = *reinterpret_cast<const uint4*>(rec + 1024 + 16 * n);
+    pb = make_uint4(0, 0, 0, 0);
+    hw = make_uint2(0, 0);
   }
 }
 
@@ -818,7 +825,9 @@ static hipError_t launch_decode_t(const DecodeArgs& a, const DecodeWs& w, hipStr
 hipError_t launch_decode(const DecodeArgs& a, const DecodeWs& w, hipStream_t st) {
 #define MOE_DEC_CASE(TT)                                                              \
   case TT:                                                                            \
-    return a.fmt == kQ2 ? launch_decode_t<TT, kQ2>(a, w, st) : launch_decode_t<TT, kQ3>(a, w, st);
+    return a.fmt == kQ2   ? launch_decode_t<TT, kQ2>(a, w, st)                    \
+           : a.fmt == kQ3 ? launch_decode_t<TT, kQ3>(a, w, st)                    \
+                          : launch_decode_t<TT, kQ2S>(a, w, st);
   switch (a.T) {
     MOE_DEC_CASE(1)
     MOE_DEC_CASE(2)

@@ -103,7 +103,7 @@ __global__ __launch_bounds__(64) void pack_kernel(int D, int F, const uint8_t* _
       const uint16_t m = blk < nblk ? mm[pi] : (uint16_t)0;
       *reinterpret_cast<uint32_t*>(rec + 1024 + 4 * e) = (uint32_t)s | ((uint32_t)m << 16);
     } else {
-      *reinterpret_cast<uint16_t*>(rec + 1536 + 2 * e) = s;
+      *reinterpret_cast<uint16_t*>(rec + (FMT == kQ3 ? 1536 : 1024) + 2 * e) = s;
     }
   }
 }
@@ -158,7 +158,7 @@ __global__ __launch_bounds__(64) void unpack_kernel(int D, int F, const uint8_t*
       sm[pi] = (uint16_t)(v & 0xFFFFu);
       if (mins) mins[((size_t)ex * 3 + ri.mat) * (mat_elems / 32) + pi] = (uint16_t)(v >> 16);
     } else {
-      sm[pi] = *reinterpret_cast<const uint16_t*>(rec + 1536 + 2 * e);
+      sm[pi] = *reinterpret_cast<const uint16_t*>(rec + (FMT == kQ3 ? 1536 : 1024) + 2 * e);
     }
   }
 }
@@ -170,9 +170,12 @@ hipError_t launch_pack(int fmt, int D, int F, int n, const void* codes, const ui
   if (fmt == kQ2)
     pack_kernel<kQ2><<<grid, 64, 0, st>>>(D, F, (const uint8_t*)codes, scale, mins,
                                           (uint8_t*)dst, dst_stride);
-  else
+  else if (fmt == kQ3)
     pack_kernel<kQ3><<<grid, 64, 0, st>>>(D, F, (const uint8_t*)codes, scale, nullptr,
                                           (uint8_t*)dst, dst_stride);
+  else
+    pack_kernel<kQ2S><<<grid, 64, 0, st>>>(D, F, (const uint8_t*)codes, scale, nullptr,
+                                           (uint8_t*)dst, dst_stride);
   return hipGetLastError();
 }
 
@@ -183,9 +186,12 @@ hipError_t launch_unpack(int fmt, int D, int F, int n, const void* src, size_t s
   if (fmt == kQ2)
     unpack_kernel<kQ2><<<grid, 64, 0, st>>>(D, F, (const uint8_t*)src, src_stride,
                                             (uint8_t*)codes, scale, mins);
-  else
+  else if (fmt == kQ3)
     unpack_kernel<kQ3><<<grid, 64, 0, st>>>(D, F, (const uint8_t*)src, src_stride,
                                             (uint8_t*)codes, scale, nullptr);
+  else
+    unpack_kernel<kQ2S><<<grid, 64, 0, st>>>(D, F, (const uint8_t*)src, src_stride,
+                                             (uint8_t*)codes, scale, nullptr);
   return hipGetLastError();
 }
 

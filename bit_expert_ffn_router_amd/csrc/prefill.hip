@@ -183,6 +183,13 @@ __device__ __forceinline__ void q2_table(uint32_t sm, uint32_t& lo, uint32_t& hi
   lo = cvt_pk_bf16(m, s + m);
   hi = cvt_pk_bf16(fmaf(2.f, s, m), fmaf(3.f, s, m));
 }
+// Q2S: the four values s*(u - 2) of a block whose fp16 scale is half `hf` of
+// word `sw`.
+__device__ __forceinline__ void q2s_table(uint32_t sw, int hf, uint32_t& lo, uint32_t& hi) {
+  const float s = f16_to_f32((uint16_t)(hf ? (sw >> 16) : (sw & 0xFFFFu)));
+  lo = cvt_pk_bf16(-2.f * s, -s);
+  hi = cvt_pk_bf16(0.f, s);
+}
 // Eight consecutive weights (k = 8q .. 8q+7 of one block) of one weight row:
 // code word W of lane (q, n), block half sh / 8; slot j of the half holds the
 // codes of columns 2j (bits sh+2j) and 2j+1 (bits 16+sh+2j).
@@ -257,9 +264,12 @@ constexpr int kPfDmaB = 6;
 
 // Grouped GEMM tile.  MODE 0: gate/up (A = gathered activations, K = D, B =
 // the expert's gate/up rows, SwiGLU epilogue into H).  MODE 1: down (A = H
-// rows, K = F, B = W_down rows, epilogue into Y).
-template <int MODE>
+// rows, K = F, B = W_down rows, epilogue into Y).  FMT: Q2SM or Q2S weights
+// (the same code words; Q2S records carry scales only).
+template <int MODE, int FMT>
 __global__ __launch_bounds__(kPfThreads, 1) void pf_gemm_kernel(PfArgs a, int nN, int nwork) {
+  static_assert(FMT == kQ2 || FMT == kQ2S, "prefill formats");
+  constexpr int kRec = rec_bytes(FMT);
   __shared__ PfA sa0, sa1, sa2, sa3;
   __shared__ PfB sb0, sb1;
   // wave index as a uniform (scalar) value: the weight addresses stay in SGPRs
@@ -309,16 +319,18 @@ __global__ __launch_bounds__(kPfThreads, 1) void pf_gemm_kernel(PfArgs a, int nN
     int w0 = nb * kBN + (4 * wv + j) * 16;
     if (w0 >= NW) w0 = (j & 1) ? nb * kBN + (4 * wv + j - 1) * 16 : 0;
     if (w0 >= NW) w0 = 0;
-    trec[j] = base + (MODE == 0 ? 0 : down_offset(a.D, F, kQ2)) + (size_t)(w0 / 16) * oK * kRecQ2;
+    trec[j] = base + (MODE == 0 ? 0 : down_offset(a.D, F, FMT)) + (size_t)(w0 / 16) * oK * kRec;
   }
   // (scale, min) pieces: lanes 0..31 / 32..63 take tile 2i / 2i+1 of pair i,
   // 16 bytes each: row lane % 16, blocks 4 h .. 4 h + 3 with h = (lane / 16) % 2
-  // (in LDS: [tile of pair][h][row], so a k-step's reads conflict at most 2-way)
+  // (in LDS: [tile of pair][h][row], so a k-step's reads conflict at most 2-way).
+  // Q2S: the 16 bytes of row lane % 16 hold all 8 scales; both h take them.
   const uint8_t* smp[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const ptrdiff_t d = trec[2 * i + 1] - trec[2 * i];  // uniform; no indexed pointer array
-    smp[i] = trec[2 * i] + (lane >= 32 ? d : 0) + 1024 + 32 * (lane & 15) + 16 * ((lane >> 4) & 1);
+    smp[i] = trec[2 * i] + (lane >= 32 ? d : 0) + 1024 +
+             (FMT == kQ2 ? 32 * (lane & 15) + 16 * ((lane >> 4) & 1) : 16 * (lane & 15));
   }
   const int n = lane & 15, q = lane >> 4;
 
@@ -333,7 +345,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void pf_gemm_kernel(PfArgs a, int nN
     }
   };
   auto issue_b = [&](PfB& B, int o0) __attribute__((always_inline)) {
-    const size_t ro = (size_t)(o0 < oK ? o0 : 0) * kRecQ2;
+    const size_t ro = (size_t)(o0 < oK ? o0 : 0) * kRec;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       dma16(reinterpret_cast<const uint4*>(trec[j] + ro) + lane, &B.code[wv][j][0]);
@@ -364,7 +376,10 @@ __global__ __launch_bounds__(kPfThreads, 1) void pf_gemm_kernel(PfArgs a, int nN
     for (int j = 0; j < 4; ++j) {
       const uint32_t w = wd == 0 ? cwo[j].x : (wd == 1 ? cwo[j].y : (wd == 2 ? cwo[j].z : cwo[j].w));
       uint32_t lo, hi;
-      q2_table(smw[(j >> 1) * 256 + ((j & 1) * 32 + (b >> 2) * 16 + n) * 4 + (b & 3)], lo, hi);
+      if constexpr (FMT == kQ2)
+        q2_table(smw[(j >> 1) * 256 + ((j & 1) * 32 + (b >> 2) * 16 + n) * 4 + (b & 3)], lo, hi);
+      else
+        q2s_table(smw[(j >> 1) * 256 + ((j & 1) * 32 + n) * 4 + (b >> 1)], b & 1, lo, hi);
       bf[j] = q2_frag(w, 8 * kk, lo, hi);
     }
   };
@@ -512,34 +527,43 @@ __global__ __launch_bounds__(kPfThreads, 1) void pf_gemm_kernel(PfArgs a, int nN
 }
 
 // ----------------------------------------------------------------------------
-// out_t = sum_j g_tj * Y[inv[t*k + j]] + Y[P + t], in a fixed order.
-__global__ __launch_bounds__(256) void pf_combine_kernel(PfArgs a, int has_shared) {
-  const int t = blockIdx.x, tid = threadIdx.x;
-  const int P = a.T * a.k, D = a.D;
-  for (int c = tid; c < D / 8; c += 256) {
+// out_t = sum_j g_tj * Y[inv[t*k + j]] + Y[P + t], in a fixed order.  One
+// block per token: the token's rows and gates go to LDS first, then each
+// thread has all of its 16-byte pieces of those rows in flight together (up
+// to 16 at a time) before it sums them in order j = 0..k-1.
+__global__ __launch_bounds__(512) void pf_combine_kernel(PfArgs a, int has_shared) {
+  __shared__ int32_t s_row[kMaxTopK];
+  __shared__ float s_g[kMaxTopK];
+  const int t = blockIdx.x, tid = threadIdx.x, k = a.k;
+  const int P = a.T * k, D = a.D;
+  if (tid < k) {
+    s_row[tid] = a.w.inv[(size_t)t * k + tid];
+    s_g[tid] = a.w.gate[(size_t)t * k + tid];
+  }
+  __syncthreads();
+  auto add = [](float (&o)[8], const uint4& y, float g) __attribute__((always_inline)) {
+    const uint32_t yy[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[2 * i] += g * bf16_lo(yy[i]);
+      o[2 * i + 1] += g * bf16_hi(yy[i]);
+    }
+  };
+  for (int c = tid; c < D / 8; c += blockDim.x) {
     float o[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) o[i] = 0.f;
-    for (int j = 0; j < a.k; ++j) {
-      const int p = t * a.k + j;
-      const float g = a.w.gate[p];
-      const uint4 y = reinterpret_cast<const uint4*>(a.w.Y + (size_t)a.w.inv[p] * D)[c];
-      const uint32_t yy[4] = {y.x, y.y, y.z, y.w};
+    const uint4 ys = reinterpret_cast<const uint4*>(a.w.Y + (size_t)(P + t) * D)[has_shared ? c : 0];
+    for (int j0 = 0; j0 < k; j0 += 16) {
+      uint4 y[16];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        o[2 * i] += g * bf16_lo(yy[i]);
-        o[2 * i + 1] += g * bf16_hi(yy[i]);
-      }
-    }
-    if (has_shared) {
-      const uint4 y = reinterpret_cast<const uint4*>(a.w.Y + (size_t)(P + t) * D)[c];
-      const uint32_t yy[4] = {y.x, y.y, y.z, y.w};
+      for (int jj = 0; jj < 16; ++jj)
+        if (j0 + jj < k) y[jj] = reinterpret_cast<const uint4*>(a.w.Y + (size_t)s_row[j0 + jj] * D)[c];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        o[2 * i] += bf16_lo(yy[i]);
-        o[2 * i + 1] += bf16_hi(yy[i]);
-      }
+      for (int jj = 0; jj < 16; ++jj)
+        if (j0 + jj < k) add(o, y[jj], s_g[j0 + jj]);
     }
+    if (has_shared) add(o, ys, 1.f);
     if (a.out_bf16) {
       uint4 v;
       v.x = pack_bf16x2(o[0], o[1]);
@@ -588,11 +612,21 @@ hipError_t launch_prefill(const PrefillArgs& pa, void* ws, hipStream_t st) {
   const int nN_gu = (2 * w.Fmax + kBN - 1) / kBN;
   const int nN_dn = (D + kBN - 1) / kBN;
   const int nw_gu = w.max_tiles * nN_gu, nw_dn = w.max_tiles * nN_dn;
-  if ((e = launch_timed(pf_gemm_kernel<0>, dim3((nw_gu + 7) / 8 * 8), dim3(kPfThreads), 0u, st, a,
-                        nN_gu, nw_gu)) != hipSuccess)
-    return e;
-  pf_gemm_kernel<1><<<(nw_dn + 7) / 8 * 8, kPfThreads, 0, st>>>(a, nN_dn, nw_dn);
-  pf_combine_kernel<<<T, 256, 0, st>>>(a, has_sh);
+  if (pa.fmt == kQ2) {
+    if ((e = launch_timed(pf_gemm_kernel<0, kQ2>, dim3((nw_gu + 7) / 8 * 8), dim3(kPfThreads), 0u,
+                          st, a, nN_gu, nw_gu)) != hipSuccess)
+      return e;
+    pf_gemm_kernel<1, kQ2><<<(nw_dn + 7) / 8 * 8, kPfThreads, 0, st>>>(a, nN_dn, nw_dn);
+  } else {
+    if ((e = launch_timed(pf_gemm_kernel<0, kQ2S>, dim3((nw_gu + 7) / 8 * 8), dim3(kPfThreads), 0u,
+                          st, a, nN_gu, nw_gu)) != hipSuccess)
+      return e;
+    pf_gemm_kernel<1, kQ2S><<<(nw_dn + 7) / 8 * 8, kPfThreads, 0, st>>>(a, nN_dn, nw_dn);
+  }
+  // One thread per 16-byte piece of a row (384 for d_model 3072), at least
+  // one wave, at most 512 threads.
+  const int cthreads = std::min(512, std::max(64, (D / 8 + 63) / 64 * 64));
+  pf_combine_kernel<<<T, cthreads, 0, st>>>(a, has_sh);
   return hipGetLastError();
 }
 

@@ -45,11 +45,18 @@
  *   MOE_Q2SM32: u in {0,1,2,3}, fp16 scale s and fp16 min m per block:
  *               w = s*u + m                                (3.0 bits/weight)
  *   MOE_Q3S32:  q in {-4..3}, fp16 scale s per block: w = s*q  (3.5 bits/weight)
+ *   MOE_Q2S32:  u in {0,1,2,3}, fp16 scale s per block: w = s*(u - 2)
+ *               (2.5 bits/weight).  The pages' fastest tier is a uniform
+ *               2-bit format of about this footprint ([KC-en] sections
+ *               "Detailed Performance Numbers" and "Memory Requirements
+ *               (RAM + VRAM combined)"); they give no formula, and the zero
+ *               point in the middle of the four codes is the reading taken
+ *               here.
  *
  * Logical (unpacked) expert weights, the input of moe_pack_weights, for an
  * expert of model width D and FFN width F: three matrices in the order
  * W_gate [F][D], W_up [F][D], W_down [D][F], each row-major; codes are one
- * byte per weight ([3][F*D]; Q2SM: u; Q3S: q as a signed byte); scales and
+ * byte per weight ([3][F*D]; Q2SM, Q2S: u; Q3S: q as a signed byte); scales and
  * mins are fp16 bit patterns, one per block ([3][F*D/32], row-major over
  * [rows][K/32]).
  *
@@ -73,6 +80,8 @@
  *     2h+1: the high bit ((q+4) >> 2) of the code at bit p of low word 2h is
  *     bit p+1 of the high word, of low word 2h+1 bit p; bytes [1536,1792):
  *     the fp16 scale of (row n, block b) at byte 1536 + 2*(8*n + b).
+ *   Q2S record, 1280 bytes: bytes [0,1024) code words as in Q2SM; bytes
+ *     [1024,1280): the fp16 scale of (row n, block b) at byte 1024 + 2*(8*n + b).
  * A packed expert is its gate/up region followed by its down region:
  *   gate/up: for g in 0..F/16-1, for matrix in (W_gate, W_up), for each
  *     octet o of D: the record of rows 16g..16g+15, columns 256o..256o+255;
@@ -100,7 +109,7 @@ typedef enum {
   MOE_ENOSPACE = -4      /* workspace or miss-list capacity too small */
 } moe_status;
 
-typedef enum { MOE_Q2SM32 = 1, MOE_Q3S32 = 2 } moe_qfmt;
+typedef enum { MOE_Q2SM32 = 1, MOE_Q3S32 = 2, MOE_Q2S32 = 3 } moe_qfmt;
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
 /* Input flag of moe_layer_forward: normalise each token's input first,
@@ -154,10 +163,11 @@ typedef struct {
 size_t moe_packed_expert_bytes(const moe_shape* shape, int32_t d_ff);
 
 /* Pack n logical experts (layout above) into the packed format.
- *   codes:  device, n*3*d_ff*d_model bytes (Q2SM: u in 0..3; Q3S: signed q
- *           in -4..3; only the low 2 resp. 3 bits of u resp. q+4 are used).
+ *   codes:  device, n*3*d_ff*d_model bytes (Q2SM, Q2S: u in 0..3; Q3S:
+ *           signed q in -4..3; only the low 2 resp. 3 bits of u resp. q+4
+ *           are used).
  *   scale:  device fp16 bits, n*3*d_ff*d_model/32.
- *   min:    device fp16 bits, same size (Q2SM), NULL for Q3S.
+ *   min:    device fp16 bits, same size (Q2SM), NULL for Q3S and Q2S.
  *   dst:    device; expert i is written at dst + i*dst_stride
  *           (dst_stride >= moe_packed_expert_bytes, multiple of 256).
  * Deterministic; the output bytes depend only on the inputs. */
@@ -167,7 +177,7 @@ moe_status moe_pack_weights(const moe_shape* shape, int32_t n, int32_t d_ff,
 
 /* Inverse of moe_pack_weights (padding dropped), for round trips and
  * inspection.  Q3S codes come back as signed q; min is not written for Q3S
- * (may be NULL). */
+ * and Q2S (may be NULL). */
 moe_status moe_unpack_weights(const moe_shape* shape, int32_t n, int32_t d_ff,
                               const void* src, size_t src_stride,
                               void* codes, uint16_t* scale, uint16_t* min,
@@ -201,7 +211,8 @@ size_t moe_workspace_bytes(const moe_shape* shape, int32_t tokens);
  * Paths: T <= 4 runs the decode path (dequantising MFMA GEMV that streams
  * each distinct selected expert once); larger T runs the prefill path
  * (routing, stable token permutation, grouped MFMA GEMM, combine).  The
- * prefill path supports MOE_Q2SM32 only (MOE_EUNSUPPORTED otherwise).
+ * prefill path supports MOE_Q2SM32 and MOE_Q2S32 (MOE_EUNSUPPORTED for
+ * MOE_Q3S32).
  * Results are deterministic: the same inputs give the same output bits. */
 moe_status moe_layer_forward(const moe_shape* shape, int32_t tokens,
                              const void* x, int32_t x_dtype, uint32_t flags,

@@ -103,10 +103,24 @@ def dequant_q3s(codes, scale_bits, rows: int, cols: int) -> np.ndarray:
     return np.repeat(s, 32, axis=1) * q
 
 
+def dequant_q2s(codes, scale_bits, rows: int, cols: int) -> np.ndarray:
+    """Q2S: w = s*(u - 2) with u in {0,1,2,3} and s the fp16 scale of the block.
+
+    The pages' fastest tier is a uniform 2-bit format of about 2.5 bits per
+    weight ([KC-en] "Detailed Performance Numbers", "Memory Requirements (RAM
+    + VRAM combined)"); they give no formula.  Reading taken: one fp16 scale
+    per 32-weight block and the zero point in the middle of the four codes.
+    """
+    u = np.asarray(codes, dtype=np.uint8).reshape(rows, cols).astype(np.float64)
+    s = f16_to_f64(scale_bits).reshape(rows, cols // 32)
+    return np.repeat(s, 32, axis=1) * (u - 2.0)
+
+
 def expert_matrices(codes, scale_bits, min_bits, d_model: int, d_ff: int, fmt: int):
     """Logical expert weights -> (W_gate [F][D], W_up [F][D], W_down [D][F]) in float64.
 
-    ``fmt`` 1 = Q2SM, 2 = Q3S (the same numbering as the library's formats).
+    ``fmt`` 1 = Q2SM, 2 = Q3S, 3 = Q2S (the same numbering as the library's
+    formats).
     """
     D, F = d_model, d_ff
     codes = np.asarray(codes).reshape(3, F * D)
@@ -120,6 +134,8 @@ def expert_matrices(codes, scale_bits, min_bits, d_model: int, d_ff: int, fmt: i
             out.append(dequant_q2sm(codes[mat], sc[mat], mn[mat], r, c))
         elif fmt == 2:
             out.append(dequant_q3s(codes[mat], sc[mat], r, c))
+        elif fmt == 3:
+            out.append(dequant_q2s(codes[mat], sc[mat], r, c))
         else:
             raise ValueError("unknown format %r" % (fmt,))
     return tuple(out)
@@ -276,13 +292,15 @@ def rms_chain(y):
 # 512 B of high-plane words (2 per lane; word h covers low words 2h and
 # 2h+1: the high bit of the code at bit p of low word 2h sits at bit p+1, of
 # low word 2h+1 at bit p), then for n in 0..15, b in 0..7: fp16 scale.
+# Q2S record (1280 B): 1024 B of code words as in Q2SM, then for n in 0..15,
+# b in 0..7: fp16 scale.
 #
 # Expert = gate/up region (for g in 0..F/16-1, for m in (gate, up), for each
 # K-octet of D: the record of rows 16g..16g+15 of matrix m), then the down
 # region (for r in 0..D/16-1, for each K-octet of F (padded): the record of
 # rows 16r..16r+15 of W_down).
 
-REC_BYTES = {1: 1536, 2: 1792}
+REC_BYTES = {1: 1536, 2: 1792, 3: 1280}
 
 
 def _octets(K: int) -> int:
@@ -290,7 +308,7 @@ def _octets(K: int) -> int:
 
 
 def _pack_matrix(codes, scale_bits, min_bits, R: int, K: int, fmt: int) -> bytes:
-    """Pack one [R][K] matrix (codes: uint8 u (Q2SM) or u3 = q+4 (Q3S)).
+    """Pack one [R][K] matrix (codes: uint8 u (Q2SM, Q2S) or u3 = q+4 (Q3S)).
 
     Column index inside the padded row: col = 256*o + 32*b + 8*q + 2*j + h
     with b = 2*w + bb, so the codes are viewed as
@@ -393,7 +411,7 @@ def unpack_expert(buf: bytes, d_model: int, d_ff: int, fmt: int):
                 off += rb
                 lo = rec[:1024].view("<u4").reshape(64, 4)
                 hi = rec[1024:1536].view("<u4").reshape(64, 2) if fmt == 2 else None
-                par = rec[1024 if fmt == 1 else 1536:].view("<u2").reshape(16, 8, 2 if fmt == 1 else 1)
+                par = rec[1536 if fmt == 2 else 1024:].view("<u2").reshape(16, 8, 2 if fmt == 1 else 1)
                 for lane in range(64):
                     n, q = lane % 16, lane // 16
                     row = 16 * rt + n
@@ -436,4 +454,6 @@ def unpack_expert(buf: bytes, d_model: int, d_ff: int, fmt: int):
     if fmt == 1:
         mins[0], mins[1], mins[2] = gate_m.reshape(-1), up_m.reshape(-1), dm.reshape(-1)
         return codes, scale, mins
+    if fmt == 3:
+        return codes, scale, None
     return (codes.astype(np.int16) - 4).astype(np.int8), scale, None

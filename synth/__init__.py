@@ -30,6 +30,8 @@ reduction dimension of one output row):
 * Q3S (signed 3-bit codes q in {-4..3}, fp16 scale per block): the low two
   bits of u3 = q + 4 are the Q2SM code words above, the high bit is bit k of
   draw(key(field=2), block); the scale is drawn as for Q2SM.
+* Q2S (2-bit codes u in {0..3}, fp16 scale per block): codes and scale as
+  for Q2SM, no min.
 * TAB_SCALE[i] = fp16_RNE(|Phi^-1((i + 0.5) / 65536)| * 0.02) and
   TAB_MIN[i] = fp16_RNE(Phi^-1((i + 0.5) / 65536) * 0.01): 65536-point
   inverse-CDF tables of |N(0, 0.02)| and N(0, 0.01) (standard deviations),
@@ -38,8 +40,8 @@ reduction dimension of one output row):
 Logical weight arrays of one expert with model width D and FFN width F:
 ``codes[3][F*D]`` (matrix 0 = W_gate [F][D], 1 = W_up [F][D], 2 = W_down
 [D][F], each row-major) and ``scale[3][F*D/32]`` / ``min[3][F*D/32]`` (one
-entry per block, row-major over [rows][K/32]).  Q2SM codes are u in 0..3;
-Q3S codes are stored as the signed byte q in -4..3.
+entry per block, row-major over [rows][K/32]).  Q2SM and Q2S codes are u in
+0..3; Q3S codes are stored as the signed byte q in -4..3.
 """
 from __future__ import annotations
 
@@ -48,7 +50,7 @@ import numpy as np
 __all__ = [
     "GAMMA", "mix64", "stream_key", "draw", "tables", "expert_weights",
     "activations_bf16", "router_logits", "zipf_log_popularity",
-    "bf16_bits_from_f32", "WORKLOADS", "FMT_Q2SM", "FMT_Q3S",
+    "bf16_bits_from_f32", "WORKLOADS", "FMT_Q2SM", "FMT_Q3S", "FMT_Q2S",
 ]
 
 GAMMA = np.uint64(0x9E3779B97F4A7C15)
@@ -57,6 +59,7 @@ _M2 = np.uint64(0x94D049BB133111EB)
 
 FMT_Q2SM = 1
 FMT_Q3S = 2
+FMT_Q2S = 3
 
 FIELD_CODES = 0
 FIELD_SCALE_MIN = 1
@@ -111,9 +114,9 @@ def expert_weights(seed: int, layer: int, expert: int, d_model: int, d_ff: int,
                    fmt: int = FMT_Q2SM):
     """Logical weights of one expert.
 
-    Returns (codes, scale, min): codes uint8 [3][d_ff*d_model] (Q2SM: u in
-    0..3) or int8 (Q3S: q in -4..3); scale, min uint16 fp16 bit patterns
-    [3][d_ff*d_model/32] (min is None for Q3S).
+    Returns (codes, scale, min): codes uint8 [3][d_ff*d_model] (Q2SM, Q2S:
+    u in 0..3) or int8 (Q3S: q in -4..3); scale, min uint16 fp16 bit
+    patterns [3][d_ff*d_model/32] (min is None for Q3S and Q2S).
     """
     assert d_model % 32 == 0 and d_ff % 32 == 0
     n = d_ff * d_model
@@ -133,6 +136,8 @@ def expert_weights(seed: int, layer: int, expert: int, d_model: int, d_ff: int,
         if fmt == FMT_Q2SM:
             codes[mat] = lo.reshape(-1)
             mins[mat] = tm[((sm >> np.uint64(16)) & np.uint64(0xFFFF)).astype(np.int64)]
+        elif fmt == FMT_Q2S:
+            codes[mat] = lo.reshape(-1)
         elif fmt == FMT_Q3S:
             h = draw(stream_key(seed, layer, expert, mat, FIELD_Q3_HIGH), blk)
             hi = ((h[:, None] >> shifts1[None, :]) & np.uint64(1)).astype(np.uint8)
@@ -242,6 +247,9 @@ WORKLOADS = {
     "prefill_8192": dict(d_model=3072, d_ff=512, n_experts=512, top_k=10, d_ff_shared=512,
                          tokens=8192, layers=1, fmt=FMT_Q2SM, x_dtype="bf16", zipf_s=1.1,
                          alpha=1.0, min_gap=None),
+    "decode_q2s_t1": dict(d_model=3072, d_ff=512, n_experts=512, top_k=10, d_ff_shared=512,
+                          tokens=1, layers=1, fmt=FMT_Q2S, x_dtype="bf16", zipf_s=1.1,
+                          alpha=1.0, min_gap=None),
     "slot_q3s_t1_48l": dict(d_model=3072, d_ff=512, n_experts=512, top_k=10,
                             d_ff_shared=512, tokens=1, layers=48, fmt=FMT_Q3S,
                             x_dtype="bf16", zipf_s=SLOT_ZIPF_S, alpha=SLOT_ALPHA,

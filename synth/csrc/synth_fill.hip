@@ -78,7 +78,7 @@ extern "C" int synth_fill_expert_weights(uint64_t seed, int layer, int expert0, 
                                          const uint16_t* tab_min, void* codes, uint16_t* scale,
                                          uint16_t* mins, hipStream_t stream) {
   if (n <= 0) return 0;
-  if (d_model % 32 || d_ff % 32 || (fmt != 1 && fmt != 2) || !codes || !scale || !tab_scale ||
+  if (d_model % 32 || d_ff % 32 || fmt < 1 || fmt > 3 || !codes || !scale || !tab_scale ||
       (fmt == 1 && (!mins || !tab_min)))
     return -1;
   const int nblk = d_ff * d_model / 32;

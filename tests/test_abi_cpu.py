@@ -41,6 +41,8 @@ def test_every_header_function_is_exported():
 def test_packed_bytes_formula():
     assert moe.moe_packed_expert_bytes(shape(d_model=3072, d_ff=512), 512) == 1769472
     assert moe.moe_packed_expert_bytes(shape(d_model=3072, d_ff=512, qfmt=2), 512) == 2064384
+    assert moe.moe_packed_expert_bytes(shape(d_model=3072, d_ff=512, qfmt=3), 512) == 1474560
+    assert moe.moe_packed_expert_bytes(shape(qfmt=4), 64) == 0   # unknown format
     # padding of the down reduction (d_ff = 64 -> one 256-column octet)
     assert moe.moe_packed_expert_bytes(shape(), 64) == 2 * 4 * 1 * 1536 + 16 * 1 * 1536
     assert moe.moe_packed_expert_bytes(shape(d_model=100), 64) == 0

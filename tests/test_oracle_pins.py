@@ -49,6 +49,25 @@ def test_dequant_unit_scale_returns_codes():
     q, _, _ = synth.expert_weights(0, 0, 0, 256, 64, synth.FMT_Q3S)
     w3 = O.dequant_q3s(q[0], one, 64, 256)
     assert np.array_equal(w3, q[0].reshape(64, 256).astype(np.float64))
+    # Q2S: unit scale gives the codes moved to a zero point in the middle of
+    # 0..3, i.e. the values -2, -1, 0, 1
+    u, _, _ = synth.expert_weights(0, 0, 0, 256, 64, synth.FMT_Q2S)
+    w2 = O.dequant_q2s(u[0], one, 64, 256)
+    assert np.array_equal(w2, u[0].reshape(64, 256).astype(np.float64) - 2.0)
+    assert set(np.unique(w2).tolist()) == {-2.0, -1.0, 0.0, 1.0}
+
+
+def test_dequant_q2s_brute_force_blocks():
+    rng = np.random.default_rng(2)
+    R, K = 3, 96
+    u = rng.integers(0, 4, R * K).astype(np.uint8)
+    s = rng.integers(0, 0xFBFF, R * K // 32).astype(np.uint16)   # both signs, subnormals
+    w = O.dequant_q2s(u, s, R, K)
+    for r in range(R):
+        for c in range(K):
+            blk = r * (K // 32) + c // 32
+            sv = float(np.uint16(s[blk]).view(np.float16))
+            assert w[r, c] == sv * (int(u[r * K + c]) - 2)
 
 
 def test_dequant_brute_force_blocks():
@@ -278,12 +297,12 @@ def test_pack_hand_derived_bit_positions_q3s():
     assert rec[1620:1622].view("<u2")[0] == 0x2222
 
 
-@pytest.mark.parametrize("fmt", [synth.FMT_Q2SM, synth.FMT_Q3S])
+@pytest.mark.parametrize("fmt", [synth.FMT_Q2SM, synth.FMT_Q3S, synth.FMT_Q2S])
 def test_pack_round_trip_and_size(fmt):
-    for D, F in ((256, 64), (512, 256)):
+    for D, F in ((256, 64), (512, 256), (256, 96)):
         c, s, m = synth.expert_weights(0, 1, 2, D, F, fmt)
         buf = O.pack_expert(c, s, m, D, F, fmt)
-        rb = 1536 if fmt == 1 else 1792
+        rb = {1: 1536, 2: 1792, 3: 1280}[fmt]
         assert len(buf) == 2 * (F // 16) * (D // 256) * rb + (D // 16) * ((F + 255) // 256) * rb
         c2, s2, m2 = O.unpack_expert(buf, D, F, fmt)
         assert np.array_equal(c2.view(np.uint8), c.view(np.uint8))
@@ -291,7 +310,38 @@ def test_pack_round_trip_and_size(fmt):
         assert (m is None and m2 is None) or np.array_equal(m2, m)
 
 
+def test_pack_hand_derived_bit_positions_q2s():
+    # Code words exactly as in Q2SM (row 5, column 77 -> word 85, bit 20);
+    # the scale of (row 5, block 2) at byte 1024 + (5*8 + 2)*2 = 1108, and
+    # nothing else in the 1280-byte record.
+    codes = np.zeros((16, 256), np.uint8)
+    codes[5, 77] = 3
+    s = np.zeros((16, 8), np.uint16); s[5, 2] = 0x3456
+    rec = np.frombuffer(O._pack_matrix(codes, s, None, 16, 256, 3), np.uint8)
+    assert rec.size == 1280
+    words = rec[:1024].view("<u4")
+    assert words[85] == 3 << 20 and np.count_nonzero(words) == 1
+    assert rec[1108:1110].view("<u2")[0] == 0x3456 and np.count_nonzero(rec[1024:]) <= 2
+
+
+def test_q2s_record_is_q2sm_record_without_mins():
+    # Same codes and scales: every Q2S record is the Q2SM record's code words
+    # followed by the scale halves of its (scale, min) pairs.
+    D, F = 512, 96
+    c, s, m = synth.expert_weights(0, 2, 3, D, F, synth.FMT_Q2SM)
+    c2, s2, m2 = synth.expert_weights(0, 2, 3, D, F, synth.FMT_Q2S)
+    assert m2 is None and np.array_equal(c, c2) and np.array_equal(s, s2)
+    a = np.frombuffer(O.pack_expert(c, s, m, D, F, 1), np.uint8).reshape(-1, 1536)
+    b = np.frombuffer(O.pack_expert(c2, s2, None, D, F, 3), np.uint8).reshape(-1, 1280)
+    assert a.shape[0] == b.shape[0]
+    assert np.array_equal(a[:, :1024], b[:, :1024])
+    pairs = a[:, 1024:].copy().view("<u2").reshape(a.shape[0], 128, 2)
+    assert np.array_equal(pairs[:, :, 0], b[:, 1024:].copy().view("<u2"))
+
+
 def test_packed_size_full_width_matches_page_accounting():
-    # 3 bits per weight (Q2SM) and 3.5 (Q3S) on a 3072 x 512 SwiGLU expert
+    # 3 bits per weight (Q2SM), 3.5 (Q3S) and 2.5 (Q2S) on a 3072 x 512
+    # SwiGLU expert
     assert O.packed_expert_bytes(3072, 512, 1) == 3 * 3072 * 512 * 3 // 8
     assert O.packed_expert_bytes(3072, 512, 2) == 3 * 3072 * 512 * 7 // 16
+    assert O.packed_expert_bytes(3072, 512, 3) == 3 * 3072 * 512 * 5 // 16

@@ -34,6 +34,9 @@ def test_expert_weights_deterministic_and_in_range():
     assert m is None and q.dtype == np.int8 and q.min() == -4 and q.max() == 3
     # the low two bits of u3 = q + 4 are the Q2SM code stream of the same key
     assert np.array_equal(((q.astype(np.int16) + 4) & 3).astype(np.uint8), c1)
+    # Q2S: the Q2SM codes and scales of the same key, no min
+    u, s2, m2 = synth.expert_weights(0, 3, 7, 256, 64, synth.FMT_Q2S)
+    assert m2 is None and np.array_equal(u, c1) and np.array_equal(s2, s1)
     # codes are uniform: each value about 1/4 (Q2SM) or 1/8 (Q3S) of the draws
     assert np.allclose(np.bincount(c1.reshape(-1), minlength=4) / c1.size, 0.25, atol=0.01)
     assert np.allclose(np.bincount((q.reshape(-1) + 4), minlength=8) / q.size, 0.125, atol=0.01)
