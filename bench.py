@@ -21,6 +21,9 @@ scale and min, or signed 3-bit blocks with an fp16 scale):
                      layer (hit rate about 70 %), misses returned
   decode_q2s_t1      as decode_t1 with scale-only 2-bit blocks (2.5 bits per
                      weight, 36.3 GB for 48 layers)
+  decode_router_t1   decode_t1 with the router projection (bf16 W_r [512][3072]
+                     per layer) computed on the GPU ahead of the top-k
+  prefill_router_8192  prefill_8192 with the router projection (bf16 MFMA GEMM)
 
 Output: one JSON line (see the end of main()).
 """
@@ -48,7 +51,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=None, help="timed steps of the primary workload")
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workloads",
-                    default="decode_t1,mtp_verify_t4_48l,prefill_8192,slot_q3s_t1_48l,decode_q2s_t1")
+                    default="decode_t1,mtp_verify_t4_48l,prefill_8192,slot_q3s_t1_48l,decode_q2s_t1,"
+                            "decode_router_t1,prefill_router_8192")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-graph", action="store_true", help="launch steps eagerly")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -140,7 +144,7 @@ class HipEvents:
         self.pairs = []
 
 
-def run_steps(ctx, launch, K, W, use_graph, timer_events=False):
+def run_steps(ctx, launch, K, W, use_graph, timer_events=False, timer="kernel"):
     """Warm up W eager steps, then time exactly K steps.
 
     The timed region replays the K steps captured into one HIP graph (or
@@ -149,6 +153,7 @@ def run_steps(ctx, launch, K, W, use_graph, timer_events=False):
     the library recording a HIP event pair around its dominant kernel in
     each step; that pass is queued behind a device-side spin so the GPU runs
     the steps back to back and the events do not include host launch gaps.
+    timer="router" times the router projection kernel instead.
     Returns (seconds of the timed region, per-step dominant-kernel ms or None).
     """
     torch = ctx.torch
@@ -178,8 +183,9 @@ def run_steps(ctx, launch, K, W, use_graph, timer_events=False):
     if timer_events:
         evs = HipEvents(K)
         torch.cuda._sleep(int(2.0e5 * K))     # ~ tens of microseconds of GPU spin per step
+        arm = ctx.moe.moe_set_router_timer if timer == "router" else ctx.moe.moe_set_kernel_timer
         for i in range(K):
-            ctx.moe.moe_set_kernel_timer(*evs.pairs[i])
+            arm(*evs.pairs[i])
             launch(i)
         torch.cuda.synchronize()
         kms = evs.elapsed_ms()
@@ -307,6 +313,33 @@ def bench_prefill(ctx, stack, K, W, use_graph, n_layers=4):
     kavg = sum(kms) / len(kms) * 1e-3
     return dict(tokens=K * T, seconds=dt, kernel_s=kavg, flops_per_launch=flops_gu,
                 flops_layer=flops_layer)
+
+
+def bench_router(ctx, stack, K, W, use_graph, T, n_layers):
+    """The layer with its router projection: T tokens through one layer per
+    step, rotating over n_layers layers, each with its own bf16 W_r."""
+    torch, moe, synth = ctx.torch, ctx.moe, ctx.synth
+    w, shape, layers = stack
+    L, D, E = min(n_layers, len(layers)), w["d_model"], w["n_experts"]
+    wr = [ctx.dev_u16(synth.router_weights(0, l, E, D)) for l in range(L)]
+    xs = [ctx.dev_u16(synth.activations_bf16(0, 100 + l, T, D)) for l in range(L)]
+    logits = [torch.empty(T * E, dtype=torch.float32, device=ctx.dev) for _ in range(L)]
+    wsb = moe.moe_workspace_bytes(shape, T)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=ctx.dev)
+    out = torch.empty(T * D, dtype=torch.int16, device=ctx.dev)
+    tables = [layers[l].table(router=wr[l]) for l in range(L)]
+
+    def launch(i):
+        l = i % L
+        moe.moe_layer_forward(shape, T, xs[l], moe.MOE_BF16, 0, logits[l], tables[l], out,
+                              moe.MOE_BF16, None, 0, None, ws, wsb)
+
+    launch(0)
+    torch.cuda.synchronize()
+    dt, kms = run_steps(ctx, launch, K, W, use_graph, timer_events=True, timer="router")
+    kavg = sum(kms) / len(kms) * 1e-3
+    return dict(tokens=K * T, seconds=dt, router_s=kavg,
+                router_bytes=E * D * 2 + T * D * 2 + T * E * 4, router_flops=2.0 * T * E * D)
 
 
 def build_slot_stack(ctx, name):
@@ -444,6 +477,39 @@ def main():
                       "kernel_us": r["kernel_s"] * 1e6})
         print("prefill_8192: %.3f ms/step, gate/up kernel %.1f us (%.1f TFLOP/s)" %
               (sps * 1e3, r["kernel_s"] * 1e6, achieved), file=sys.stderr, flush=True)
+    if "decode_router_t1" in wl:
+        if stack is None or len(stack[2]) < 48:
+            stack = decode_stack(ctx, "mtp_verify_t4_48l", 48)
+        r = bench_router(ctx, stack, K, W, use_graph, T=1, n_layers=48)
+        achieved = r["router_bytes"] / r["router_s"] / 1e9
+        results["decode_router_t1"] = dict(
+            value=r["tokens"] / r["seconds"], unit="tokens/s", steps=K,
+            ms_per_step=r["seconds"] / K * 1e3,
+            config="decode_t1 with the router projection on the GPU (bf16 W_r 512 x 3072 per "
+                   "layer, 48 layers rotated)",
+            roofline={"bound": "hbm", "kernel": "router_gemv_kernel (bf16 W_r GEMV)",
+                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                      "bytes_per_launch": r["router_bytes"], "kernel_us": r["router_s"] * 1e6})
+        print("decode_router_t1: %.1f us/step, router kernel %.2f us" %
+              (r["seconds"] / K * 1e6, r["router_s"] * 1e6), file=sys.stderr, flush=True)
+    if "prefill_router_8192" in wl:
+        if stack is None:
+            stack = decode_stack(ctx, "prefill_8192", 4)
+        Kp = max(2, K // 48)
+        r = bench_router(ctx, stack, Kp, 2, use_graph, T=8192, n_layers=4)
+        achieved = r["router_flops"] / r["router_s"] / 1e12
+        results["prefill_router_8192"] = dict(
+            value=r["tokens"] / r["seconds"], unit="tokens/s", steps=Kp,
+            ms_per_step=r["seconds"] / Kp * 1e3,
+            config="prefill_8192 with the router projection on the GPU (bf16 MFMA GEMM "
+                   "8192 x 3072 x 512), 4 layers rotated",
+            roofline={"bound": "mfma", "kernel": "router_gemm_kernel (bf16 MFMA GEMM)",
+                      "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                      "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                      "flops_per_launch": r["router_flops"], "kernel_us": r["router_s"] * 1e6})
+        print("prefill_router_8192: %.3f ms/step, router kernel %.1f us" %
+              (r["seconds"] / Kp * 1e3, r["router_s"] * 1e6), file=sys.stderr, flush=True)
     if stack is not None:
         del stack
         torch.cuda.empty_cache()

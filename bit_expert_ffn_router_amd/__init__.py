@@ -21,8 +21,10 @@ __all__ = [
     "MoeError", "MoeShape", "MoeExpertTable", "MoeMiss", "MoeSlotTable",
     "moe_packed_expert_bytes", "moe_pack_weights", "moe_unpack_weights",
     "moe_workspace_bytes", "moe_layer_forward", "moe_slot_table_init",
-    "moe_slot_table_update", "moe_route", "moe_permute_workspace_bytes", "moe_permute",
-    "moe_last_error", "moe_abi_version", "moe_set_kernel_timer", "LIB_PATH",
+    "moe_slot_table_update", "moe_route", "moe_router_logits", "moe_permute_workspace_bytes",
+    "moe_permute",
+    "moe_last_error", "moe_abi_version", "moe_set_kernel_timer", "moe_set_router_timer",
+    "LIB_PATH",
 ]
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EHIP, MOE_ENOSPACE = 0, -1, -2, -3, -4
@@ -64,7 +66,7 @@ class MoeShape(ctypes.Structure):
 class MoeExpertTable(ctypes.Structure):
     _fields_ = [("routed", ctypes.c_void_p), ("expert_stride", ctypes.c_size_t),
                 ("slot_of", ctypes.c_void_p), ("n_slots", ctypes.c_int32),
-                ("shared", ctypes.c_void_p)]
+                ("shared", ctypes.c_void_p), ("router", ctypes.c_void_p)]
 
 
 class MoeMiss(ctypes.Structure):
@@ -95,9 +97,11 @@ _sigs = {
     "moe_slot_table_init": (_I, [ctypes.POINTER(MoeSlotTable), _P]),
     "moe_slot_table_update": (_I, [ctypes.POINTER(MoeSlotTable), _I, _P, _P, _P, _P]),
     "moe_route": (_I, [_P, _I, _I, _I, _P, _P, _P]),
+    "moe_router_logits": (_I, [ctypes.POINTER(MoeShape), _I, _P, _I, ctypes.c_uint32, _P, _P, _P]),
     "moe_permute_workspace_bytes": (_Z, [_I, _I, _I]),
     "moe_permute": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _Z, _P]),
     "moe_set_kernel_timer": (_I, [_P, _P]),
+    "moe_set_router_timer": (_I, [_P, _P]),
 }
 for _name, (_res, _args) in _sigs.items():
     _f = getattr(_lib, _name)
@@ -182,6 +186,11 @@ def moe_route(logits, tokens, n_experts, top_k, idx, gate, stream=None):
                           _stream(stream)))
 
 
+def moe_router_logits(shape, tokens, x, x_dtype, flags, w_router, logits, stream=None):
+    _check(_lib.moe_router_logits(ctypes.byref(shape), tokens, _ptr(x), x_dtype, flags,
+                                  _ptr(w_router), _ptr(logits), _stream(stream)))
+
+
 def moe_permute_workspace_bytes(tokens: int, top_k: int, n_experts: int) -> int:
     return _lib.moe_permute_workspace_bytes(tokens, top_k, n_experts)
 
@@ -203,3 +212,13 @@ def moe_set_kernel_timer(before, after):
             return ev
         return ev.cuda_event
     _check(_lib.moe_set_kernel_timer(h(before), h(after)))
+
+
+def moe_set_router_timer(before, after):
+    """Time this thread's next router projection kernel (same arguments as
+    moe_set_kernel_timer)."""
+    def h(ev):
+        if ev is None or isinstance(ev, int):
+            return ev
+        return ev.cuda_event
+    _check(_lib.moe_set_router_timer(h(before), h(after)))

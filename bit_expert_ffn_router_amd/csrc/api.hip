@@ -70,6 +70,10 @@ KernelTimer& kernel_timer() {
   thread_local KernelTimer t;
   return t;
 }
+KernelTimer& router_timer() {
+  thread_local KernelTimer t;
+  return t;
+}
 
 }  // namespace moe
 
@@ -82,6 +86,14 @@ moe_status moe_set_kernel_timer(void* before, void* after) {
     return fail(MOE_EINVAL, "before and after must both be set or both be NULL");
   moe::kernel_timer().before = (hipEvent_t)before;
   moe::kernel_timer().after = (hipEvent_t)after;
+  return ok();
+}
+
+moe_status moe_set_router_timer(void* before, void* after) {
+  if ((before == nullptr) != (after == nullptr))
+    return fail(MOE_EINVAL, "before and after must both be set or both be NULL");
+  moe::router_timer().before = (hipEvent_t)before;
+  moe::router_timer().after = (hipEvent_t)after;
   return ok();
 }
 
@@ -165,6 +177,8 @@ moe_status moe_layer_forward(const moe_shape* shape, int32_t tokens, const void*
     return fail(MOE_EINVAL, "table->shared must be given iff d_ff_shared > 0");
   if (table->shared && !aligned256(table->shared))
     return fail(MOE_EINVAL, "table->shared must be 256-byte aligned");
+  if (table->router && ((uintptr_t)table->router & 15u))
+    return fail(MOE_EINVAL, "table->router must be 16-byte aligned");
   const bool slots = table->slot_of != nullptr;
   if (slots) {
     if (table->n_slots <= 0) return fail(MOE_EINVAL, "n_slots must be > 0 with a slot table");
@@ -205,6 +219,12 @@ moe_status moe_layer_forward(const moe_shape* shape, int32_t tokens, const void*
     a.miss = (moe::MissRec*)miss;
     a.miss_count = miss_count;
     const moe::DecodeWs w = moe::decode_ws_carve(ws, T, a.D, a.F, a.Fs, a.E, a.k);
+    if (table->router) {
+      moe::RouterArgs r{T, a.D, a.E, x, a.x_bf16, a.rmsnorm, (const uint16_t*)table->router,
+                        const_cast<float*>(router_logits)};
+      moe_status rs = hip_status(moe::launch_router(r, (hipStream_t)stream), "router launch");
+      if (rs != MOE_OK) return rs;
+    }
     return hip_status(moe::launch_decode(a, w, (hipStream_t)stream), "decode launch");
   }
   if (slots) return fail(MOE_EUNSUPPORTED, "slot tables are supported on the decode path (tokens <= 4)");
@@ -226,7 +246,25 @@ moe_status moe_layer_forward(const moe_shape* shape, int32_t tokens, const void*
   a.shared = (const uint8_t*)table->shared;
   a.out = out;
   a.out_bf16 = out_dtype == MOE_BF16;
+  a.router = (const uint16_t*)table->router;
   return hip_status(moe::launch_prefill(a, ws, (hipStream_t)stream), "prefill launch");
+}
+
+moe_status moe_router_logits(const moe_shape* shape, int32_t tokens, const void* x,
+                             int32_t x_dtype, uint32_t flags, const void* w_router, float* logits,
+                             moe_stream_t stream) {
+  moe_status s = check_shape(shape);
+  if (s != MOE_OK) return s;
+  if (tokens < 0) return fail(MOE_EINVAL, "tokens %d < 0", (int)tokens);
+  if (x_dtype != MOE_BF16 && x_dtype != MOE_F32) return fail(MOE_EINVAL, "bad x_dtype %d", (int)x_dtype);
+  if (flags & ~(uint32_t)MOE_FLAG_RMSNORM_INPUT) return fail(MOE_EINVAL, "unknown flags 0x%x", flags);
+  if (tokens == 0) return ok();
+  if (!x || !w_router || !logits) return fail(MOE_EINVAL, "x, w_router and logits are required");
+  if (((uintptr_t)x & 15u) || ((uintptr_t)w_router & 15u) || ((uintptr_t)logits & 3u))
+    return fail(MOE_EINVAL, "x and w_router must be 16-byte aligned, logits 4-byte aligned");
+  moe::RouterArgs r{tokens, shape->d_model, shape->n_experts, x, x_dtype == MOE_BF16,
+                    (flags & MOE_FLAG_RMSNORM_INPUT) != 0, (const uint16_t*)w_router, logits};
+  return hip_status(moe::launch_router(r, (hipStream_t)stream), "router launch");
 }
 
 moe_status moe_slot_table_init(moe_slot_table* t, moe_stream_t stream) {

@@ -18,17 +18,17 @@ struct MissRec {
 struct KernelTimer {
   hipEvent_t before = nullptr, after = nullptr;
 };
-KernelTimer& kernel_timer();
+KernelTimer& kernel_timer();  // the layer's dominant kernel
+KernelTimer& router_timer();  // the router projection kernel
 
-// Launch `kernel` on st.  When the calling thread has armed the kernel timer,
+// Launch `kernel` on st.  When the calling thread has armed the timer `tm`,
 // the launch carries its two events (hipExtLaunchKernel), which then take the
 // kernel's own start and end timestamps, and the timer is disarmed.  A timed
 // launch is refused while st is capturing a graph.
 template <typename... P, typename... A>
-hipError_t launch_timed(void (*kernel)(P...), dim3 grid, dim3 block, uint32_t lds, hipStream_t st,
-                        A... args) {
+hipError_t launch_timed_by(KernelTimer& tm, void (*kernel)(P...), dim3 grid, dim3 block,
+                           uint32_t lds, hipStream_t st, A... args) {
   static_assert(sizeof...(P) == sizeof...(A), "argument count");
-  KernelTimer& tm = kernel_timer();
   if (tm.before == nullptr) {
     kernel<<<grid, block, lds, st>>>(args...);
     return hipGetLastError();
@@ -42,6 +42,11 @@ hipError_t launch_timed(void (*kernel)(P...), dim3 grid, dim3 block, uint32_t ld
                          tm.before, tm.after, 0);
   tm.before = tm.after = nullptr;
   return e;
+}
+template <typename... P, typename... A>
+hipError_t launch_timed(void (*kernel)(P...), dim3 grid, dim3 block, uint32_t lds, hipStream_t st,
+                        A... args) {
+  return launch_timed_by(kernel_timer(), kernel, grid, block, lds, st, args...);
 }
 
 // ---------------------------------------------------------------- packing
@@ -103,6 +108,18 @@ size_t decode_ws_bytes(int T, int D, int F, int Fs, int E, int k);
 DecodeWs decode_ws_carve(void* ws, int T, int D, int F, int Fs, int E, int k);
 hipError_t launch_decode(const DecodeArgs& a, const DecodeWs& w, hipStream_t st);
 
+// ---------------------------------------------------------------- router projection
+struct RouterArgs {
+  int T, D, E;
+  const void* x;
+  int x_bf16;
+  int rmsnorm;
+  const uint16_t* w;  // bf16 [E][D]
+  float* logits;      // fp32 [T][E]
+};
+bool router_uses_gemv(int T, int D);
+hipError_t launch_router(const RouterArgs& a, hipStream_t st);
+
 // ---------------------------------------------------------------- prefill path
 struct PrefillArgs {
   int T, D, F, Fs, E, k, fmt;
@@ -115,6 +132,7 @@ struct PrefillArgs {
   const uint8_t* shared;
   void* out;
   int out_bf16;
+  const uint16_t* router;  // bf16 [E][D] or null: then `logits` is computed first
 };
 size_t prefill_ws_bytes(int T, int D, int F, int Fs, int E, int k);
 hipError_t launch_prefill(const PrefillArgs& a, void* ws, hipStream_t st);

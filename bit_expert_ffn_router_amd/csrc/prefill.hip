@@ -585,12 +585,16 @@ hipError_t launch_prefill(const PrefillArgs& pa, void* ws, hipStream_t st) {
   const int T = pa.T, D = pa.D, E = pa.E, k = pa.k;
   PfWs w = pf_carve(ws, T, D, pa.F, pa.Fs, E, k);
   hipError_t e;
-  if ((e = launch_route(pa.logits, T, E, k, w.idx, w.gate, st)) != hipSuccess) return e;
   const uint16_t* xb = (const uint16_t*)pa.x;
   if (pa.rmsnorm || !pa.x_bf16) {
     pf_xprep_kernel<<<T, 256, 0, st>>>(pa.x, pa.x_bf16, pa.rmsnorm, D, w.xb);
     xb = w.xb;
   }
+  if (pa.router) {  // logits of the activations the experts see (bf16, after the RMS rule)
+    RouterArgs r{T, D, E, xb, 1, 0, pa.router, const_cast<float*>(pa.logits)};
+    if ((e = launch_router(r, st)) != hipSuccess) return e;
+  }
+  if ((e = launch_route(pa.logits, T, E, k, w.idx, w.gate, st)) != hipSuccess) return e;
   if ((e = launch_permute(w.idx, T, k, E, w.offsets, w.sorted, w.inv, w.perm, st)) != hipSuccess)
     return e;
   const int has_sh = pa.shared != nullptr;

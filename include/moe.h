@@ -141,13 +141,19 @@ typedef struct {
  *                  section "命中率七成，代价是答案会变").
  *   n_slots:       slots in `routed` when slot_of != NULL.
  *   shared:        device; the packed shared expert (width d_ff_shared), or
- *                  NULL when d_ff_shared == 0.  256-byte aligned. */
+ *                  NULL when d_ff_shared == 0.  256-byte aligned.
+ *   router:        device bf16 [n_experts][d_model] router projection W_r
+ *                  (row e = expert e, contiguous along d_model), 16-byte
+ *                  aligned, or NULL.  With it, moe_layer_forward computes the
+ *                  logits itself (see moe_router_logits) and `router_logits`
+ *                  becomes an output. */
 typedef struct {
   const void* routed;
   size_t expert_stride;
   const int32_t* slot_of;
   int32_t n_slots;
   const void* shared;
+  const void* router;
 } moe_expert_table;
 
 /* One routed (token, rank) pair whose expert is not resident. */
@@ -193,6 +199,10 @@ size_t moe_workspace_bytes(const moe_shape* shape, int32_t tokens);
  *                  16-byte aligned.
  *   flags:         0 or MOE_FLAG_RMSNORM_INPUT.
  *   router_logits: device fp32 [T][n_experts], 4-byte aligned; must be finite.
+ *                  An input when table->router is NULL.  Otherwise an output:
+ *                  the layer first writes the router projection of its input
+ *                  there (as moe_router_logits, on the input the experts
+ *                  see) and routes on it.
  *   table:         where the experts are (see moe_expert_table).
  *   out:           device [T][d_model], dtype out_dtype, 16-byte aligned.
  *                  Written in full.
@@ -220,6 +230,25 @@ moe_status moe_layer_forward(const moe_shape* shape, int32_t tokens,
                              void* out, int32_t out_dtype,
                              moe_miss* miss, int32_t miss_cap, int32_t* miss_count,
                              void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/* Router projection (the router the pages keep resident on the GPU, [AF]
+ * section "命中率七成，代价是答案会变"; they give no formula; reading taken:
+ * an unquantised bf16 linear map without bias):
+ *   logits[t][e] = sum_d W_r[e][d] * xhat[t][d],  accumulated in fp32,
+ * xhat = x (flags 0) or bf16(x / sqrt(mean(x^2) + 1e-6)) (MOE_FLAG_RMSNORM_INPUT).
+ *   x:        device [T][d_model], x_dtype MOE_BF16 or MOE_F32, 16-byte aligned.
+ *   w_router: device bf16 [n_experts][d_model], 16-byte aligned.
+ *   logits:   device fp32 [T][n_experts], 4-byte aligned; written in full.
+ * T <= 4 with T*d_model <= 15360 (at d_model 3072: every T <= 4): a GEMV on
+ * the activations as given (fp32 input stays fp32).  Otherwise a bf16 MFMA
+ * GEMM: fp32 input is rounded to bf16
+ * first, exactly as the layer's prefill path rounds it, so that the logits
+ * moe_layer_forward computes for the same input are the same bits.  Only
+ * shape->d_model and shape->n_experts are used (and validated with the rest
+ * of the shape).  T == 0 launches nothing. */
+moe_status moe_router_logits(const moe_shape* shape, int32_t tokens, const void* x,
+                             int32_t x_dtype, uint32_t flags, const void* w_router,
+                             float* logits, moe_stream_t stream);
 
 /* Resident-expert slot table (the GPU hot-expert cache of the pages, [AF]
  * section "命中率七成，代价是答案会变"; [JD] section "为什么从 18t/s 变成
@@ -281,11 +310,17 @@ moe_status moe_permute(const int32_t* idx, int32_t tokens, int32_t top_k, int32_
  * pair.  Thread-local; no device work is done by this call itself. */
 moe_status moe_set_kernel_timer(void* before, void* after);
 
+/* The same for the router projection kernel: the pair is attached to the
+ * next router launch of the calling thread, from moe_router_logits or from a
+ * moe_layer_forward call whose table has a router.  Independent of the pair
+ * of moe_set_kernel_timer; same rules. */
+moe_status moe_set_router_timer(void* before, void* after);
+
 /* The calling thread's message for its last failed call ("" if none). */
 const char* moe_last_error(void);
 
 /* ABI version of this header. */
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 int32_t moe_abi_version(void);
 
 #ifdef __cplusplus

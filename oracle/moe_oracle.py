@@ -168,6 +168,22 @@ def route(logits, k: int):
     return idx, gate
 
 
+def router_logits(x, w_router_bits, rms: bool = False):
+    """Router projection: logits[t][e] = sum_d W_r[e][d] * xhat[t][d].
+
+    The pages keep the router resident on the GPU with the shared expert
+    ([AF] "命中率七成，代价是答案会变") and give no formula.  Reading taken:
+    an unquantised bf16 linear map without bias, applied to the input the
+    experts see (xhat = x, or rms_chain(x) under the RMS input rule).
+    x: float64 [T][D] (exact values of the stored input); w_router_bits:
+    uint16 bf16 bits [E][D].  Returns float64 [T][E].
+    """
+    x = np.asarray(x, dtype=np.float64)
+    xhat = bf16_to_f64(rms_chain(x)) if rms else x
+    w = bf16_to_f64(w_router_bits)
+    return xhat @ w.T
+
+
 # --------------------------------------------------------------------------
 # Token-to-expert permutation (histogram, exclusive scan, stable scatter).
 # Pair p = t*k + j is the j-th expert choice of token t.

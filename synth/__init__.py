@@ -11,7 +11,9 @@ recipe that turns a seed into numbers:
   expert of any layer can be regenerated on its own, on the host (here, with
   numpy) or on the device (``synth/csrc/synth_fill.hip``, bit-identical);
 * bf16 activations ~ N(0, 1);
-* fp32 router logits ~ N(0, 1) plus an optional Zipf log-popularity bias.
+* fp32 router logits ~ N(0, 1) plus an optional Zipf log-popularity bias;
+* bf16 router projection weights ~ N(0, 1/d_model), so that the projected
+  logits of N(0, 1) activations are about N(0, 1) as well.
 
 Counter-based generator: SplitMix64 (G. Steele, D. Lea, C. Flood, "Fast
 splittable pseudorandom number generators", OOPSLA 2014).  Output i of a
@@ -50,7 +52,7 @@ import numpy as np
 __all__ = [
     "GAMMA", "mix64", "stream_key", "draw", "tables", "expert_weights",
     "activations_bf16", "router_logits", "zipf_log_popularity",
-    "bf16_bits_from_f32", "WORKLOADS", "FMT_Q2SM", "FMT_Q3S", "FMT_Q2S",
+    "bf16_bits_from_f32", "WORKLOADS", "FMT_Q2SM", "FMT_Q3S", "FMT_Q2S", "router_weights",
 ]
 
 GAMMA = np.uint64(0x9E3779B97F4A7C15)
@@ -175,6 +177,17 @@ def activations_f32(seed: int, tag: int, tokens: int, d_model: int) -> np.ndarra
     """fp32 activations ~ N(0, 1) [tokens][d_model] (same stream as the bf16 ones)."""
     rng = np.random.default_rng([seed, 1, tag])
     return rng.standard_normal((tokens, d_model)).astype(np.float32)
+
+
+def router_weights(seed: int, layer: int, n_experts: int, d_model: int) -> np.ndarray:
+    """bf16 router projection W_r: uint16 bits [n_experts][d_model].
+
+    float32(N(0, 1) / sqrt(d_model)) from PCG64 seeded with [seed, 4, layer],
+    rounded to bf16.
+    """
+    rng = np.random.default_rng([seed, 4, layer])
+    z = (rng.standard_normal((n_experts, d_model)) / np.sqrt(d_model)).astype(np.float32)
+    return bf16_bits_from_f32(z)
 
 
 def zipf_log_popularity(seed: int, layer: int, n_experts: int, s: float) -> np.ndarray:

@@ -35,7 +35,7 @@ def test_every_header_function_is_exported():
     lib = ctypes.CDLL(moe.LIB_PATH)
     for n in names:
         getattr(lib, n)
-    assert moe.moe_abi_version() == 1
+    assert moe.moe_abi_version() == 2
 
 
 def test_packed_bytes_formula():
@@ -165,3 +165,24 @@ def test_slot_update_validation():
         moe.moe_slot_table_update(t, [0], [1], [None], stream=S)
     # nothing changed on the host
     assert hs[5] == 2 and he[2] == 5 and (hs >= 0).sum() == 1
+
+
+def test_router_argument_checks():
+    sh = shape(d_model=256, d_ff=64)
+    with pytest.raises(moe.MoeError) as ei:                     # misaligned x
+        moe.moe_router_logits(sh, 2, 0x1008, moe.MOE_BF16, 0, 0x2000, 0x3000, S)
+    assert ei.value.status == moe.MOE_EINVAL
+    with pytest.raises(moe.MoeError) as ei:                     # bad dtype
+        moe.moe_router_logits(sh, 2, 0x1000, 7, 0, 0x2000, 0x3000, S)
+    assert ei.value.status == moe.MOE_EINVAL
+    with pytest.raises(moe.MoeError) as ei:                     # missing weights
+        moe.moe_router_logits(sh, 2, 0x1000, moe.MOE_BF16, 0, None, 0x3000, S)
+    assert ei.value.status == moe.MOE_EINVAL
+    moe.moe_router_logits(sh, 0, None, moe.MOE_BF16, 0, None, None, S)   # T == 0: nothing
+    # a misaligned router in the table is rejected before any launch
+    stride = (moe.moe_packed_expert_bytes(sh, 64) + 255) // 256 * 256
+    t = moe.MoeExpertTable(0x10000, stride, None, 0, 0x20000, 0x30008)
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_layer_forward(sh, 2, 0x1000, moe.MOE_BF16, 0, 0x1000, t, 0x1000, moe.MOE_BF16,
+                              None, 0, None, 0x100000, 1 << 30, S)
+    assert ei.value.status == moe.MOE_EINVAL and "router" in moe.moe_last_error()

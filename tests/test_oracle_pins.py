@@ -87,6 +87,30 @@ def test_dequant_brute_force_blocks():
 
 # ---------------------------------------------------------------- routing
 
+def test_router_logits_pins():
+    """One-hot inputs read out W_r's columns exactly; the map is linear in x
+    and in W_r; under the RMS rule a power-of-two scale of x changes nothing
+    (up to the 1e-6 term, whose shift stays far below bf16 resolution here)."""
+    D, E = 256, 24
+    w = synth.router_weights(0, 3, E, D)
+    wf = O.bf16_to_f64(w)
+    eye = np.eye(D)[[0, 5, 255]]
+    assert np.array_equal(O.router_logits(eye, w), wf[:, [0, 5, 255]].T)
+    x = O.bf16_to_f64(synth.activations_bf16(0, 3, 3, D))
+    l1 = O.router_logits(x, w)
+    assert np.array_equal(O.router_logits(4.0 * x, w), 4.0 * l1)
+    w2 = O.f64_to_bf16(2.0 * wf)                    # doubling a bf16 value is exact
+    assert np.array_equal(O.router_logits(x, w2), 2.0 * l1)
+    r1 = O.router_logits(x, w, rms=True)
+    assert np.array_equal(O.router_logits(8.0 * x, w, rms=True), r1)
+    # a row of the projection is a plain dot product, checked with math.fsum
+    import math
+    assert abs(l1[1, 7] - math.fsum(x[1, d] * wf[7, d] for d in range(D))) <= 1e-12 * np.sum(np.abs(x[1] * wf[7]))
+    # the generator: about N(0, 1/D) entries, so the logits of N(0,1) inputs are about N(0,1)
+    big = O.router_logits(O.bf16_to_f64(synth.activations_bf16(0, 4, 64, D)), w)
+    assert 0.8 < np.std(big) < 1.2
+
+
 def test_route_brute_force_tiny():
     lg = synth.router_logits(0, 0, 4, 16, min_gap=1e-3)
     for k in (1, 2, 5, 16):
