@@ -489,7 +489,9 @@ def main():
                    "layer, 48 layers rotated)",
             roofline={"bound": "hbm", "kernel": "router_gemv_kernel (bf16 W_r GEMV)",
                       "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                      "frac": achieved / HBM_PEAK_GBS,
+                      "traffic": traffic_from_profile("router_gemv_t1",
+                                                      ["router.hip", "common.hpp", "kernels.hpp"], None),
                       "bytes_per_launch": r["router_bytes"], "kernel_us": r["router_s"] * 1e6})
         print("decode_router_t1: %.1f us/step, router kernel %.2f us" %
               (r["seconds"] / K * 1e6, r["router_s"] * 1e6), file=sys.stderr, flush=True)
@@ -506,7 +508,9 @@ def main():
                    "8192 x 3072 x 512), 4 layers rotated",
             roofline={"bound": "mfma", "kernel": "router_gemm_kernel (bf16 MFMA GEMM)",
                       "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                      "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                      "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+                      "traffic": traffic_from_profile("router_gemm_8192",
+                                                      ["router.hip", "common.hpp", "kernels.hpp"], None),
                       "flops_per_launch": r["router_flops"], "kernel_us": r["router_s"] * 1e6})
         print("prefill_router_8192: %.3f ms/step, router kernel %.1f us" %
               (r["seconds"] / Kp * 1e3, r["router_s"] * 1e6), file=sys.stderr, flush=True)
@@ -537,7 +541,10 @@ def main():
             layer_hbm_frac=r["layer_bytes"] / (r["seconds"] / K) / 1e9 / HBM_PEAK_GBS,
             roofline={"bound": "hbm", "kernel": "decode_gateup_kernel (Q2S)",
                       "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                      "frac": achieved / HBM_PEAK_GBS,
+                      "traffic": traffic_from_profile(
+                          "decode_gateup_q2s_t1",
+                          ["decode.hip", "common.hpp", "route_common.hpp", "kernels.hpp"], None),
                       "bytes_per_launch": r["bytes_per_launch"], "kernel_us": r["kernel_s"] * 1e6})
         print("decode_q2s_t1: %.1f us/step, gate/up kernel %.2f us" %
               (r["seconds"] / K * 1e6, r["kernel_s"] * 1e6), file=sys.stderr, flush=True)
