@@ -24,6 +24,12 @@ scale and min, or signed 3-bit blocks with an fp16 scale):
   decode_router_t1   decode_t1 with the router projection (bf16 W_r [512][3072]
                      per layer) computed on the GPU ahead of the top-k
   prefill_router_8192  prefill_8192 with the router projection (bf16 MFMA GEMM)
+  slot_policy_q3s_t1_8l  a 2048-token stream through 8 chained Q3S slot layers
+                     (128 resident + 8 spare slots) whose popular experts drift;
+                     the frequency-driven policy plans every 32 tokens and
+                     copies admitted experts from pinned host memory on a
+                     side stream while the next period runs; the same stream
+                     with the policy off is the static baseline
 
 Output: one JSON line (see the end of main()).
 """
@@ -52,7 +58,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workloads",
                     default="decode_t1,mtp_verify_t4_48l,prefill_8192,slot_q3s_t1_48l,decode_q2s_t1,"
-                            "decode_router_t1,prefill_router_8192")
+                            "decode_router_t1,prefill_router_8192,slot_policy_q3s_t1_8l")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-graph", action="store_true", help="launch steps eagerly")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -373,6 +379,185 @@ def build_slot_stack(ctx, name):
     return (w, shape, layers), tables, keep
 
 
+class HipHost:
+    """Pinned host memory of an exact size (hipHostMalloc) and blocking copies."""
+
+    def __init__(self):
+        import ctypes
+        self.ct = ctypes
+        lib = ctypes.CDLL("libamdhip64.so")
+        lib.hipHostMalloc.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_size_t,
+                                      ctypes.c_uint]
+        lib.hipHostMalloc.restype = ctypes.c_int
+        lib.hipHostFree.argtypes = [ctypes.c_void_p]
+        lib.hipHostFree.restype = ctypes.c_int
+        lib.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+        lib.hipMemcpy.restype = ctypes.c_int
+        self.lib, self.ptrs = lib, []
+
+    def alloc(self, n):
+        p = self.ct.c_void_p()
+        if self.lib.hipHostMalloc(self.ct.byref(p), n, 0):
+            raise RuntimeError("hipHostMalloc(%d) failed" % n)
+        self.ptrs.append(p.value)
+        return p.value
+
+    def d2h(self, dst, src, n):
+        if self.lib.hipMemcpy(dst, src, n, 2):
+            raise RuntimeError("hipMemcpy D2H failed")
+
+    def close(self):
+        for p in self.ptrs:
+            self.lib.hipHostFree(p)
+        self.ptrs = []
+
+
+def bench_slot_policy(ctx, name="slot_policy_q3s_t1_8l"):
+    """One token at a time through L chained slot layers over a drifting
+    stream: first with the maps fixed (static), then with the policy.
+
+    Per period of P tokens: the P x L layer calls replay as one HIP graph;
+    then, per layer, the previous plan is committed (the layer stream waits
+    for its copies) and the usage counts are taken.  The next period is
+    queued before the host waits for those counts, so the plan is made on
+    the host while the GPU runs; its experts are copied from pinned host
+    memory into spare slots on a side stream, overlapping that period, and
+    committed after it.
+    """
+    torch, moe, synth, np = ctx.torch, ctx.moe, ctx.synth, ctx.np
+    w = synth.WORKLOADS[name]
+    shape = ctx.shape(w)
+    E, R, SP, L, D, k = (w["n_experts"], w["n_slots"], w["spare_slots"], w["layers"],
+                         w["d_model"], w["top_k"])
+    S, N, P = R + SP, w["stream_tokens"], w["period"]
+    stride = ctx.stride_of(shape, w["d_ff"])
+    eb = moe.moe_packed_expert_bytes(shape, w["d_ff"])
+    hh = HipHost()
+    src = hh.alloc(L * E * stride)                     # every routed expert, packed, in host memory
+    st = []
+    for l in range(L):
+        full = ctx.build_layer(shape, 0, l, ctx.dev)
+        torch.cuda.synchronize()
+        hh.d2h(src + l * E * stride, full.routed.data_ptr(), E * stride)
+        g = synth.zipf_log_popularity(0, l, E, w["zipf_s"])
+        resident = [int(e) for e in np.argsort(-g, kind="stable")[:R]]
+        slot_of = torch.empty(E, dtype=torch.int32, device=ctx.dev)
+        eos = torch.empty(S, dtype=torch.int32, device=ctx.dev)
+        hs, he = np.empty(E, np.int32), np.empty(S, np.int32)
+        storage = torch.empty(S * stride, dtype=torch.uint8, device=ctx.dev)
+        t = moe.MoeSlotTable(E, S, slot_of.data_ptr(), eos.data_ptr(), hs.ctypes.data,
+                             he.ctypes.data, storage.data_ptr(), stride, eb)
+        moe.moe_slot_table_init(t)
+        for i0 in range(0, R, 32):
+            moe.moe_slot_table_update(t, list(range(i0, i0 + 32)), resident[i0:i0 + 32],
+                                      [full.routed.data_ptr() + e * stride for e in resident[i0:i0 + 32]])
+        use = torch.zeros(E, dtype=torch.int32, device=ctx.dev)
+        torch.cuda.synchronize()
+        init = (hs.copy(), he.copy())
+        del full.routed
+        table = moe.MoeExpertTable(storage.data_ptr(), stride, slot_of.data_ptr(), S,
+                                   full.shared.data_ptr(), None, use.data_ptr())
+        st.append(dict(t=t, slot_of=slot_of, eos=eos, hs=hs, he=he, storage=storage, use=use,
+                       shared=full.shared, table=table, init=init))
+        del full
+    logits = [ctx.dev_f32(synth.router_logits_drifting(0, l, N, E, w["zipf_s"], w["alpha"],
+                                                       w["alpha_context"], w["segment"]))
+              for l in range(L)]
+    win = [torch.empty(P * E, dtype=torch.float32, device=ctx.dev) for _ in range(L)]
+    x0 = ctx.dev_u16(synth.activations_bf16(0, 0, P, D)).reshape(-1)
+    wsb = moe.moe_workspace_bytes(shape, 1)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=ctx.dev)
+    acts = [torch.empty(D, dtype=torch.int16, device=ctx.dev) for _ in range(L)]
+    miss = torch.empty(k * 4, dtype=torch.int32, device=ctx.dev)
+    mcount = torch.zeros(P * L, dtype=torch.int32, device=ctx.dev)
+
+    def period_calls():
+        for j in range(P):
+            for l in range(L):
+                x = x0[j * D:(j + 1) * D] if l == 0 else acts[l - 1]
+                fl = 0 if l == 0 else moe.MOE_FLAG_RMSNORM_INPUT
+                moe.moe_layer_forward(shape, 1, x, moe.MOE_BF16, fl, win[l].data_ptr() + 4 * j * E,
+                                      st[l]["table"], acts[l], moe.MOE_BF16, miss, k,
+                                      mcount.data_ptr() + 4 * (j * L + l), ws, wsb)
+
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        period_calls()
+    side = torch.cuda.Stream()
+    host_counts = [torch.empty(E, dtype=torch.int32).pin_memory() for _ in range(L)]
+
+    def run(policy):
+        main = torch.cuda.current_stream()
+        for l, d in enumerate(st):                # same start for both runs
+            moe.moe_slot_table_init(d["t"])
+            res = [int(e) for e in d["init"][1][:R]]
+            for i0 in range(0, R, 32):
+                moe.moe_slot_table_update(d["t"], list(range(i0, i0 + 32)), res[i0:i0 + 32],
+                                          [src + l * E * stride + e * stride
+                                           for e in res[i0:i0 + 32]])
+            d["use"].zero_()
+        torch.cuda.synchronize()
+        pending, staged = [None] * L, [None] * L
+        misses = swaps = 0
+        NP = N // P
+        mc_host = torch.empty(P * L, dtype=torch.int32).pin_memory()
+        ev_res = [torch.cuda.Event(), torch.cuda.Event()]
+        done = [torch.cuda.Event(), torch.cuda.Event()]
+
+        def head(p):                              # period p's layer calls
+            for l in range(L):
+                win[l].copy_(logits[l][p * P:(p + 1) * P].reshape(-1))
+            graph.replay()
+
+        def tail(p):                              # after period p, on the layer stream
+            if policy:
+                for l in range(L):
+                    if pending[l] and pending[l][0]:
+                        main.wait_event(staged[l])
+                        a, v, sl = pending[l]
+                        moe.moe_slot_table_commit(st[l]["t"], sl, a, v)
+                done[p % 2].record(main)
+                for l in range(L):
+                    moe.moe_slot_counts_take(st[l]["use"], E, host_counts[l])
+            mc_host.copy_(mcount, non_blocking=True)
+            ev_res[p % 2].record(main)
+
+        t0 = time.perf_counter()
+        head(0)
+        tail(0)
+        for p in range(1, NP + 1):
+            if p < NP:
+                head(p)                           # queued before the host waits for p - 1
+            ev_res[(p - 1) % 2].synchronize()
+            misses += int(mc_host.sum().item())
+            if policy:
+                side.wait_event(done[(p - 1) % 2])  # spare slots are free once those commits ran
+                for l in range(L):
+                    plan = moe.moe_slot_policy_plan(st[l]["t"], host_counts[l].numpy().view(np.uint32),
+                                                    SP, w["margin"])
+                    pending[l] = plan
+                    if plan[0]:
+                        moe.moe_slot_table_stage(st[l]["t"], plan[2], plan[0],
+                                                 [src + l * E * stride + e * stride for e in plan[0]],
+                                                 stream=side)
+                        ev = torch.cuda.Event()
+                        ev.record(side)
+                        staged[l] = ev
+                        swaps += len(plan[0])
+            if p < NP:
+                tail(p)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        return dict(seconds=dt, hit_rate=1.0 - misses / (N * L * k), swaps=swaps,
+                    fill_bytes=swaps * eb)
+
+    static = run(False)
+    adaptive = run(True)
+    hh.close()
+    return w, static, adaptive
+
+
 # ----------------------------------------------------------------------------
 def cpu_baseline_decode(budget_s=15.0):
     """The fp64 oracle on single-token, single-layer decode: a bounded sample."""
@@ -549,6 +734,23 @@ def main():
         print("decode_q2s_t1: %.1f us/step, gate/up kernel %.2f us" %
               (r["seconds"] / K * 1e6, r["kernel_s"] * 1e6), file=sys.stderr, flush=True)
         del qstack
+        torch.cuda.empty_cache()
+
+    if "slot_policy_q3s_t1_8l" in wl:
+        w, st_, ad = bench_slot_policy(ctx)
+        N, L = w["stream_tokens"], w["layers"]
+        results["slot_policy_q3s_t1_8l"] = dict(
+            value=N / ad["seconds"], unit="tokens/s", steps=N, ms_per_step=ad["seconds"] / N * 1e3,
+            hit_rate=ad["hit_rate"], hit_rate_static=st_["hit_rate"],
+            static_tokens_per_s=N / st_["seconds"], swaps=ad["swaps"],
+            fill_bytes=ad["fill_bytes"],
+            config="2048 tokens x 8 chained Q3S slot layers, 128 resident + 8 spare slots, "
+                   "drifting popularity (global 0.2 + per-1024-token context 0.3, Zipf 1.2); "
+                   "policy every 32 tokens (margin 4, <= 8 swaps/layer), fills from pinned "
+                   "host memory on a side stream")
+        print("slot_policy_q3s_t1_8l: %.3f ms/token (static %.3f), hit %.3f (static %.3f), "
+              "%d swaps" % (ad["seconds"] / N * 1e3, st_["seconds"] / N * 1e3, ad["hit_rate"],
+                            st_["hit_rate"], ad["swaps"]), file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
 
     line = {

@@ -24,6 +24,8 @@ __all__ = [
     "moe_slot_table_update", "moe_route", "moe_router_logits", "moe_permute_workspace_bytes",
     "moe_permute",
     "moe_last_error", "moe_abi_version", "moe_set_kernel_timer", "moe_set_router_timer",
+    "moe_slot_counts_take", "moe_slot_policy_plan", "moe_slot_table_stage",
+    "moe_slot_table_commit",
     "LIB_PATH",
 ]
 
@@ -66,7 +68,8 @@ class MoeShape(ctypes.Structure):
 class MoeExpertTable(ctypes.Structure):
     _fields_ = [("routed", ctypes.c_void_p), ("expert_stride", ctypes.c_size_t),
                 ("slot_of", ctypes.c_void_p), ("n_slots", ctypes.c_int32),
-                ("shared", ctypes.c_void_p), ("router", ctypes.c_void_p)]
+                ("shared", ctypes.c_void_p), ("router", ctypes.c_void_p),
+                ("use_count", ctypes.c_void_p)]
 
 
 class MoeMiss(ctypes.Structure):
@@ -102,6 +105,11 @@ _sigs = {
     "moe_permute": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _Z, _P]),
     "moe_set_kernel_timer": (_I, [_P, _P]),
     "moe_set_router_timer": (_I, [_P, _P]),
+    "moe_slot_counts_take": (_I, [_P, _I, _P, _P]),
+    "moe_slot_policy_plan": (_I, [ctypes.POINTER(MoeSlotTable), _P, _I, ctypes.c_uint32, _P, _P,
+                                  _P, _P]),
+    "moe_slot_table_stage": (_I, [ctypes.POINTER(MoeSlotTable), _I, _P, _P, _P, _P]),
+    "moe_slot_table_commit": (_I, [ctypes.POINTER(MoeSlotTable), _I, _P, _P, _P, _P]),
 }
 for _name, (_res, _args) in _sigs.items():
     _f = getattr(_lib, _name)
@@ -179,6 +187,49 @@ def moe_slot_table_update(table: MoeSlotTable, slots, experts, src_ptrs, stream=
     _check(_lib.moe_slot_table_update(ctypes.byref(table), n, ctypes.cast(s_arr, _P),
                                       ctypes.cast(e_arr, _P), ctypes.cast(p_arr, _P),
                                       _stream(stream)))
+
+
+def _i32(seq):
+    n = len(seq)
+    return (ctypes.c_int32 * max(n, 1))(*seq)
+
+
+def moe_slot_table_stage(table: MoeSlotTable, slots, experts, src_ptrs, stream=None):
+    """Copy experts into empty slots without touching the maps."""
+    n = len(slots)
+    p_arr = (ctypes.c_void_p * max(n, 1))(*[_ptr(p) for p in src_ptrs])
+    _check(_lib.moe_slot_table_stage(ctypes.byref(table), n, ctypes.cast(_i32(slots), _P),
+                                     ctypes.cast(_i32(experts), _P), ctypes.cast(p_arr, _P),
+                                     _stream(stream)))
+
+
+def moe_slot_table_commit(table: MoeSlotTable, slots, experts, evict, stream=None):
+    """Install staged experts into their slots and evict `evict` (map edits only)."""
+    n = len(slots)
+    _check(_lib.moe_slot_table_commit(ctypes.byref(table), n, ctypes.cast(_i32(slots), _P),
+                                      ctypes.cast(_i32(experts), _P),
+                                      ctypes.cast(_i32(evict), _P) if evict is not None else None,
+                                      _stream(stream)))
+
+
+def moe_slot_counts_take(use_count, n, host_out, stream=None):
+    """Copy the device usage counts to host_out (address or pinned tensor), then halve them."""
+    _check(_lib.moe_slot_counts_take(_ptr(use_count), n, _ptr(host_out), _stream(stream)))
+
+
+def moe_slot_policy_plan(table: MoeSlotTable, counts, max_swaps: int, margin: int):
+    """Plan swaps from host counts (numpy uint32 [n_experts]); returns (admit, evict, slots)."""
+    import numpy as np
+    c = np.ascontiguousarray(counts, dtype=np.uint32)
+    a = (ctypes.c_int32 * max(max_swaps, 1))()
+    v = (ctypes.c_int32 * max(max_swaps, 1))()
+    sl = (ctypes.c_int32 * max(max_swaps, 1))()
+    m = ctypes.c_int32(0)
+    _check(_lib.moe_slot_policy_plan(ctypes.byref(table), c.ctypes.data, max_swaps, margin,
+                                     ctypes.cast(a, _P), ctypes.cast(v, _P), ctypes.cast(sl, _P),
+                                     ctypes.byref(m)))
+    k = m.value
+    return list(a[:k]), list(v[:k]), list(sl[:k])
 
 
 def moe_route(logits, tokens, n_experts, top_k, idx, gate, stream=None):

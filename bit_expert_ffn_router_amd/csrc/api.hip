@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "../../include/moe.h"
@@ -179,6 +180,8 @@ moe_status moe_layer_forward(const moe_shape* shape, int32_t tokens, const void*
     return fail(MOE_EINVAL, "table->shared must be 256-byte aligned");
   if (table->router && ((uintptr_t)table->router & 15u))
     return fail(MOE_EINVAL, "table->router must be 16-byte aligned");
+  if (table->use_count && ((uintptr_t)table->use_count & 3u))
+    return fail(MOE_EINVAL, "table->use_count must be 4-byte aligned");
   const bool slots = table->slot_of != nullptr;
   if (slots) {
     if (table->n_slots <= 0) return fail(MOE_EINVAL, "n_slots must be > 0 with a slot table");
@@ -218,6 +221,7 @@ moe_status moe_layer_forward(const moe_shape* shape, int32_t tokens, const void*
     a.out_bf16 = out_dtype == MOE_BF16;
     a.miss = (moe::MissRec*)miss;
     a.miss_count = miss_count;
+    a.use_count = slots ? table->use_count : nullptr;
     const moe::DecodeWs w = moe::decode_ws_carve(ws, T, a.D, a.F, a.Fs, a.E, a.k);
     if (table->router) {
       moe::RouterArgs r{T, a.D, a.E, x, a.x_bf16, a.rmsnorm, (const uint16_t*)table->router,
@@ -248,6 +252,145 @@ moe_status moe_layer_forward(const moe_shape* shape, int32_t tokens, const void*
   a.out_bf16 = out_dtype == MOE_BF16;
   a.router = (const uint16_t*)table->router;
   return hip_status(moe::launch_prefill(a, ws, (hipStream_t)stream), "prefill launch");
+}
+
+// Validation shared by stage and commit: `slots` name distinct empty slots,
+// `experts` distinct experts that are not resident.
+static moe_status check_installs(const moe_slot_table* t, int32_t n, const int32_t* slots,
+                                 const int32_t* experts, std::vector<char>& slot_named,
+                                 std::vector<char>& expert_named) {
+  if (!t) return fail(MOE_EINVAL, "table is NULL");
+  if (n < 0) return fail(MOE_EINVAL, "n %d < 0", (int)n);
+  if (!t->slot_of || !t->expert_of_slot || !t->host_slot_of || !t->host_expert_of_slot ||
+      !t->storage)
+    return fail(MOE_EINVAL, "table arrays are required");
+  if (t->n_experts <= 0 || t->n_slots <= 0) return fail(MOE_EINVAL, "n_experts and n_slots must be > 0");
+  if (n > 0 && (!slots || !experts)) return fail(MOE_EINVAL, "slots and experts are required");
+  slot_named.assign(t->n_slots, 0);
+  expert_named.assign(t->n_experts, 0);
+  for (int i = 0; i < n; ++i) {
+    const int sl = slots[i], ex = experts[i];
+    if (sl < 0 || sl >= t->n_slots) return fail(MOE_EINVAL, "slot %d out of range", sl);
+    if (ex < 0 || ex >= t->n_experts) return fail(MOE_EINVAL, "expert %d out of range", ex);
+    if (slot_named[sl]) return fail(MOE_EINVAL, "slot %d named twice", sl);
+    if (expert_named[ex]) return fail(MOE_EINVAL, "expert %d named twice", ex);
+    slot_named[sl] = 1;
+    expert_named[ex] = 1;
+    if (t->host_expert_of_slot[sl] >= 0)
+      return fail(MOE_EINVAL, "slot %d is not empty (expert %d)", sl, t->host_expert_of_slot[sl]);
+    if (t->host_slot_of[ex] >= 0)
+      return fail(MOE_EINVAL, "expert %d is already resident in slot %d", ex, t->host_slot_of[ex]);
+  }
+  return ok();
+}
+
+moe_status moe_slot_table_stage(moe_slot_table* t, int32_t n, const int32_t* slots,
+                                const int32_t* experts, const void* const* src,
+                                moe_stream_t stream) {
+  std::vector<char> sn, en;
+  moe_status s = check_installs(t, n, slots, experts, sn, en);
+  if (s != MOE_OK) return s;
+  if (n == 0) return ok();
+  if (t->stride % 256 != 0 || t->expert_bytes > t->stride || !aligned256(t->storage))
+    return fail(MOE_EINVAL, "storage must be 256-byte aligned, stride a multiple of 256 >= expert_bytes");
+  if (!src) return fail(MOE_EINVAL, "src is required");
+  for (int i = 0; i < n; ++i)
+    if (!src[i]) return fail(MOE_EINVAL, "src[%d] is NULL", i);
+  for (int i = 0; i < n; ++i) {
+    hipError_t e = hipMemcpyAsync((uint8_t*)t->storage + (size_t)slots[i] * t->stride, src[i],
+                                  t->expert_bytes, hipMemcpyDefault, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e, "slot copy");
+  }
+  return ok();
+}
+
+moe_status moe_slot_table_commit(moe_slot_table* t, int32_t n, const int32_t* slots,
+                                 const int32_t* experts, const int32_t* evict,
+                                 moe_stream_t stream) {
+  std::vector<char> sn, en;
+  moe_status s = check_installs(t, n, slots, experts, sn, en);
+  if (s != MOE_OK) return s;
+  if (n == 0) return ok();
+  std::vector<char> evicted(t->n_experts, 0);
+  if (evict) {
+    for (int i = 0; i < n; ++i) {
+      const int v = evict[i];
+      if (v < -1 || v >= t->n_experts) return fail(MOE_EINVAL, "evict %d out of range", v);
+      if (v < 0) continue;
+      if (evicted[v]) return fail(MOE_EINVAL, "expert %d evicted twice", v);
+      if (t->host_slot_of[v] < 0) return fail(MOE_EINVAL, "evicted expert %d is not resident", v);
+      evicted[v] = 1;
+    }
+  }
+  std::vector<moe::SlotEdit> edits;
+  for (int i = 0; i < n; ++i) {
+    if (evict && evict[i] >= 0) edits.push_back({t->host_slot_of[evict[i]], -1, evict[i], 0});
+    edits.push_back({slots[i], experts[i], -1, 0});
+  }
+  // Evictions and installs touch distinct slots and experts, so chunking the
+  // batch keeps the result of applying it at once.
+  for (size_t i0 = 0; i0 < edits.size(); i0 += moe::kSlotEditsPerLaunch) {
+    const int m = (int)std::min<size_t>(edits.size() - i0, moe::kSlotEditsPerLaunch);
+    hipError_t e = moe::launch_slot_edits(t->slot_of, t->expert_of_slot, edits.data() + i0, m,
+                                          (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e, "slot edit launch");
+  }
+  for (const auto& ed : edits) {
+    if (ed.old_expert >= 0) t->host_slot_of[ed.old_expert] = -1;
+    t->host_expert_of_slot[ed.slot] = ed.expert;
+    if (ed.expert >= 0) t->host_slot_of[ed.expert] = ed.slot;
+  }
+  return ok();
+}
+
+moe_status moe_slot_counts_take(uint32_t* use_count, int32_t n, uint32_t* host_out,
+                                moe_stream_t stream) {
+  if (n < 0) return fail(MOE_EINVAL, "n %d < 0", (int)n);
+  if (n == 0) return ok();
+  if (!use_count || !host_out) return fail(MOE_EINVAL, "use_count and host_out are required");
+  if ((uintptr_t)use_count & 3u) return fail(MOE_EINVAL, "use_count must be 4-byte aligned");
+  hipError_t e = hipMemcpyAsync(host_out, use_count, (size_t)n * sizeof(uint32_t),
+                                hipMemcpyDeviceToHost, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_status(e, "count copy");
+  return hip_status(moe::launch_counts_halve(use_count, n, (hipStream_t)stream), "count halve launch");
+}
+
+moe_status moe_slot_policy_plan(const moe_slot_table* t, const uint32_t* counts, int32_t max_swaps,
+                                uint32_t margin, int32_t* admit, int32_t* evict, int32_t* slots,
+                                int32_t* n_swaps) {
+  if (!t || !counts || !n_swaps) return fail(MOE_EINVAL, "table, counts and n_swaps are required");
+  if (!t->host_slot_of || !t->host_expert_of_slot) return fail(MOE_EINVAL, "host mirrors are required");
+  if (t->n_experts <= 0 || t->n_slots <= 0) return fail(MOE_EINVAL, "n_experts and n_slots must be > 0");
+  if (max_swaps < 0) return fail(MOE_EINVAL, "max_swaps %d < 0", (int)max_swaps);
+  if (max_swaps > 0 && (!admit || !evict || !slots))
+    return fail(MOE_EINVAL, "admit, evict and slots are required");
+  const int E = t->n_experts, S = t->n_slots;
+  std::vector<int32_t> cand, vict, empty;
+  for (int e = 0; e < E; ++e) {
+    if (t->host_slot_of[e] >= 0)
+      vict.push_back(e);
+    else if (counts[e] > 0)
+      cand.push_back(e);
+  }
+  for (int sl = 0; sl < S; ++sl)
+    if (t->host_expert_of_slot[sl] < 0) empty.push_back(sl);
+  std::sort(cand.begin(), cand.end(), [&](int32_t x, int32_t y) {
+    return counts[x] != counts[y] ? counts[x] > counts[y] : x < y;
+  });
+  std::sort(vict.begin(), vict.end(), [&](int32_t x, int32_t y) {
+    return counts[x] != counts[y] ? counts[x] < counts[y] : x < y;
+  });
+  const size_t lim = std::min({(size_t)max_swaps, cand.size(), vict.size(), empty.size()});
+  int32_t m = 0;
+  for (size_t i = 0; i < lim; ++i) {
+    if ((uint64_t)counts[cand[i]] <= (uint64_t)counts[vict[i]] + margin) break;
+    admit[m] = cand[i];
+    evict[m] = vict[i];
+    slots[m] = empty[i];
+    ++m;
+  }
+  *n_swaps = m;
+  return ok();
 }
 
 moe_status moe_router_logits(const moe_shape* shape, int32_t tokens, const void* x,

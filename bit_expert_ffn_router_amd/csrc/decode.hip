@@ -128,6 +128,7 @@ __device__ __forceinline__ void publish_t1(const DecodeArgs& a, const DecodeWs& 
   if (lane < k) {
     w.idx[lane] = e;
     w.gate[lane] = g;
+    if (a.use_count) atomicAdd(&a.use_count[e], 1u);
     if ((hits >> lane) & 1ull) {
       const int i = base + __popcll(hits & below);
       w.work_ref[i] = ref;
@@ -214,6 +215,7 @@ __device__ __forceinline__ void build_list(const DecodeArgs& a, const DecodeWs& 
   for (int i = lane; i < P; i += 64) {
     w.idx[i] = R.e[i];
     w.gate[i] = R.g[i];
+    if (a.use_count) atomicAdd(&a.use_count[R.e[i]], 1u);
   }
   if (lane == 0) {
     *w.nwork = nu;

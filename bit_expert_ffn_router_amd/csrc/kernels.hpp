@@ -102,6 +102,7 @@ struct DecodeArgs {
   int out_bf16;
   MissRec* miss;
   int32_t* miss_count;
+  uint32_t* use_count;  // NULL, or [E]: +1 per routed pair (slot policy statistics)
 };
 
 size_t decode_ws_bytes(int T, int D, int F, int Fs, int E, int k);
@@ -144,6 +145,7 @@ struct SlotEdit {
 constexpr int kSlotEditsPerLaunch = 32;
 hipError_t launch_slot_edits(int32_t* slot_of, int32_t* expert_of_slot, const SlotEdit* edits,
                              int n, hipStream_t st);
+hipError_t launch_counts_halve(uint32_t* counts, int n, hipStream_t st);
 hipError_t launch_slot_init(int32_t* slot_of, int E, int32_t* expert_of_slot, int S,
                             hipStream_t st);
 

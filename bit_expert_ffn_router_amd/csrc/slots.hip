@@ -25,6 +25,17 @@ __global__ void slot_edit_kernel(int32_t* slot_of, int32_t* expert_of_slot, Slot
   }
 }
 
+// Halve every usage count (the decay step of the slot policy's statistics).
+__global__ void counts_halve_kernel(uint32_t* counts, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) counts[i] >>= 1;
+}
+
+hipError_t launch_counts_halve(uint32_t* counts, int n, hipStream_t st) {
+  counts_halve_kernel<<<(n + 255) / 256, 256, 0, st>>>(counts, n);
+  return hipGetLastError();
+}
+
 __global__ void slot_init_kernel(int32_t* slot_of, int E, int32_t* expert_of_slot, int S) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < E) slot_of[i] = -1;

@@ -146,7 +146,11 @@ typedef struct {
  *                  (row e = expert e, contiguous along d_model), 16-byte
  *                  aligned, or NULL.  With it, moe_layer_forward computes the
  *                  logits itself (see moe_router_logits) and `router_logits`
- *                  becomes an output. */
+ *                  becomes an output.
+ *   use_count:     device uint32 [n_experts], 4-byte aligned, or NULL.  Used
+ *                  only with a slot table: every routed (token, rank) pair
+ *                  adds 1 to its expert's entry (hit or miss), the usage
+ *                  statistics of moe_slot_policy_plan. */
 typedef struct {
   const void* routed;
   size_t expert_stride;
@@ -154,6 +158,7 @@ typedef struct {
   int32_t n_slots;
   const void* shared;
   const void* router;
+  uint32_t* use_count;
 } moe_expert_table;
 
 /* One routed (token, rank) pair whose expert is not resident. */
@@ -284,6 +289,63 @@ moe_status moe_slot_table_update(moe_slot_table* t, int32_t n, const int32_t* sl
                                  const int32_t* experts, const void* const* src,
                                  moe_stream_t stream);
 
+/* Frequency-driven slot policy with fills that overlap the layers.  The pages
+ * swap experts while serving, moving an expert onto the GPU once it starts to
+ * be used often, and report a higher hit rate for that than for a fixed set
+ * chosen from the overall frequency curve ([AF] section "命中率七成，代价是
+ * 答案会变").  They give no algorithm; the reading implemented here:
+ *   - statistics: use_count (see moe_expert_table) counts routed pairs; each
+ *     period the caller takes a snapshot and halves the counts, so the score
+ *     of an expert is its usage with a weight of 1/2 per period of age;
+ *   - plan: the non-resident experts with a nonzero score, hottest first
+ *     (ties: lower id), are paired with the resident experts, coldest first
+ *     (ties: lower id), and with the empty slots in ascending order; pair i is
+ *     a swap while score(candidate i) > score(victim i) + margin, at most
+ *     max_swaps of them;
+ *   - fills: the admitted experts are copied into empty (spare) slots, which
+ *     no layer reads, on a side stream while later layers run; a map-only
+ *     commit on the layer stream then installs them and evicts the victims,
+ *     whose slots become the spares of the next period.
+ * A table built for this keeps n_slots = resident + spare slots. */
+
+/* Copy use_count [n] to host_out (host memory; pinned for an asynchronous
+ * copy), then halve every device count.  Both are ordered on the stream; the
+ * caller synchronises before reading host_out. */
+moe_status moe_slot_counts_take(uint32_t* use_count, int32_t n, uint32_t* host_out,
+                                moe_stream_t stream);
+
+/* Plan up to max_swaps swaps from the scores `counts` (host [n_experts]) and
+ * the table's host mirrors (rule above).  Writes admit[i] (expert to
+ * install), evict[i] (resident expert to evict) and slots[i] (empty slot for
+ * the admitted expert), i < *n_swaps.  Host only; deterministic; changes
+ * nothing in the table. */
+moe_status moe_slot_policy_plan(const moe_slot_table* t, const uint32_t* counts,
+                                int32_t max_swaps, uint32_t margin, int32_t* admit,
+                                int32_t* evict, int32_t* slots, int32_t* n_swaps);
+
+/* Copy the packed bytes of experts[i] from src[i] (device or pinned host)
+ * into slots[i], for i < n, without touching the maps: the slots must be
+ * empty (expert_of_slot == -1 in the host mirror) and stay so until the
+ * matching moe_slot_table_commit, so no layer reads them meanwhile.  The
+ * experts must be distinct and not resident, the slots distinct
+ * (MOE_EINVAL otherwise, nothing enqueued).  The caller must not stage into
+ * a slot again before committing it. */
+moe_status moe_slot_table_stage(moe_slot_table* t, int32_t n, const int32_t* slots,
+                                const int32_t* experts, const void* const* src,
+                                moe_stream_t stream);
+
+/* Map-only install of staged experts: experts[i] becomes resident in
+ * slots[i] (empty, its bytes already staged and the copy ordered before this
+ * call, e.g. by an event), and evict[i] (a resident expert, or -1; evict may
+ * be NULL) stops being resident, its slot becoming empty.  Validated as for
+ * moe_slot_table_stage, plus: each evicted expert resident and named once.
+ * The map edits are ordered on the stream; the host mirror is updated before
+ * return. */
+moe_status moe_slot_table_commit(moe_slot_table* t, int32_t n, const int32_t* slots,
+                                 const int32_t* experts, const int32_t* evict,
+                                 moe_stream_t stream);
+
+
 /* Routing alone (the first step of the layer): device fp32 logits [T][E] ->
  * device int32 idx [T][k] and fp32 gates [T][k], as defined above. */
 moe_status moe_route(const float* logits, int32_t tokens, int32_t n_experts, int32_t top_k,
@@ -320,7 +382,7 @@ moe_status moe_set_router_timer(void* before, void* after);
 const char* moe_last_error(void);
 
 /* ABI version of this header. */
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 int32_t moe_abi_version(void);
 
 #ifdef __cplusplus

@@ -275,6 +275,70 @@ def slot_layer_forward(x, logits, k: int, get_expert, shared, slot_of):
     return partial, misses, idx, gate
 
 
+def slot_policy_plan(counts, slot_of, expert_of_slot, max_swaps: int, margin: int):
+    """One planning step of the frequency-driven slot policy.
+
+    The pages move an expert onto the GPU once it starts to be used often and
+    swap experts while serving ([AF] "命中率七成，代价是答案会变"); they give
+    no algorithm.  Reading taken: rank the non-resident experts with a
+    nonzero score from hottest to coldest (ties: lower id first) and the
+    resident experts from coldest to hottest (ties: lower id first); the i-th
+    of each, with the i-th empty slot in ascending order, is a swap as long
+    as score(candidate) > score(victim) + margin, for at most max_swaps.
+    Returns (admit, evict, slots) lists.
+    """
+    E = len(slot_of)
+    cand = [e for e in range(E) if slot_of[e] < 0 and counts[e] > 0]
+    vict = [e for e in range(E) if slot_of[e] >= 0]
+    empty = [s for s in range(len(expert_of_slot)) if expert_of_slot[s] < 0]
+    cand.sort(key=lambda e: (-int(counts[e]), e))
+    vict.sort(key=lambda e: (int(counts[e]), e))
+    admit, evict, slots = [], [], []
+    for i in range(min(max_swaps, len(cand), len(vict), len(empty))):
+        if int(counts[cand[i]]) <= int(counts[vict[i]]) + margin:
+            break
+        admit.append(cand[i])
+        evict.append(vict[i])
+        slots.append(empty[i])
+    return admit, evict, slots
+
+
+def slot_policy_simulate(routed_ids, slot_of, expert_of_slot, period: int, max_swaps: int,
+                         margin: int):
+    """Run the slot policy over a stream of routed expert ids.
+
+    routed_ids: per token, the list of its routed expert ids (one per rank).
+    Schedule: every routed pair adds 1 to its expert's count; after each
+    period the counts are snapshotted and halved and a plan is made from the
+    snapshot; that plan's experts are copied while the next period runs and
+    are installed (their victims evicted) after it, so a plan made after
+    period p serves from period p + 2 on.  Returns (hits per token, plans
+    made after each period, final slot_of, final expert_of_slot).
+    """
+    slot_of = list(slot_of)
+    expert_of_slot = list(expert_of_slot)
+    counts = [0] * len(slot_of)
+    hits, plans, pending = [], [], None
+    n = len(routed_ids)
+    for p0 in range(0, n, period):
+        for ids in routed_ids[p0:p0 + period]:
+            hits.append([slot_of[e] >= 0 for e in ids])
+            for e in ids:
+                counts[e] += 1
+        if pending is not None:
+            for a, v, s in zip(*pending):
+                old = slot_of[v]
+                slot_of[v] = -1
+                expert_of_slot[old] = -1
+                slot_of[a] = s
+                expert_of_slot[s] = a
+        snap = list(counts)
+        counts = [c >> 1 for c in counts]
+        pending = slot_policy_plan(snap, slot_of, expert_of_slot, max_swaps, margin)
+        plans.append(pending)
+    return hits, plans, slot_of, expert_of_slot
+
+
 def rms_chain(y):
     """Input of the next layer from this layer's output.
 

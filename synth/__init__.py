@@ -238,6 +238,28 @@ def router_logits(seed: int, layer: int, tokens: int, n_experts: int,
     return out
 
 
+def router_logits_drifting(seed: int, layer: int, tokens: int, n_experts: int, zipf_s: float,
+                           alpha_global: float, alpha_context: float, segment: int) -> np.ndarray:
+    """fp32 router logits [tokens][n_experts] whose popular experts drift.
+
+    logits = float32(N(0,1) + alpha_global * log p_{r(e)} + alpha_context *
+    log p_{r_c(e)}): r is the layer's fixed popularity ranking (as in
+    router_logits), r_c a second ranking drawn anew for every run of
+    `segment` tokens (one "conversation"; PCG64 seeded with [seed, 3, layer]
+    and [seed + 1000 + c, 3, layer] for segment c, through
+    zipf_log_popularity).  N(0,1) from PCG64 seeded with [seed, 2, layer].
+    """
+    rng = np.random.default_rng([seed, 2, layer])
+    g = zipf_log_popularity(seed, layer, n_experts, zipf_s)
+    out = np.empty((tokens, n_experts), dtype=np.float32)
+    for s0 in range(0, tokens, segment):
+        n = min(segment, tokens - s0)
+        c = zipf_log_popularity(seed + 1000 + s0 // segment, layer, n_experts, zipf_s)
+        out[s0:s0 + n] = (rng.standard_normal((n, n_experts)) + alpha_global * g
+                          + alpha_context * c).astype(np.float32)
+    return out
+
+
 # Slot-table workload: Zipf exponent 1.2; alpha chosen (by
 # oracle/calibrate_slot_alpha.py, which prints this value) so that with the
 # 128 most popular of 512 experts resident, about 70 % of routed
@@ -267,4 +289,15 @@ WORKLOADS = {
                             d_ff_shared=512, tokens=1, layers=48, fmt=FMT_Q3S,
                             x_dtype="bf16", zipf_s=SLOT_ZIPF_S, alpha=SLOT_ALPHA,
                             min_gap=None, n_slots=128),
+    # The slot policy with fills from host memory: 8 chained layers, 128
+    # resident + 8 spare slots each, a 2048-token stream whose popular
+    # experts follow a fixed ranking (weight 0.2) and a per-1024-token
+    # "conversation" ranking (weight 0.3); plans every 32 tokens with a
+    # margin of 4 and up to 8 swaps per layer.
+    "slot_policy_q3s_t1_8l": dict(d_model=3072, d_ff=512, n_experts=512, top_k=10,
+                                  d_ff_shared=512, tokens=1, layers=8, fmt=FMT_Q3S,
+                                  x_dtype="bf16", zipf_s=SLOT_ZIPF_S, alpha=0.2,
+                                  alpha_context=0.3, segment=1024, stream_tokens=2048,
+                                  min_gap=None, n_slots=128, spare_slots=8, period=32,
+                                  margin=4),
 }

@@ -30,12 +30,13 @@ class PackedLayer:
     def __init__(self, routed, shared, stride, stride_s):
         self.routed, self.shared, self.stride, self.stride_s = routed, shared, stride, stride_s
 
-    def table(self, slot_of=None, n_slots=0, routed=None, router=None):
+    def table(self, slot_of=None, n_slots=0, routed=None, router=None, use_count=None):
         return moe.MoeExpertTable(
             (routed if routed is not None else self.routed).data_ptr(), self.stride,
             None if slot_of is None else slot_of.data_ptr(), n_slots,
             None if self.shared is None else self.shared.data_ptr(),
-            None if router is None else router.data_ptr())
+            None if router is None else router.data_ptr(),
+            None if use_count is None else use_count.data_ptr())
 
 
 def pack_experts(shape, seed, layer, expert0, n, d_ff, out, stride, device, chunk=32):

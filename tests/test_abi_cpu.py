@@ -35,7 +35,7 @@ def test_every_header_function_is_exported():
     lib = ctypes.CDLL(moe.LIB_PATH)
     for n in names:
         getattr(lib, n)
-    assert moe.moe_abi_version() == 2
+    assert moe.moe_abi_version() == 3
 
 
 def test_packed_bytes_formula():
