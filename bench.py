@@ -30,6 +30,9 @@ scale and min, or signed 3-bit blocks with an fp16 scale):
                      copies admitted experts from pinned host memory on a
                      side stream while the next period runs; the same stream
                      with the policy off is the static baseline
+  slot_host_q3s_t1_8l  8 chained Q3S slot layers (128 of 512 resident); every
+                     layer's misses are computed on the host's cores
+                     (moe_host_miss_ffn) and added into the partial output
 
 Output: one JSON line (see the end of main()).
 """
@@ -58,7 +61,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workloads",
                     default="decode_t1,mtp_verify_t4_48l,prefill_8192,slot_q3s_t1_48l,decode_q2s_t1,"
-                            "decode_router_t1,prefill_router_8192,slot_policy_q3s_t1_8l")
+                            "decode_router_t1,prefill_router_8192,slot_policy_q3s_t1_8l,"
+                            "slot_host_q3s_t1_8l")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-graph", action="store_true", help="launch steps eagerly")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -558,6 +562,97 @@ def bench_slot_policy(ctx, name="slot_policy_q3s_t1_8l"):
     return w, static, adaptive
 
 
+def bench_slot_host(ctx, n_tokens=16, name="slot_host_q3s_t1_8l"):
+    """Each token through L chained slot layers; after each layer the miss
+    list comes to the host, the host pool computes those rows and they are
+    added into the layer's output on the GPU before the next layer."""
+    torch, moe, synth, np = ctx.torch, ctx.moe, ctx.synth, ctx.np
+    w = synth.WORKLOADS[name]
+    shape = ctx.shape(w)
+    E, R, L, D, k = w["n_experts"], w["n_slots"], w["layers"], w["d_model"], w["top_k"]
+    stride = ctx.stride_of(shape, w["d_ff"])
+    st = []
+    for l in range(L):
+        full = ctx.build_layer(shape, 0, l, ctx.dev)
+        host = full.routed.cpu().numpy()                 # every routed expert in host memory
+        ranks = synth.expert_ranks(0, l, E)
+        resident = [int(e) for e in np.argsort(ranks)[:R]]
+        slot_of = torch.empty(E, dtype=torch.int32, device=ctx.dev)
+        eos = torch.empty(R, dtype=torch.int32, device=ctx.dev)
+        hs, he = np.empty(E, np.int32), np.empty(R, np.int32)
+        storage = torch.empty(R * stride, dtype=torch.uint8, device=ctx.dev)
+        t = moe.MoeSlotTable(E, R, slot_of.data_ptr(), eos.data_ptr(), hs.ctypes.data,
+                             he.ctypes.data, storage.data_ptr(), stride,
+                             moe.moe_packed_expert_bytes(shape, w["d_ff"]))
+        moe.moe_slot_table_init(t)
+        for i0 in range(0, R, 32):
+            moe.moe_slot_table_update(t, list(range(i0, i0 + 32)), resident[i0:i0 + 32],
+                                      [full.routed.data_ptr() + e * stride for e in resident[i0:i0 + 32]])
+        torch.cuda.synchronize()
+        del full.routed
+        st.append(dict(t=t, keep=(slot_of, eos, hs, he, storage, full.shared), host=host,
+                       ptrs=[host.ctypes.data + e * stride for e in range(E)],
+                       table=moe.MoeExpertTable(storage.data_ptr(), stride, slot_of.data_ptr(), R,
+                                                full.shared.data_ptr())))
+        del full
+    logits = [ctx.dev_f32(synth.router_logits(0, l, n_tokens, E, zipf_s=w["zipf_s"],
+                                              alpha=w["alpha"])) for l in range(L)]
+    x0 = synth.activations_bf16(0, 0, n_tokens, D)
+    wsb = moe.moe_workspace_bytes(shape, 1)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=ctx.dev)
+    outs = [torch.empty(D, dtype=torch.float32, device=ctx.dev) for _ in range(L)]
+    miss = torch.empty(k * 4, dtype=torch.int32, device=ctx.dev)
+    mcount = torch.zeros(1, dtype=torch.int32, device=ctx.dev)
+    miss_h = torch.empty(k * 4 + 1, dtype=torch.int32).pin_memory()
+    y_h = torch.empty(D, dtype=torch.float32).pin_memory()
+    y_d = torch.empty(D, dtype=torch.float32, device=ctx.dev)
+    xin_h = torch.empty(D, dtype=torch.float32).pin_memory()
+    x0_d = ctx.dev_u16(x0).reshape(-1)
+    threads = min(16, os.cpu_count() or 1)
+    pool = moe.HostPool(threads)
+    host_s = 0.0
+    nmiss = 0
+
+    def token(i):
+        nonlocal host_s, nmiss
+        for l in range(L):
+            fl = 0 if l == 0 else moe.MOE_FLAG_RMSNORM_INPUT
+            x = x0_d[i * D:(i + 1) * D] if l == 0 else outs[l - 1]
+            xdt = moe.MOE_BF16 if l == 0 else moe.MOE_F32
+            moe.moe_layer_forward(shape, 1, x, xdt, fl, logits[l].data_ptr() + 4 * i * E,
+                                  st[l]["table"], outs[l], moe.MOE_F32, miss, k, mcount, ws, wsb)
+            miss_h[: 4 * k].copy_(miss, non_blocking=True)
+            miss_h[4 * k:].copy_(mcount, non_blocking=True)
+            if l > 0:
+                xin_h.copy_(outs[l - 1], non_blocking=True)   # the layer input, for the host rows
+            torch.cuda.current_stream().synchronize()
+            nm = int(miss_h[4 * k].item())
+            nmiss += nm
+            h0 = time.perf_counter()
+            if l == 0:
+                xp, xd = x0[i].ctypes.data, moe.MOE_BF16
+            else:
+                xp, xd = xin_h.data_ptr(), moe.MOE_F32
+            moe.moe_host_miss_ffn(shape, 1, xp, xd, fl, miss_h.data_ptr(), nm, st[l]["ptrs"],
+                                  y_h.data_ptr(), pool)
+            host_s += time.perf_counter() - h0
+            y_d.copy_(y_h, non_blocking=True)
+            moe.moe_add_rows(outs[l], moe.MOE_F32, y_d, 1, D)
+
+    token(0)
+    torch.cuda.synchronize()
+    host_s, nmiss = 0.0, 0
+    t0 = time.perf_counter()
+    for i in range(1, n_tokens):
+        token(i)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    pool.close()
+    n = n_tokens - 1
+    return dict(tokens=n, seconds=dt, host_s=host_s, misses_per_layer=nmiss / (n * L),
+                hit_rate=1.0 - nmiss / (n * L * k), threads=threads, layers=L)
+
+
 # ----------------------------------------------------------------------------
 def cpu_baseline_decode(budget_s=15.0):
     """The fp64 oracle on single-token, single-layer decode: a bounded sample."""
@@ -751,6 +846,22 @@ def main():
         print("slot_policy_q3s_t1_8l: %.3f ms/token (static %.3f), hit %.3f (static %.3f), "
               "%d swaps" % (ad["seconds"] / N * 1e3, st_["seconds"] / N * 1e3, ad["hit_rate"],
                             st_["hit_rate"], ad["swaps"]), file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+
+    if "slot_host_q3s_t1_8l" in wl:
+        r = bench_slot_host(ctx)
+        n, L = r["tokens"], r["layers"]
+        results["slot_host_q3s_t1_8l"] = dict(
+            value=n / r["seconds"], unit="tokens/s", steps=n, ms_per_step=r["seconds"] / n * 1e3,
+            host_ms_per_layer=r["host_s"] / (n * L) * 1e3,
+            layer_ms=r["seconds"] / (n * L) * 1e3, misses_per_layer=r["misses_per_layer"],
+            hit_rate=r["hit_rate"], host_threads=r["threads"],
+            config="1 token x 8 chained Q3S slot layers, 128/512 resident (Zipf 1.2, alpha "
+                   "0.331); misses computed on the host (fp32, %d threads) and added into "
+                   "each layer's output" % r["threads"])
+        print("slot_host_q3s_t1_8l: %.2f ms/token, host %.3f ms/layer, %.2f misses/layer" %
+              (r["seconds"] / n * 1e3, r["host_s"] / (n * L) * 1e3, r["misses_per_layer"]),
+              file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
 
     line = {

@@ -25,7 +25,7 @@ __all__ = [
     "moe_permute",
     "moe_last_error", "moe_abi_version", "moe_set_kernel_timer", "moe_set_router_timer",
     "moe_slot_counts_take", "moe_slot_policy_plan", "moe_slot_table_stage",
-    "moe_slot_table_commit",
+    "moe_slot_table_commit", "HostPool", "moe_host_miss_ffn", "moe_add_rows",
     "LIB_PATH",
 ]
 
@@ -110,6 +110,11 @@ _sigs = {
                                   _P, _P]),
     "moe_slot_table_stage": (_I, [ctypes.POINTER(MoeSlotTable), _I, _P, _P, _P, _P]),
     "moe_slot_table_commit": (_I, [ctypes.POINTER(MoeSlotTable), _I, _P, _P, _P, _P]),
+    "moe_host_pool_create": (_I, [_I, ctypes.POINTER(_P)]),
+    "moe_host_pool_destroy": (None, [_P]),
+    "moe_host_miss_ffn": (_I, [ctypes.POINTER(MoeShape), _I, _P, _I, ctypes.c_uint32, _P, _I, _P,
+                               _P, _P]),
+    "moe_add_rows": (_I, [_P, _I, _P, _I, _I, _P]),
 }
 for _name, (_res, _args) in _sigs.items():
     _f = getattr(_lib, _name)
@@ -230,6 +235,36 @@ def moe_slot_policy_plan(table: MoeSlotTable, counts, max_swaps: int, margin: in
                                      ctypes.byref(m)))
     k = m.value
     return list(a[:k]), list(v[:k]), list(sl[:k])
+
+
+class HostPool:
+    """Caller-owned worker threads for moe_host_miss_ffn (n_threads includes the caller)."""
+
+    def __init__(self, n_threads: int):
+        self.h = ctypes.c_void_p()
+        _check(_lib.moe_host_pool_create(n_threads, ctypes.byref(self.h)))
+
+    def close(self):
+        if self.h:
+            _lib.moe_host_pool_destroy(self.h)
+            self.h = ctypes.c_void_p()
+
+    def __del__(self):
+        self.close()
+
+
+def moe_host_miss_ffn(shape, tokens, x_host, x_dtype, flags, misses, n_miss, expert_ptrs, y_host,
+                      pool=None):
+    """misses: address of n_miss moe_miss records (host); expert_ptrs: sequence of host
+    addresses (0/None for experts never missed); x_host, y_host: host addresses."""
+    arr = (ctypes.c_void_p * max(len(expert_ptrs), 1))(*[p or None for p in expert_ptrs])
+    _check(_lib.moe_host_miss_ffn(ctypes.byref(shape), tokens, x_host, x_dtype, flags, misses,
+                                  n_miss, ctypes.cast(arr, _P), y_host,
+                                  pool.h if pool is not None else None))
+
+
+def moe_add_rows(out, out_dtype, y, tokens, d_model, stream=None):
+    _check(_lib.moe_add_rows(_ptr(out), out_dtype, _ptr(y), tokens, d_model, _stream(stream)))
 
 
 def moe_route(logits, tokens, n_experts, top_k, idx, gate, stream=None):

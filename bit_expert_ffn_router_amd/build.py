@@ -27,7 +27,8 @@ HIPCC_FLAGS = [
 LIBS = {
     os.path.join(HERE, "libmoe.so"): [
         os.path.join(HERE, "csrc", f) for f in
-        ("api.hip", "pack.hip", "route.hip", "router.hip", "decode.hip", "prefill.hip", "slots.hip")
+        ("api.hip", "pack.hip", "route.hip", "router.hip", "decode.hip", "prefill.hip", "slots.hip",
+         "host_ffn.hip")
     ],
     os.path.join(ROOT, "synth", "libmoe_synth.so"): [
         os.path.join(ROOT, "synth", "csrc", "synth_fill.hip"),

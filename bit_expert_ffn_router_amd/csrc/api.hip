@@ -393,6 +393,68 @@ moe_status moe_slot_policy_plan(const moe_slot_table* t, const uint32_t* counts,
   return ok();
 }
 
+moe_status moe_host_pool_create(int32_t n_threads, moe_host_pool** pool) {
+  if (!pool) return fail(MOE_EINVAL, "pool is NULL");
+  if (n_threads < 1 || n_threads > 1024) return fail(MOE_EINVAL, "n_threads %d not in 1..1024", (int)n_threads);
+  try {
+    *pool = moe_host_pool_new(n_threads);
+  } catch (...) {
+    *pool = nullptr;
+    return fail(MOE_EINVAL, "could not start %d threads", (int)n_threads);
+  }
+  return ok();
+}
+
+void moe_host_pool_destroy(moe_host_pool* pool) {
+  if (pool) moe_host_pool_delete(pool);
+}
+
+moe_status moe_host_miss_ffn(const moe_shape* shape, int32_t tokens, const void* x, int32_t x_dtype,
+                             uint32_t flags, const moe_miss* misses, int32_t n_miss,
+                             const void* const* experts, float* y, moe_host_pool* pool) {
+  moe_status s = check_shape(shape);
+  if (s != MOE_OK) return s;
+  if (tokens < 0 || n_miss < 0) return fail(MOE_EINVAL, "tokens and n_miss must be >= 0");
+  if (x_dtype != MOE_BF16 && x_dtype != MOE_F32) return fail(MOE_EINVAL, "bad x_dtype %d", (int)x_dtype);
+  if (flags & ~(uint32_t)MOE_FLAG_RMSNORM_INPUT) return fail(MOE_EINVAL, "unknown flags 0x%x", flags);
+  if (tokens == 0) return ok();
+  if (!x || !y) return fail(MOE_EINVAL, "x and y are required");
+  if (n_miss > 0 && (!misses || !experts)) return fail(MOE_EINVAL, "misses and experts are required");
+  for (int i = 0; i < n_miss; ++i) {
+    const moe_miss& m = misses[i];
+    if (m.token < 0 || m.token >= tokens) return fail(MOE_EINVAL, "miss %d: token %d out of range", i, m.token);
+    if (m.expert < 0 || m.expert >= shape->n_experts)
+      return fail(MOE_EINVAL, "miss %d: expert %d out of range", i, m.expert);
+    if (!experts[m.expert]) return fail(MOE_EINVAL, "miss %d: experts[%d] is NULL", i, m.expert);
+    if (i > 0 && (m.token < misses[i - 1].token ||
+                  (m.token == misses[i - 1].token && m.rank <= misses[i - 1].rank)))
+      return fail(MOE_EINVAL, "misses must be in (token, rank) order");
+  }
+  try {
+    std::vector<float> xhat((size_t)tokens * shape->d_model);
+    moe::host_prepare_x(tokens, shape->d_model, x, x_dtype == MOE_BF16,
+                        (flags & MOE_FLAG_RMSNORM_INPUT) != 0, xhat.data());
+    moe::host_miss_ffn(shape->d_model, shape->d_ff, shape->qfmt, tokens, xhat.data(),
+                       reinterpret_cast<const moe::MissRec*>(misses), n_miss,
+                       reinterpret_cast<const uint8_t* const*>(experts), y, pool);
+  } catch (...) {
+    return fail(MOE_EINVAL, "host miss path: out of host memory");
+  }
+  return ok();
+}
+
+moe_status moe_add_rows(void* out, int32_t out_dtype, const float* y, int32_t tokens,
+                        int32_t d_model, moe_stream_t stream) {
+  if (out_dtype != MOE_BF16 && out_dtype != MOE_F32) return fail(MOE_EINVAL, "bad out_dtype %d", (int)out_dtype);
+  if (tokens < 0 || d_model < 0) return fail(MOE_EINVAL, "tokens and d_model must be >= 0");
+  if ((size_t)tokens * d_model == 0) return ok();
+  if (!out || !y) return fail(MOE_EINVAL, "out and y are required");
+  if (((uintptr_t)out & 3u) || ((uintptr_t)y & 3u)) return fail(MOE_EINVAL, "out and y must be 4-byte aligned");
+  return hip_status(moe::launch_add_rows(out, out_dtype == MOE_BF16, y, (size_t)tokens * d_model,
+                                         (hipStream_t)stream),
+                    "add launch");
+}
+
 moe_status moe_router_logits(const moe_shape* shape, int32_t tokens, const void* x,
                              int32_t x_dtype, uint32_t flags, const void* w_router, float* logits,
                              moe_stream_t stream) {

@@ -1,0 +1,320 @@
+// Host half of the slot-mode layer: the FFNs of the non-resident pairs,
+// computed on the CPU from packed experts kept in host memory, and the GPU
+// kernel that adds them into the partial output.
+//
+// The pages keep the hot experts on the GPU and let the CPU compute the
+// experts that are not there, both sides working at the same time and their
+// results added into the same layer ([AF] "个人开发者用 AI 十天写出 Strata
+// 引擎…", section "命中率七成，代价是答案会变"; [SL] section "12GB 显存装
+// 下 1250 亿参数").  Nothing here stands in for the GPU path: it runs only
+// for the miss list a slot-mode layer returns.
+//
+// The packed record layout is the one include/moe.h specifies; this file
+// reads it with its own host code.  Arithmetic: exact fp32 weights (an fp16
+// scale times a small integer, plus an fp16 min), fp32 activations, fp32
+// accumulation, fp32 h and output.
+#include <atomic>
+#include <condition_variable>
+#include <functional>
+#include <mutex>
+#include <thread>
+#include <vector>
+
+#include "kernels.hpp"
+
+// ---------------------------------------------------------------------------
+// Thread pool (caller-owned; see moe_host_pool_create).
+struct moe_host_pool {
+  std::vector<std::thread> threads;
+  std::mutex mu;
+  std::condition_variable cv_work, cv_done;
+  std::function<void(int)> job;
+  int n_items = 0;
+  std::atomic<int> next{0};
+  int busy = 0;
+  uint64_t gen = 0;
+  bool stop = false;
+
+  void drain() {
+    for (int i = next.fetch_add(1); i < n_items; i = next.fetch_add(1)) job(i);
+  }
+  void worker() {
+    uint64_t seen = 0;
+    for (;;) {
+      {
+        std::unique_lock<std::mutex> lk(mu);
+        cv_work.wait(lk, [&] { return stop || gen != seen; });
+        if (stop) return;
+        seen = gen;
+      }
+      drain();
+      {
+        std::lock_guard<std::mutex> lk(mu);
+        if (--busy == 0) cv_done.notify_all();
+      }
+    }
+  }
+  // Items 0..n-1 of fn over the workers and the calling thread; returns when
+  // all are done.  Items must write disjoint outputs.
+  void run(int n, std::function<void(int)> fn) {
+    if (threads.empty()) {
+      for (int i = 0; i < n; ++i) fn(i);
+      return;
+    }
+    {
+      std::lock_guard<std::mutex> lk(mu);
+      job = std::move(fn);
+      n_items = n;
+      next.store(0);
+      busy = (int)threads.size();
+      ++gen;
+    }
+    cv_work.notify_all();
+    drain();
+    std::unique_lock<std::mutex> lk(mu);
+    cv_done.wait(lk, [&] { return busy == 0; });
+  }
+};
+
+namespace moe {
+namespace {
+
+float half_to_float(uint16_t h) {
+  const uint32_t s = (uint32_t)(h >> 15) << 31, e = (h >> 10) & 31u, m = h & 1023u;
+  uint32_t bits;
+  if (e == 0) {
+    if (m == 0) {
+      bits = s;
+    } else {  // subnormal: m * 2^-24, exact in fp32
+      float v = (float)m * 5.9604644775390625e-08f;
+      bits = s | (__builtin_bit_cast(uint32_t, v) & 0x7FFFFFFFu);
+    }
+  } else if (e == 31) {
+    bits = s | 0x7F800000u | (m << 13);
+  } else {
+    bits = s | ((e + 112u) << 23) | (m << 13);
+  }
+  return __builtin_bit_cast(float, bits);
+}
+float bf16_bits_to_float(uint16_t v) { return __builtin_bit_cast(float, (uint32_t)v << 16); }
+uint16_t float_to_bf16_bits(float f) {
+  uint32_t b = __builtin_bit_cast(uint32_t, f);
+  b += 0x7FFFu + ((b >> 16) & 1u);
+  return (uint16_t)(b >> 16);
+}
+
+// The packed row layout, read without unpacking weight by weight: for row n
+// of a record, block b and column quarter q, the eight columns
+// 32 b + 8 q + 0..7 have their codes in one 32-bit word (lane 16 q + n, word
+// b / 2): column 32 b + 8 q + 2 j in bits 8 (b % 2) + 2 j of the low half,
+// column 32 b + 8 q + 2 j + 1 in the same bits of the high half.  So the
+// byte (W >> 8 (b % 2)) holds the even columns' codes and (W >> (16 +
+// 8 (b % 2))) the odd ones'; a 256-entry table turns a byte into its four
+// codes.  Q3S's third bit sits in the high-plane word at bit 2 j + extra of
+// the same bytes (mask 0x55 after the shift).
+struct CodeTables {
+  float code[256][4];  // (v >> 2 j) & 3
+  float bit[256][4];   // (v >> 2 j) & 1
+  CodeTables() {
+    for (int v = 0; v < 256; ++v)
+      for (int j = 0; j < 4; ++j) {
+        code[v][j] = (float)((v >> (2 * j)) & 3);
+        bit[v][j] = (float)((v >> (2 * j)) & 1);
+      }
+  }
+};
+const CodeTables& tables() {
+  static const CodeTables t;
+  return t;
+}
+
+// A vector of length K (a multiple of 256 after padding) in record order:
+// per octet o, block b, quarter q: the 4 even then the 4 odd columns of
+// 256 o + 32 b + 8 q; plus the sum of each 32-block.
+struct RecVec {
+  std::vector<float> v;    // [oK][8][4][8]
+  std::vector<float> sum;  // [oK][8]
+  void set(const float* x, int K) {
+    const int oK = (K + 255) / 256;
+    v.assign((size_t)oK * 256, 0.f);
+    sum.assign((size_t)oK * 8, 0.f);
+    for (int o = 0; o < oK; ++o)
+      for (int b = 0; b < 8; ++b) {
+        float bs = 0.f;
+        for (int q = 0; q < 4; ++q) {
+          const int c = 256 * o + 32 * b + 8 * q;
+          float* d = &v[(size_t)o * 256 + 32 * b + 8 * q];
+          for (int j = 0; j < 4; ++j) {
+            d[j] = c + 2 * j < K ? x[c + 2 * j] : 0.f;
+            d[4 + j] = c + 2 * j + 1 < K ? x[c + 2 * j + 1] : 0.f;
+          }
+          for (int j = 0; j < 8; ++j) bs += d[j];
+        }
+        sum[(size_t)o * 8 + b] = bs;
+      }
+  }
+};
+
+// Four floats as one SSE2 register (every x86-64 CPU has it); the sums stay
+// vectors until the end of a block.
+typedef float v4f __attribute__((vector_size(16)));
+inline v4f ld4(const float* p) {
+  v4f v;
+  __builtin_memcpy(&v, p, sizeof v);
+  return v;
+}
+inline float hsum(v4f v) { return (v[0] + v[1]) + (v[2] + v[3]); }
+
+// Row n of one record dotted with octet o of a record-order vector.
+float record_row_dot(const uint8_t* rec, int fmt, int n, const float* xv, const float* xs) {
+  const CodeTables& T = tables();
+  const uint32_t* lo = reinterpret_cast<const uint32_t*>(rec);           // word (L, w): 4 L + w
+  const uint32_t* hi = reinterpret_cast<const uint32_t*>(rec + 1024);    // Q3S: (L, h): 2 L + h
+  float s = 0.f;
+  for (int b = 0; b < 8; ++b) {
+    const int wd = b / 2, sh = 8 * (b % 2);
+    const int extra = (wd % 2 == 0) ? 1 : 0;
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < 4; ++q) {
+      const int L = 16 * q + n;
+      const uint32_t W = lo[4 * L + wd];
+      const float* xe = xv + 32 * b + 8 * q;
+      v4f ce = ld4(T.code[(W >> sh) & 255u]), co = ld4(T.code[(W >> (16 + sh)) & 255u]);
+      if (fmt == kQ3) {  // u3 = u + 4 * (third bit)
+        const uint32_t H = hi[2 * L + wd / 2];
+        ce += 4.f * ld4(T.bit[(H >> (sh + extra)) & 0x55u]);
+        co += 4.f * ld4(T.bit[(H >> (16 + sh + extra)) & 0x55u]);
+      }
+      acc += ce * ld4(xe) + co * ld4(xe + 4);
+    }
+    float sc, off;
+    if (fmt == kQ2) {
+      const uint16_t* pp = reinterpret_cast<const uint16_t*>(rec + 1024 + 4 * (8 * n + b));
+      sc = half_to_float(pp[0]);
+      off = half_to_float(pp[1]);  // w = s u + m
+    } else {
+      const int base = fmt == kQ3 ? 1536 : 1024;
+      sc = half_to_float(*reinterpret_cast<const uint16_t*>(rec + base + 2 * (8 * n + b)));
+      off = -(fmt == kQ3 ? 4.f : 2.f) * sc;  // w = s (u - 4) or s (u - 2)
+    }
+    s += sc * hsum(acc) + off * xs[b];
+  }
+  return s;
+}
+
+// Row `row` of a matrix stored from `base` as 16-row groups of octet records
+// (reduction length K), dotted with the record-order vector v.
+float matrix_row_dot(const uint8_t* base, int fmt, int row, int K, const RecVec& v) {
+  const int oK = (K + 255) / 256, rb = rec_bytes(fmt);
+  const uint8_t* grp = base + (size_t)(row / 16) * oK * rb;
+  float s = 0.f;
+  for (int o = 0; o < oK; ++o)
+    s += record_row_dot(grp + (size_t)o * rb, fmt, row % 16, &v.v[(size_t)o * 256], &v.sum[(size_t)o * 8]);
+  return s;
+}
+
+}  // namespace
+
+hipError_t launch_add_rows(void* out, int out_bf16, const float* y, size_t n, hipStream_t st);
+
+}  // namespace moe
+
+namespace {
+
+__global__ void add_rows_kernel(void* out, int out_bf16, const float* __restrict__ y, size_t n) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  if (out_bf16) {
+    uint16_t* o = reinterpret_cast<uint16_t*>(out);
+    o[i] = moe::f32_to_bf16(moe::bf16_to_f32(o[i]) + y[i]);
+  } else {
+    reinterpret_cast<float*>(out)[i] += y[i];
+  }
+}
+
+}  // namespace
+
+namespace moe {
+
+hipError_t launch_add_rows(void* out, int out_bf16, const float* y, size_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  add_rows_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(out, out_bf16, y, n);
+  return hipGetLastError();
+}
+
+// y[t] = sum over the misses of token t, in list order, of gate * FFN_e(xhat_t).
+void host_miss_ffn(int D, int F, int fmt, int T, const float* xhat, const MissRec* miss, int nm,
+                   const uint8_t* const* experts, float* y, moe_host_pool* pool) {
+  const int ng = F / 16, oD = D / 256, rb = rec_bytes(fmt);
+  std::vector<RecVec> xr(T);
+  for (int t = 0; t < T; ++t) xr[t].set(xhat + (size_t)t * D, D);
+  std::vector<float> h((size_t)nm * F, 0.f);
+  // Phase 1: h rows, one item per (miss, 16-row group).
+  auto gateup = [&](int it) {
+    const int m = it / ng, g = it % ng;
+    const uint8_t* ex = experts[miss[m].expert];
+    const RecVec& x = xr[miss[m].token];
+    const uint8_t* gate = ex + (size_t)(2 * g) * oD * rb;
+    const uint8_t* up = ex + (size_t)(2 * g + 1) * oD * rb;
+    for (int n = 0; n < 16; ++n) {
+      float a = 0.f, b = 0.f;
+      for (int o = 0; o < oD; ++o) {
+        a += record_row_dot(gate + (size_t)o * rb, fmt, n, &x.v[(size_t)o * 256], &x.sum[(size_t)o * 8]);
+        b += record_row_dot(up + (size_t)o * rb, fmt, n, &x.v[(size_t)o * 256], &x.sum[(size_t)o * 8]);
+      }
+      h[(size_t)m * F + 16 * g + n] = a / (1.0f + expf(-a)) * b;
+    }
+  };
+  if (pool) pool->run(nm * ng, gateup);
+  else for (int i = 0; i < nm * ng; ++i) gateup(i);
+  std::vector<RecVec> hr(nm);
+  for (int m = 0; m < nm; ++m) hr[m].set(&h[(size_t)m * F], F);
+  // Phase 2: output rows, one item per 16-row group of d_model; each y[t][d]
+  // sums its token's misses in list order.
+  for (size_t i = 0; i < (size_t)T * D; ++i) y[i] = 0.f;
+  auto down = [&](int rg) {
+    for (int m = 0; m < nm; ++m) {
+      const uint8_t* dn = experts[miss[m].expert] + down_offset(D, F, fmt);
+      float* yt = y + (size_t)miss[m].token * D;
+      for (int r = 16 * rg; r < 16 * rg + 16; ++r)
+        yt[r] += miss[m].gate * matrix_row_dot(dn, fmt, r, F, hr[m]);
+    }
+  };
+  if (pool) pool->run(D / 16, down);
+  else for (int i = 0; i < D / 16; ++i) down(i);
+}
+
+void host_prepare_x(int T, int D, const void* x, bool x_bf16, bool rms, float* out) {
+  for (int t = 0; t < T; ++t) {
+    const size_t base = (size_t)t * D;
+    auto val = [&](int i) {
+      return x_bf16 ? bf16_bits_to_float(((const uint16_t*)x)[base + i]) : ((const float*)x)[base + i];
+    };
+    float r = 1.f;
+    if (rms) {
+      double ss = 0.0;  // the host's own mean square; the GPU sums in another order
+      for (int i = 0; i < D; ++i) ss += (double)val(i) * val(i);
+      r = 1.0f / sqrtf((float)(ss / D) + 1e-6f);
+    }
+    for (int i = 0; i < D; ++i)
+      out[base + i] = rms ? bf16_bits_to_float(float_to_bf16_bits(val(i) * r)) : val(i);
+  }
+}
+
+}  // namespace moe
+
+moe_host_pool* moe_host_pool_new(int n_threads) {
+  moe_host_pool* p = new moe_host_pool;
+  for (int i = 0; i + 1 < n_threads; ++i) p->threads.emplace_back([p] { p->worker(); });
+  return p;
+}
+
+void moe_host_pool_delete(moe_host_pool* p) {
+  {
+    std::lock_guard<std::mutex> lk(p->mu);
+    p->stop = true;
+  }
+  p->cv_work.notify_all();
+  for (auto& t : p->threads) t.join();
+  delete p;
+}

@@ -109,6 +109,17 @@ size_t decode_ws_bytes(int T, int D, int F, int Fs, int E, int k);
 DecodeWs decode_ws_carve(void* ws, int T, int D, int F, int Fs, int E, int k);
 hipError_t launch_decode(const DecodeArgs& a, const DecodeWs& w, hipStream_t st);
 
+// ---------------------------------------------------------------- host miss path
+}  // namespace moe
+struct moe_host_pool;
+moe_host_pool* moe_host_pool_new(int n_threads);
+void moe_host_pool_delete(moe_host_pool* p);
+namespace moe {
+void host_prepare_x(int T, int D, const void* x, bool x_bf16, bool rms, float* out);
+void host_miss_ffn(int D, int F, int fmt, int T, const float* xhat, const MissRec* miss, int nm,
+                   const uint8_t* const* experts, float* y, moe_host_pool* pool);
+hipError_t launch_add_rows(void* out, int out_bf16, const float* y, size_t n, hipStream_t st);
+
 // ---------------------------------------------------------------- router projection
 struct RouterArgs {
   int T, D, E;

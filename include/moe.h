@@ -236,6 +236,47 @@ moe_status moe_layer_forward(const moe_shape* shape, int32_t tokens,
                              moe_miss* miss, int32_t miss_cap, int32_t* miss_count,
                              void* ws, size_t ws_bytes, moe_stream_t stream);
 
+/* Host half of the slot-mode layer.  The pages compute the experts that are
+ * not on the GPU with the CPU, at the same time as the GPU computes its own,
+ * and add both into the same layer ([AF] section "命中率七成，代价是答案会
+ * 变"; [SL] section "12GB 显存装下 1250 亿参数").  These run only for the
+ * miss list of a slot-mode moe_layer_forward call; no GPU step falls back to
+ * them. */
+
+/* Opaque pool of worker threads for moe_host_miss_ffn, owned by the caller
+ * (n_threads counts the calling thread: n_threads - 1 workers are started).
+ * Destroy joins the workers. */
+typedef struct moe_host_pool moe_host_pool;
+moe_status moe_host_pool_create(int32_t n_threads, moe_host_pool** pool);
+void moe_host_pool_destroy(moe_host_pool* pool);
+
+/* y[t] = sum over the misses of token t, in list order, of
+ * gate * FFN_expert(xhat_t), for t < tokens (rows without misses are zero).
+ *   x:        host [tokens][d_model], x_dtype MOE_BF16 or MOE_F32; flags as
+ *             for moe_layer_forward (xhat = x, or the RMS rule computed on the
+ *             host: an fp64 mean square, so a bf16 value may differ by one
+ *             unit from the GPU's in rare ties).
+ *   misses:   host, n_miss entries in (token, rank) order, as a slot-mode
+ *             layer returns them (gates are the full top-k gates).
+ *   experts:  host [n_experts] pointers to packed experts (the layout above,
+ *             shape->qfmt) in host memory; the entry of every missed expert
+ *             must be non-NULL.
+ *   y:        host fp32 [tokens][d_model], written in full.
+ *   pool:     worker threads, or NULL for the calling thread alone.
+ * fp32 throughout (weights exact in fp32).  Deterministic: each output
+ * element is summed by one thread in a fixed order, whatever the pool size.
+ * Synchronous; touches no GPU state. */
+moe_status moe_host_miss_ffn(const moe_shape* shape, int32_t tokens, const void* x,
+                             int32_t x_dtype, uint32_t flags, const moe_miss* misses,
+                             int32_t n_miss, const void* const* experts, float* y,
+                             moe_host_pool* pool);
+
+/* out[i] += y[i] for i < tokens * d_model on the stream (out bf16, rounded
+ * to nearest even after the add, or fp32; y device fp32): completes a
+ * slot-mode layer output once the host's miss rows are on the device. */
+moe_status moe_add_rows(void* out, int32_t out_dtype, const float* y, int32_t tokens,
+                        int32_t d_model, moe_stream_t stream);
+
 /* Router projection (the router the pages keep resident on the GPU, [AF]
  * section "命中率七成，代价是答案会变"; they give no formula; reading taken:
  * an unquantised bf16 linear map without bias):

@@ -289,6 +289,13 @@ WORKLOADS = {
                             d_ff_shared=512, tokens=1, layers=48, fmt=FMT_Q3S,
                             x_dtype="bf16", zipf_s=SLOT_ZIPF_S, alpha=SLOT_ALPHA,
                             min_gap=None, n_slots=128),
+    # The slot layer completed on the host: 8 chained layers with 128 of 512
+    # experts resident (the most popular), each miss list computed by the
+    # CPU and added into the partial before the next layer.
+    "slot_host_q3s_t1_8l": dict(d_model=3072, d_ff=512, n_experts=512, top_k=10,
+                                d_ff_shared=512, tokens=1, layers=8, fmt=FMT_Q3S,
+                                x_dtype="bf16", zipf_s=SLOT_ZIPF_S, alpha=SLOT_ALPHA,
+                                min_gap=None, n_slots=128),
     # The slot policy with fills from host memory: 8 chained layers, 128
     # resident + 8 spare slots each, a 2048-token stream whose popular
     # experts follow a fixed ranking (weight 0.2) and a per-1024-token

@@ -186,3 +186,35 @@ def test_router_argument_checks():
         moe.moe_layer_forward(sh, 2, 0x1000, moe.MOE_BF16, 0, 0x1000, t, 0x1000, moe.MOE_BF16,
                               None, 0, None, 0x100000, 1 << 30, S)
     assert ei.value.status == moe.MOE_EINVAL and "router" in moe.moe_last_error()
+
+
+def test_host_miss_path_argument_checks():
+    import ctypes
+    sh = shape(d_model=256, d_ff=64)
+    x = np.zeros((2, 256), np.float32)
+    y = np.zeros((2, 256), np.float32)
+    mis = np.array([1, 0, 3, 0], np.int32)                       # token 1, rank 0, expert 3
+    ptrs = [0] * 16
+    with pytest.raises(moe.MoeError) as ei:                       # expert 3 has no bytes
+        moe.moe_host_miss_ffn(sh, 2, x.ctypes.data, moe.MOE_F32, 0, mis.ctypes.data, 1, ptrs,
+                              y.ctypes.data)
+    assert ei.value.status == moe.MOE_EINVAL
+    bad = np.array([2, 0, 3, 0], np.int32)                       # token out of range
+    with pytest.raises(moe.MoeError):
+        moe.moe_host_miss_ffn(sh, 2, x.ctypes.data, moe.MOE_F32, 0, bad.ctypes.data, 1,
+                              [1] * 16, y.ctypes.data)
+    order = np.array([1, 0, 3, 0, 0, 1, 2, 0], np.int32)          # not in (token, rank) order
+    with pytest.raises(moe.MoeError):
+        moe.moe_host_miss_ffn(sh, 2, x.ctypes.data, moe.MOE_F32, 0, order.ctypes.data, 2,
+                              [1] * 16, y.ctypes.data)
+    # no misses: y is written as zeros, no pool needed
+    y[:] = 7.0
+    moe.moe_host_miss_ffn(sh, 2, x.ctypes.data, moe.MOE_F32, 0, None, 0, [], y.ctypes.data)
+    assert not y.any()
+    pool = moe.HostPool(4)
+    pool.close()
+    with pytest.raises(moe.MoeError):
+        moe.HostPool(0)
+    with pytest.raises(moe.MoeError):
+        moe.moe_add_rows(0x1002, moe.MOE_F32, 0x2000, 1, 8, S)
+    del ctypes
