@@ -15,17 +15,18 @@
 // 0, when there is one), then the distinct resident routed experts in order
 // of first occurrence over (token, rank).
 //
-// Two launches:
+// Two launches (three with 2..4 tokens):
+//   decode_list:    2..4 tokens only, one block: wave t routes token t, wave
+//                   0 builds and publishes the list and the miss list.
 //   decode_gateup:  blocks [0, d_ff_shared/16) compute 16 FFN rows of the
 //                   shared expert each and stream its weights at once.  The
-//                   other blocks are (routed list entry, 16 FFN rows); they
-//                   route the tokens themselves first.  With one token every
-//                   wave routes it, so each wave knows its expert without
-//                   waiting for another; with 2..4 tokens wave t routes token
-//                   t and wave 0 builds the list and the miss list.  The
-//                   first routed block publishes the list for the second
-//                   kernel.  Then: dequantising MFMA GEMV of W_gate and W_up,
-//                   SwiGLU, h in bf16 hi + lo with per-block sums.
+//                   other blocks are (routed list entry, 16 FFN rows).  With
+//                   one token they route it themselves first (every wave, so
+//                   each wave knows its expert without waiting for another;
+//                   the first routed block publishes the list for the down
+//                   kernel); with 2..4 tokens they read their entry of the
+//                   published list.  Then: dequantising MFMA GEMV of W_gate
+//                   and W_up, SwiGLU, h in bf16 hi + lo with per-block sums.
 //   decode_down:    one block per 16 output rows: W_down GEMV of every listed
 //                   expert, gate-weighted sum in list order, output write.
 //
@@ -419,7 +420,6 @@ __device__ __forceinline__ void gateup_body(const DecodeArgs& a, const DecodeWs&
   uint4* s_xhi = s_dyn;                                                         // [T][D/8]
   uint4* s_xlo = s_dyn + T * D8;                                                // [T][D/8]
   float2* s_xs = reinterpret_cast<float2*>(s_dyn + (HAS_LO ? 2 : 1) * T * D8);  // [T][D/32]
-  int32_t* s_first = reinterpret_cast<int32_t*>(s_xs + T * nbD);                // [E], T > 1
 
   // 0. This block's work: shared-expert rows, or a routed list entry.
   const int has_sh = a.shared != nullptr;
@@ -448,21 +448,10 @@ __device__ __forceinline__ void gateup_body(const DecodeArgs& a, const DecodeWs&
       const unsigned long long pick =
           __ballot(((hits >> lane) & 1ull) && __popcll(hits & below) == ui);
       ref = __builtin_amdgcn_readlane(rl, __builtin_ctzll(pick));
-    } else {
-      if (wv < T) {
-        int e;
-        float gt;
-        route_token(a, wv, lane, s_topk[wv], e, gt);
-        if (lane < a.k) {
-          R.e[wv * a.k + lane] = e;
-          R.g[wv * a.k + lane] = gt;
-        }
-      }
-      __syncthreads();
-      if (wv == 0) build_list<T>(a, w, R, s_first, lane, rb == 0, has_sh);
-      __syncthreads();
-      if (has_sh + ui >= R.nu) return;
-      ref = R.ref[has_sh + ui];
+    } else {  // the list was built by decode_list_kernel
+      const int nu = *w.nwork;
+      if (has_sh + ui >= nu) return;
+      ref = w.work_ref[has_sh + ui];
     }
     u = has_sh + ui;
     eb = a.routed + (size_t)ref * a.stride;
@@ -647,6 +636,31 @@ __device__ __forceinline__ void gateup_body(const DecodeArgs& a, const DecodeWs&
   }
 }
 
+// 2..4 tokens: the routing and the expert list, once per layer call.  One
+// block: wave t routes token t, then wave 0 builds and publishes the list
+// (and the miss list and usage counts).  The gate/up blocks read their entry
+// instead of each routing every token and building the list itself, work
+// that at four tokens took as long as their GEMV and ran on the same SIMDs.
+template <int T>
+__global__ __launch_bounds__(kGuThreads) void decode_list_kernel(DecodeArgs a, DecodeWs w) {
+  extern __shared__ int32_t s_first[];  // [E]
+  __shared__ RouteLds R;
+  __shared__ TopkScratch s_topk[kGuWaves];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  static_assert(T <= kGuWaves, "one wave per token");
+  if (wv < T) {
+    int e;
+    float gt;
+    route_token(a, wv, lane, s_topk[wv], e, gt);
+    if (lane < a.k) {
+      R.e[wv * a.k + lane] = e;
+      R.g[wv * a.k + lane] = gt;
+    }
+  }
+  __syncthreads();
+  if (wv == 0) build_list<T>(a, w, R, s_first, lane, true, a.shared != nullptr ? 1 : 0);
+}
+
 template <int T, int FMT, int XM>
 __global__ __launch_bounds__(kGuThreads, 2) void decode_gateup_kernel(DecodeArgs a, DecodeWs w) {
   extern __shared__ uint4 s_dyn[];
@@ -801,14 +815,17 @@ template <int T, int FMT, int XM>
 static hipError_t launch_decode_x(const DecodeArgs& a, const DecodeWs& w, hipStream_t st) {
   static size_t lds_gu = 0, lds_dn = 0;
   const int D8 = a.D / 8, nbD = a.D / 32;
-  const size_t lds = (size_t)T * D8 * 16 * (XM == kXF32 ? 2 : 1) + (size_t)T * nbD * 8 +
-                     (T > 1 ? (size_t)a.E * 4 : 0);
+  const size_t lds = (size_t)T * D8 * 16 * (XM == kXF32 ? 2 : 1) + (size_t)T * nbD * 8;
   const size_t lds_down =
       (size_t)kDnWaves * ((size_t)T * 2 * (w.Fp / 8) + (size_t)T * (w.Fp / 32) / 2) * 16;
   hipError_t e;
   if ((e = allow_lds(decode_gateup_kernel<T, FMT, XM>, lds, lds_gu)) != hipSuccess) return e;
   if ((e = allow_lds(decode_down_kernel<T, FMT>, lds_down, lds_dn)) != hipSuccess) return e;
   const int nblk = (a.shared ? a.Fs / 16 : 0) + (w.Wmax - 1) * (a.F / 16);
+  if constexpr (T > 1) {
+    decode_list_kernel<T><<<1, kGuThreads, (size_t)a.E * 4, st>>>(a, w);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if ((e = launch_timed(decode_gateup_kernel<T, FMT, XM>, dim3(nblk), dim3(kGuThreads),
                         (uint32_t)lds, st, a, w)) != hipSuccess)
     return e;
