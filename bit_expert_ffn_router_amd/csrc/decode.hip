@@ -67,6 +67,7 @@ size_t decode_ws_bytes(int T, int D, int F, int Fs, int E, int k) {
   b += align256(16 * (size_t)Wmax);                   // work_gate
   b += align256(2 * (size_t)Wmax * T * Fp) * 2;       // hh, hl
   b += align256(16 * (size_t)Wmax * T * (Fp / 32));   // hs
+  b += 256;                                           // rinv
   return b;
 }
 
@@ -84,6 +85,7 @@ DecodeWs decode_ws_carve(void* ws, int T, int D, int F, int Fs, int E, int k) {
   w.hh = (uint16_t*)take(2 * (size_t)w.Wmax * T * w.Fp);
   w.hl = (uint16_t*)take(2 * (size_t)w.Wmax * T * w.Fp);
   w.hs = (float2*)take(16 * (size_t)w.Wmax * T * (w.Fp / 32));
+  w.rinv = (float*)take(4 * kDecodeMaxT);
   return w;
 }
 
@@ -485,7 +487,10 @@ __device__ __forceinline__ void gateup_body(const DecodeArgs& a, const DecodeWs&
   float rinv[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) rinv[t] = 1.f;
-  if (RMS) {
+  if (RMS && T > 1) {  // published by decode_list_kernel
+#pragma unroll
+    for (int t = 0; t < T; ++t) rinv[t] = w.rinv[t];
+  } else if (RMS) {
     float ss[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) ss[t] = 0.f;
@@ -646,8 +651,22 @@ __global__ __launch_bounds__(kGuThreads) void decode_list_kernel(DecodeArgs a, D
   extern __shared__ int32_t s_first[];  // [E]
   __shared__ RouteLds R;
   __shared__ TopkScratch s_topk[kGuWaves];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  __shared__ float s_ss[kGuWaves][kDecodeMaxT];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   static_assert(T <= kGuWaves, "one wave per token");
+  // The RMS input factors of the tokens (for every gate/up block): the
+  // activation pieces are requested before the routing's logits, so both
+  // are in flight together; sums by thread, wave, then the waves in order.
+  constexpr int kXP = 2 * kDecodeMaxT * 4096 / 8 / kGuThreads;  // 16-byte pieces per thread (fp32, d_model 4096)
+  const int D = a.D, npc = (a.x_bf16 ? 1 : 2) * T * (D / 8);
+  uint4 xv[kXP];
+  if (a.rmsnorm) {
+#pragma unroll
+    for (int j = 0; j < kXP; ++j) {
+      const int i = tid + kGuThreads * j;
+      xv[j] = i < npc ? reinterpret_cast<const uint4*>(a.x)[i] : make_uint4(0, 0, 0, 0);
+    }
+  }
   if (wv < T) {
     int e;
     float gt;
@@ -657,7 +676,39 @@ __global__ __launch_bounds__(kGuThreads) void decode_list_kernel(DecodeArgs a, D
       R.g[wv * a.k + lane] = gt;
     }
   }
+  if (a.rmsnorm) {
+    float ss[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) ss[t] = 0.f;
+#pragma unroll
+    for (int j = 0; j < kXP; ++j) {
+      const int i = tid + kGuThreads * j;
+      const int t = a.x_bf16 ? i / (D / 8) : i / (D / 4);  // 8 bf16 or 4 fp32 values per piece
+      const uint32_t qq[4] = {xv[j].x, xv[j].y, xv[j].z, xv[j].w};
+      float q2 = 0.f;
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        if (a.x_bf16)
+          q2 += bf16_lo(qq[e2]) * bf16_lo(qq[e2]) + bf16_hi(qq[e2]) * bf16_hi(qq[e2]);
+        else
+          q2 += __uint_as_float(qq[e2]) * __uint_as_float(qq[e2]);
+      }
+#pragma unroll
+      for (int tt = 0; tt < T; ++tt) ss[tt] += (i < npc && tt == t) ? q2 : 0.f;
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const float r = wave_sum_f32(ss[t]);
+      if (lane == 0) s_ss[wv][t] = r;
+    }
+  }
   __syncthreads();
+  if (a.rmsnorm && tid < T) {
+    float ssum = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < kGuWaves; ++w2) ssum += s_ss[w2][tid];
+    w.rinv[tid] = 1.0f / sqrtf(ssum / (float)D + 1e-6f);
+  }
   if (wv == 0) build_list<T>(a, w, R, s_first, lane, true, a.shared != nullptr ? 1 : 0);
 }
 

@@ -83,6 +83,7 @@ struct DecodeWs {
   uint16_t* hh;        // [Wmax][T][Fp] bf16 hi of h
   uint16_t* hl;        // [Wmax][T][Fp] bf16 lo of h
   float2* hs;          // [Wmax][T][Fp/32][2] block sums of h, per 16-row half
+  float* rinv;         // [kDecodeMaxT] RMS input factors (2..4 tokens, from the list kernel)
   int Wmax;            // routed work capacity + 1 (shared)
   int Fp;              // padded FFN width of the h rows
 };
