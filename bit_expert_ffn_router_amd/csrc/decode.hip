@@ -642,64 +642,60 @@ __device__ __forceinline__ void gateup_body(const DecodeArgs& a, const DecodeWs&
 }
 
 // 2..4 tokens: the routing and the expert list, once per layer call.  One
-// block: wave t routes token t, then wave 0 builds and publishes the list
-// (and the miss list and usage counts).  The gate/up blocks read their entry
+// block: wave t routes token t (and waves 4..7 meanwhile find the RMS factors
+// of the input rule), then wave 0 builds and publishes the list (and the
+// miss list and usage counts).  The gate/up blocks read their entry
 // instead of each routing every token and building the list itself, work
 // that at four tokens took as long as their GEMV and ran on the same SIMDs.
 template <int T>
-__global__ __launch_bounds__(kGuThreads) void decode_list_kernel(DecodeArgs a, DecodeWs w) {
+__global__ __launch_bounds__(2 * kGuThreads) void decode_list_kernel(DecodeArgs a, DecodeWs w) {
   extern __shared__ int32_t s_first[];  // [E]
   __shared__ RouteLds R;
   __shared__ TopkScratch s_topk[kGuWaves];
   __shared__ float s_ss[kGuWaves][kDecodeMaxT];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   static_assert(T <= kGuWaves, "one wave per token");
-  // The RMS input factors of the tokens (for every gate/up block): the
-  // activation pieces are requested before the routing's logits, so both
-  // are in flight together; sums by thread, wave, then the waves in order.
-  constexpr int kXP = 2 * kDecodeMaxT * 4096 / 8 / kGuThreads;  // 16-byte pieces per thread (fp32, d_model 4096)
-  const int D = a.D, npc = (a.x_bf16 ? 1 : 2) * T * (D / 8);
-  uint4 xv[kXP];
-  if (a.rmsnorm) {
-#pragma unroll
-    for (int j = 0; j < kXP; ++j) {
-      const int i = tid + kGuThreads * j;
-      xv[j] = i < npc ? reinterpret_cast<const uint4*>(a.x)[i] : make_uint4(0, 0, 0, 0);
+  if (wv < kGuWaves) {  // waves 0..3: wave t routes token t
+    if (wv < T) {
+      int e;
+      float gt;
+      route_token(a, wv, lane, s_topk[wv], e, gt);
+      if (lane < a.k) {
+        R.e[wv * a.k + lane] = e;
+        R.g[wv * a.k + lane] = gt;
+      }
     }
-  }
-  if (wv < T) {
-    int e;
-    float gt;
-    route_token(a, wv, lane, s_topk[wv], e, gt);
-    if (lane < a.k) {
-      R.e[wv * a.k + lane] = e;
-      R.g[wv * a.k + lane] = gt;
-    }
-  }
-  if (a.rmsnorm) {
+  } else if (a.rmsnorm) {  // waves 4..7 meanwhile: the tokens' RMS factors
+    // (every gate/up block needs them); sums by thread, wave, then the four
+    // waves in order.  Piece i: 8 bf16 or 4 fp32 values of token i / (pieces
+    // per token).
+    const int tl = tid - kGuThreads, D = a.D;
+    const int ppt = (a.x_bf16 ? 1 : 2) * (D / 8);  // pieces per token
+    constexpr int kPP = 2 * 4096 / 8 / kGuThreads;  // pieces per thread and token, max
     float ss[T];
 #pragma unroll
-    for (int t = 0; t < T; ++t) ss[t] = 0.f;
+    for (int t = 0; t < T; ++t) {
+      ss[t] = 0.f;
 #pragma unroll
-    for (int j = 0; j < kXP; ++j) {
-      const int i = tid + kGuThreads * j;
-      const int t = a.x_bf16 ? i / (D / 8) : i / (D / 4);  // 8 bf16 or 4 fp32 values per piece
-      const uint32_t qq[4] = {xv[j].x, xv[j].y, xv[j].z, xv[j].w};
-      float q2 = 0.f;
+      for (int j = 0; j < kPP; ++j) {
+        const int i = tl + kGuThreads * j;
+        if (i < ppt) {
+          const uint4 v = reinterpret_cast<const uint4*>(a.x)[(size_t)t * ppt + i];
+          const uint32_t qq[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        if (a.x_bf16)
-          q2 += bf16_lo(qq[e2]) * bf16_lo(qq[e2]) + bf16_hi(qq[e2]) * bf16_hi(qq[e2]);
-        else
-          q2 += __uint_as_float(qq[e2]) * __uint_as_float(qq[e2]);
+          for (int e2 = 0; e2 < 4; ++e2) {
+            if (a.x_bf16)
+              ss[t] += bf16_lo(qq[e2]) * bf16_lo(qq[e2]) + bf16_hi(qq[e2]) * bf16_hi(qq[e2]);
+            else
+              ss[t] += __uint_as_float(qq[e2]) * __uint_as_float(qq[e2]);
+          }
+        }
       }
-#pragma unroll
-      for (int tt = 0; tt < T; ++tt) ss[tt] += (i < npc && tt == t) ? q2 : 0.f;
     }
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       const float r = wave_sum_f32(ss[t]);
-      if (lane == 0) s_ss[wv][t] = r;
+      if (lane == 0) s_ss[wv - kGuWaves][t] = r;
     }
   }
   __syncthreads();
@@ -707,7 +703,7 @@ __global__ __launch_bounds__(kGuThreads) void decode_list_kernel(DecodeArgs a, D
     float ssum = 0.f;
 #pragma unroll
     for (int w2 = 0; w2 < kGuWaves; ++w2) ssum += s_ss[w2][tid];
-    w.rinv[tid] = 1.0f / sqrtf(ssum / (float)D + 1e-6f);
+    w.rinv[tid] = 1.0f / sqrtf(ssum / (float)a.D + 1e-6f);
   }
   if (wv == 0) build_list<T>(a, w, R, s_first, lane, true, a.shared != nullptr ? 1 : 0);
 }
@@ -874,7 +870,7 @@ static hipError_t launch_decode_x(const DecodeArgs& a, const DecodeWs& w, hipStr
   if ((e = allow_lds(decode_down_kernel<T, FMT>, lds_down, lds_dn)) != hipSuccess) return e;
   const int nblk = (a.shared ? a.Fs / 16 : 0) + (w.Wmax - 1) * (a.F / 16);
   if constexpr (T > 1) {
-    decode_list_kernel<T><<<1, kGuThreads, (size_t)a.E * 4, st>>>(a, w);
+    decode_list_kernel<T><<<1, 2 * kGuThreads, (size_t)a.E * 4, st>>>(a, w);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if ((e = launch_timed(decode_gateup_kernel<T, FMT, XM>, dim3(nblk), dim3(kGuThreads),
