@@ -419,9 +419,14 @@ __device__ __forceinline__ void gateup_body(const DecodeArgs& a, const DecodeWs&
   constexpr bool HAS_LO = XM == kXF32;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int D = a.D, oD = octets(D), nbD = D / 32, D8 = D / 8;
-  uint4* s_xhi = s_dyn;                                                         // [T][D/8]
-  uint4* s_xlo = s_dyn + T * D8;                                                // [T][D/8]
-  float2* s_xs = reinterpret_cast<float2*>(s_dyn + (HAS_LO ? 2 : 1) * T * D8);  // [T][D/32]
+  // Token rows of the staged activations are D8p 16-byte pieces apart: one
+  // piece more than a row when T > 1, so that the rows one fragment read
+  // touches fall on different LDS banks (D/8 pieces is a multiple of the bank
+  // cycle for every supported d_model).
+  const int D8p = D8 + (T > 1 ? 1 : 0);
+  uint4* s_xhi = s_dyn;                                                          // [T][D8p]
+  uint4* s_xlo = s_dyn + T * D8p;                                                // [T][D8p]
+  float2* s_xs = reinterpret_cast<float2*>(s_dyn + (HAS_LO ? 2 : 1) * T * D8p);  // [T][D/32]
 
   // 0. This block's work: shared-expert rows, or a routed list entry.
   const int has_sh = a.shared != nullptr;
@@ -549,7 +554,7 @@ __device__ __forceinline__ void gateup_body(const DecodeArgs& a, const DecodeWs&
         X += v;
         Xc += dq_offset(b & 1, e2) * v;
       }
-      if (ok) s_xhi[i] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      if (ok) s_xhi[t * D8p + pc] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
       X = quad_sum(X);
       Xc = quad_sum(Xc);
       if (ok && (pc & 3) == 0) s_xs[t * nbD + b] = make_float2(X, Xc);
@@ -579,8 +584,8 @@ __device__ __forceinline__ void gateup_body(const DecodeArgs& a, const DecodeWs&
         Xc += dq_offset(b & 1, j0 + q2) * s;
       }
       if (ok) {
-        reinterpret_cast<uint2*>(s_xhi)[i] = make_uint2(hi[0], hi[1]);
-        if (HAS_LO) reinterpret_cast<uint2*>(s_xlo)[i] = make_uint2(lo[0], lo[1]);
+        reinterpret_cast<uint2*>(s_xhi)[t * 2 * D8p + pc] = make_uint2(hi[0], hi[1]);
+        if (HAS_LO) reinterpret_cast<uint2*>(s_xlo)[t * 2 * D8p + pc] = make_uint2(lo[0], lo[1]);
       }
       X = oct_sum(X);
       Xc = oct_sum(Xc);
@@ -599,7 +604,7 @@ __device__ __forceinline__ void gateup_body(const DecodeArgs& a, const DecodeWs&
     const int o = kh + 2 * i;
     if (o < oD) {
       auto xfrag = [&](int beta, bool lo) -> uint4 {  // rows n >= T are zero (a select)
-        const int idx = (n < T ? n : 0) * D8 + 4 * (8 * o + beta) + q;
+        const int idx = (n < T ? n : 0) * D8p + 4 * (8 * o + beta) + q;
         const uint4 v = lo ? s_xlo[idx] : s_xhi[idx];
         return n < T ? v : make_uint4(0, 0, 0, 0);
       };
@@ -862,7 +867,8 @@ template <int T, int FMT, int XM>
 static hipError_t launch_decode_x(const DecodeArgs& a, const DecodeWs& w, hipStream_t st) {
   static size_t lds_gu = 0, lds_dn = 0;
   const int D8 = a.D / 8, nbD = a.D / 32;
-  const size_t lds = (size_t)T * D8 * 16 * (XM == kXF32 ? 2 : 1) + (size_t)T * nbD * 8;
+  const int D8p = D8 + (T > 1 ? 1 : 0);  // padded token rows (see gateup_body)
+  const size_t lds = (size_t)T * D8p * 16 * (XM == kXF32 ? 2 : 1) + (size_t)T * nbD * 8;
   const size_t lds_down =
       (size_t)kDnWaves * ((size_t)T * 2 * (w.Fp / 8) + (size_t)T * (w.Fp / 32) / 2) * 16;
   hipError_t e;
