@@ -262,32 +262,20 @@ struct PfB {
 constexpr int kPfDmaA = 2;
 constexpr int kPfDmaB = 6;
 
-// Grouped GEMM tile.  MODE 0: gate/up (A = gathered activations, K = D, B =
-// the expert's gate/up rows, SwiGLU epilogue into H).  MODE 1: down (A = H
-// rows, K = F, B = W_down rows, epilogue into Y).  FMT: Q2SM or Q2S weights
-// (the same code words; Q2S records carry scales only).
-template <int MODE, int FMT>
-__global__ __launch_bounds__(kPfThreads, 1) void pf_gemm_kernel(PfArgs a, int nN, int nwork) {
-  static_assert(FMT == kQ2 || FMT == kQ2S, "prefill formats");
+// Grouped GEMM tile: rows row0 .. row0 + rows - 1 of the work list, weight
+// rows nb * kBN .. of the expert's matrix.  MODE 0: gate/up (A = gathered
+// activations, K = D, B = the expert's gate/up rows, SwiGLU epilogue into H).
+// MODE 1: down (A = H rows, K = F, B = W_down rows, epilogue into Y).  FMT:
+// Q2SM or Q2S weights (the same code words; Q2S records carry scales only).
+// NG: row groups of 16 that get MFMAs (rows <= 16 NG); the loads and the
+// dequantisation are the same for every NG.
+template <int MODE, int FMT, int NG>
+__device__ __forceinline__ void pf_tile(const PfArgs& a, PfA& sa0, PfA& sa1, PfA& sa2, PfA& sa3,
+                                        PfB& sb0, PfB& sb1, int e, int row0, int rows, int nb) {
   constexpr int kRec = rec_bytes(FMT);
-  __shared__ PfA sa0, sa1, sa2, sa3;
-  __shared__ PfB sb0, sb1;
+  constexpr int NV = 12 / NG;  // VALU slots per MFMA in the schedule (3 or 6)
   // wave index as a uniform (scalar) value: the weight addresses stay in SGPRs
   const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // XCD-aware order: blocks are dispatched round-robin over the 8 XCDs, so
-  // block i runs on XCD i % 8.  Each XCD gets a contiguous eighth of the
-  // work items that exist (ntiles * nN, known only here; the grid is sized
-  // for the most tiles the routing can make, nwork, and is a multiple of 8),
-  // so the column blocks of one tile and the tiles of one expert share an L2
-  // and every XCD has work.  Blocks past an XCD's share exit.
-  const int nreal = *a.w.ntiles * nN;
-  const int per_xcd = (nreal + 7) / 8;
-  const int jx = blockIdx.x / 8;
-  const int bid = (blockIdx.x % 8) * per_xcd + jx;
-  if (jx >= per_xcd || bid >= nreal || bid >= nwork) return;
-  const int ti = bid / nN, nb = bid % nN;
-  const int4 tile = a.w.tiles[ti];
-  const int e = tile.x, row0 = tile.y, rows = tile.z;
   const int P = a.T * a.k;
   const bool sh = e < 0;
   const int F = sh ? a.Fs : a.F;
@@ -296,7 +284,6 @@ __global__ __launch_bounds__(kPfThreads, 1) void pf_gemm_kernel(PfArgs a, int nN
   const int nkb = K / 32, nst = (nkb + 1) / 2;
   const int oK = octets(K);
   const int NW = MODE == 0 ? 2 * F : a.D;  // weight rows of this GEMM
-  if (nb * kBN >= NW) return;
 
   // A: this lane's 16-byte piece (row 16 wv + lane % 16, quarter lane / 16) of
   // the wave's row group; rows past the tile read row 0 (masked later).
@@ -353,9 +340,9 @@ __global__ __launch_bounds__(kPfThreads, 1) void pf_gemm_kernel(PfArgs a, int nN
     for (int i = 0; i < 2; ++i) dma16(smp[i] + ro, &B.sm[wv][i][0]);
   };
 
-  f32x4_t acc[8][4];
+  f32x4_t acc[NG][4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < NG; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
@@ -385,7 +372,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void pf_gemm_kernel(PfArgs a, int nN
   };
   auto mfmas = [&](const PfA& A, int kk, const uint4 (&bf)[4]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < NG; ++i) {
       const uint4 af = lds128(&A.a[kk][(i * 4 + q) * 16 + n]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(af, bf[j], acc[i][j]);
@@ -440,17 +427,17 @@ __global__ __launch_bounds__(kPfThreads, 1) void pf_gemm_kernel(PfArgs a, int nN
       // Instruction order for the scheduler: the LDS reads first, then each
       // MFMA followed by three VALU instructions of the other k-step's
       // dequantisation, which thereby run in the MFMAs' shadow.
-      __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);  // DS reads: A (k-step 2s), tables
+      __builtin_amdgcn_sched_group_barrier(0x100, NG + 4, 0);  // DS reads: A (k-step 2s), tables
 #pragma unroll
-      for (int t = 0; t < 32; ++t) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
+      for (int t = 0; t < 4 * NG; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);  // VALU
       }
-      __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);  // DS reads: A (k-step 2s+1), tables
+      __builtin_amdgcn_sched_group_barrier(0x100, NG + 4, 0);  // DS reads: A (k-step 2s+1), tables
 #pragma unroll
-      for (int t = 0; t < 32; ++t) {
+      for (int t = 0; t < 4 * NG; ++t) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
       }
     }
     issue_a(abuf((i + 3) % 4), s + 3);
@@ -489,7 +476,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void pf_gemm_kernel(PfArgs a, int nN
     const int hg = nb * (kBN / 32) + 2 * wv + (cb >> 4);
     const bool colok = hg * 16 < F;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < NG; ++i) {
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
@@ -509,7 +496,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void pf_gemm_kernel(PfArgs a, int nN
     for (int jj = 0; jj < 2; ++jj) {
       const int col = nb * kBN + 64 * wv + 32 * jj + cb;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < NG; ++i) {
 #pragma unroll
         for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
@@ -524,6 +511,35 @@ __global__ __launch_bounds__(kPfThreads, 1) void pf_gemm_kernel(PfArgs a, int nN
       }
     }
   }
+}
+
+template <int MODE, int FMT>
+__global__ __launch_bounds__(kPfThreads, 1) void pf_gemm_kernel(PfArgs a, int nN, int nwork) {
+  static_assert(FMT == kQ2 || FMT == kQ2S, "prefill formats");
+  __shared__ PfA sa0, sa1, sa2, sa3;
+  __shared__ PfB sb0, sb1;
+  // XCD-aware order: blocks are dispatched round-robin over the 8 XCDs, so
+  // block i runs on XCD i % 8.  Each XCD gets a contiguous eighth of the
+  // work items that exist (ntiles * nN, known only here; the grid is sized
+  // for the most tiles the routing can make, nwork, and is a multiple of 8),
+  // so the column blocks of one tile and the tiles of one expert share an L2
+  // and every XCD has work.  Blocks past an XCD's share exit.
+  const int nreal = *a.w.ntiles * nN;
+  const int per_xcd = (nreal + 7) / 8;
+  const int jx = blockIdx.x / 8;
+  const int bid = (blockIdx.x % 8) * per_xcd + jx;
+  if (jx >= per_xcd || bid >= nreal || bid >= nwork) return;
+  const int ti = bid / nN, nb = bid % nN;
+  const int4 tile = a.w.tiles[ti];
+  const int e = tile.x, row0 = tile.y, rows = tile.z;
+  const int F = e < 0 ? a.Fs : a.F;
+  if (nb * kBN >= (MODE == 0 ? 2 * F : a.D)) return;
+  // Tiles of at most 64 rows (the tails of the expert groups, and whole small
+  // groups) skip the MFMAs of their empty row groups.
+  if (rows <= 64)
+    pf_tile<MODE, FMT, 4>(a, sa0, sa1, sa2, sa3, sb0, sb1, e, row0, rows, nb);
+  else
+    pf_tile<MODE, FMT, 8>(a, sa0, sa1, sa2, sa3, sb0, sb1, e, row0, rows, nb);
 }
 
 // ----------------------------------------------------------------------------
