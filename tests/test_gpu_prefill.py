@@ -153,3 +153,50 @@ def test_identical_experts_prefill_equals_dense_swiglu(g):
     a2, b2 = x @ sg.T, x @ su.T
     dense += (a2 / (1 + np.exp(-a2)) * b2) @ sd.T
     assert rel_l2(got, dense) <= RTOL_L2
+
+
+def _forced_logits(T, E, k, counts, seed):
+    """Router logits whose top-k gives expert e exactly counts[e] pairs.
+
+    The expert ids, sorted and repeated counts[e] times, are dealt out with
+    stride T: token t takes ids[t + j*T] as its rank-j expert, which are
+    distinct because no count exceeds T.  Chosen logits are 4 - 0.3 j, the
+    rest lie near -3, so the routing is unambiguous in any precision."""
+    counts = list(counts) + [0] * (E - len(counts))
+    assert sum(counts) == T * k and max(counts) <= T
+    ids = np.repeat(np.arange(E), counts)
+    rng = np.random.default_rng(seed)
+    lg = (-3.0 + 0.1 * rng.standard_normal((T, E))).astype(np.float32)
+    for j in range(k):
+        lg[np.arange(T), ids[j * T:(j + 1) * T]] = np.float32(4.0 - 0.3 * j) + \
+            np.float32(0.01) * rng.random(T, dtype=np.float32)
+    return lg
+
+
+# group sizes on both sides of the 64-row switch between the two GEMM bodies
+# and of the 128-row tile edge, plus empty and one-row groups
+_EDGE_COUNTS = [64, 65, 1, 63, 127, 128, 129, 0, 16, 17, 31, 33, 48, 5]
+
+
+@pytest.mark.parametrize("where", ["tiny", "full"])
+def test_prefill_group_size_edges(g, tiny, full, where):
+    w, shape, L = tiny if where == "tiny" else full
+    D, E, k = w["d_model"], w["n_experts"], w["top_k"]
+    T = 400 if where == "tiny" else 300
+    counts = list(_EDGE_COUNTS)
+    rest = T * k - sum(counts)
+    while rest > 0:  # the remaining pairs in groups of at most T rows
+        counts.append(min(rest, T, 257))
+        rest -= counts[-1]
+    logits = _forced_logits(T, E, k, counts, seed=11)
+    xb = synth.activations_bf16(0, 9, T, D)
+    run = g.LayerRun(shape, T)
+    out = run(L.table(), g.u16_to_dev(xb), g.moe.MOE_BF16, g.f32_to_dev(logits), g.moe.MOE_F32)
+    got = g.out_to_f64(out, False).reshape(T, D)
+    ow = OracleWeights(0, 0, D, w["d_ff"], w["d_ff_shared"], E, w["fmt"])
+    ref, idx, _ = O.layer_forward(O.bf16_to_f64(xb), logits, k, ow, ow.shared)
+    assert np.array_equal(np.bincount(np.asarray(idx).ravel(), minlength=E)[:len(counts)],
+                          np.asarray(counts))
+    err = rel_l2(got, ref)
+    print("prefill group-size edges (%s, T=%d) rel_l2=%.3g" % (where, T, err))
+    assert err <= RTOL_L2
