@@ -15,8 +15,12 @@
 // accumulation, fp32 h and output.
 #include <atomic>
 #include <condition_variable>
+#include <cstdlib>
+#include <cstring>
+#include <fstream>
 #include <functional>
 #include <mutex>
+#include <string>
 #include <thread>
 #include <vector>
 
@@ -165,8 +169,22 @@ inline v4f ld4(const float* p) {
 }
 inline float hsum(v4f v) { return (v[0] + v[1]) + (v[2] + v[3]); }
 
-// Row n of one record dotted with octet o of a record-order vector.
-float record_row_dot(const uint8_t* rec, int fmt, int n, const float* xv, const float* xs) {
+// Block scale and offset of row n, block b: w = sc * u + off.
+inline void block_params(const uint8_t* rec, int fmt, int n, int b, float& sc, float& off) {
+  if (fmt == kQ2) {
+    const uint16_t* pp = reinterpret_cast<const uint16_t*>(rec + 1024 + 4 * (8 * n + b));
+    sc = half_to_float(pp[0]);
+    off = half_to_float(pp[1]);  // w = s u + m
+  } else {
+    const int base = fmt == kQ3 ? 1536 : 1024;
+    sc = half_to_float(*reinterpret_cast<const uint16_t*>(rec + base + 2 * (8 * n + b)));
+    off = -(fmt == kQ3 ? 4.f : 2.f) * sc;  // w = s (u - 4) or s (u - 2)
+  }
+}
+
+// Row n of one record dotted with octet o of a record-order vector (any
+// x86-64 CPU: SSE2 and code tables).
+float record_row_dot_sse2(const uint8_t* rec, int fmt, int n, const float* xv, const float* xs) {
   const CodeTables& T = tables();
   const uint32_t* lo = reinterpret_cast<const uint32_t*>(rec);           // word (L, w): 4 L + w
   const uint32_t* hi = reinterpret_cast<const uint32_t*>(rec + 1024);    // Q3S: (L, h): 2 L + h
@@ -188,29 +206,104 @@ float record_row_dot(const uint8_t* rec, int fmt, int n, const float* xv, const 
       acc += ce * ld4(xe) + co * ld4(xe + 4);
     }
     float sc, off;
-    if (fmt == kQ2) {
-      const uint16_t* pp = reinterpret_cast<const uint16_t*>(rec + 1024 + 4 * (8 * n + b));
-      sc = half_to_float(pp[0]);
-      off = half_to_float(pp[1]);  // w = s u + m
-    } else {
-      const int base = fmt == kQ3 ? 1536 : 1024;
-      sc = half_to_float(*reinterpret_cast<const uint16_t*>(rec + base + 2 * (8 * n + b)));
-      off = -(fmt == kQ3 ? 4.f : 2.f) * sc;  // w = s (u - 4) or s (u - 2)
-    }
+    block_params(rec, fmt, n, b, sc, off);
     s += sc * hsum(acc) + off * xs[b];
   }
   return s;
 }
 
-// Row `row` of a matrix stored from `base` as 16-row groups of octet records
-// (reduction length K), dotted with the record-order vector v.
-float matrix_row_dot(const uint8_t* base, int fmt, int row, int K, const RecVec& v) {
+// Four rows n0 .. n0 + 3 of one record dotted with octet o of a record-order
+// vector, with AVX2 and FMA.  The eight codes of a (block, quarter) word come
+// out of one broadcast word by per-lane shifts (even columns at bits 0, 2, 4,
+// 6 of the block's byte, odd ones 16 bits higher), already in the record
+// order of the vector; the four rows are independent FMA chains that share
+// each vector load, and each block's sum is scaled into one accumulator per
+// row, so a row ends in one horizontal sum.
+typedef float v8f __attribute__((vector_size(32)));
+typedef uint32_t v8u __attribute__((vector_size(32)));
+__attribute__((target("avx2,fma"))) void record_rows4_avx2(const uint8_t* rec, int fmt, int n0,
+                                                           const float* xv, const float* xs,
+                                                           float* out) {
+  const uint32_t* lo = reinterpret_cast<const uint32_t*>(rec);
+  const uint32_t* hi = reinterpret_cast<const uint32_t*>(rec + 1024);
+  const v8u lanes = {0, 2, 4, 6, 16, 18, 20, 22};
+  const v8f zero = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  v8f tot[4] = {zero, zero, zero, zero};
+  float offs[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int b = 0; b < 8; ++b) {
+    const int wd = b / 2, sh = 8 * (b % 2);
+    const int extra = (wd % 2 == 0) ? 1 : 0;
+    const v8u shc = lanes + (uint32_t)sh, shb = lanes + (uint32_t)(sh + extra);
+    v8f acc[4] = {zero, zero, zero, zero};
+    for (int q = 0; q < 4; ++q) {
+      v8f x;
+      __builtin_memcpy(&x, xv + 32 * b + 8 * q, sizeof x);
+      for (int r = 0; r < 4; ++r) {
+        const int L = 16 * q + n0 + r;
+        const uint32_t W = lo[4 * L + wd];
+        v8u c = ((v8u){W, W, W, W, W, W, W, W} >> shc) & 3u;
+        if (fmt == kQ3) {  // u3 = u + 4 * (third bit)
+          const uint32_t H = hi[2 * L + wd / 2];
+          c += (((v8u){H, H, H, H, H, H, H, H} >> shb) & 1u) << 2;
+        }
+        acc[r] = __builtin_convertvector(c, v8f) * x + acc[r];
+      }
+    }
+    for (int r = 0; r < 4; ++r) {
+      float sc, off;
+      block_params(rec, fmt, n0 + r, b, sc, off);
+      tot[r] = (v8f){sc, sc, sc, sc, sc, sc, sc, sc} * acc[r] + tot[r];
+      offs[r] += off * xs[b];
+    }
+  }
+  for (int r = 0; r < 4; ++r) {
+    const v8f t = tot[r];
+    out[r] = (((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]))) + offs[r];
+  }
+}
+
+// Four rows with the SSE2 row dot product.
+void record_rows4_sse2(const uint8_t* rec, int fmt, int n0, const float* xv, const float* xs,
+                       float* out) {
+  for (int r = 0; r < 4; ++r) out[r] = record_row_dot_sse2(rec, fmt, n0 + r, xv, xs);
+}
+
+// The row dot products this process uses: AVX2 + FMA where the CPU has them,
+// else SSE2.  MOE_HOST_SIMD=sse2 in the environment selects SSE2 (read at
+// every host layer call).  The two differ only in fp32 rounding order.
+typedef void (*RowDot)(const uint8_t*, int, int, const float*, const float*, float*);
+// The CPU's features come from the flags line of /proc/cpuinfo, which lists
+// only what the kernel has enabled (AVX state included).
+bool cpu_has_avx2_fma() {
+  std::ifstream f("/proc/cpuinfo");
+  std::string line;
+  while (std::getline(f, line)) {
+    if (line.compare(0, 5, "flags") != 0) continue;
+    const std::string l = " " + line + " ";
+    return l.find(" avx2 ") != std::string::npos && l.find(" fma ") != std::string::npos;
+  }
+  return false;
+}
+RowDot row_dot_impl() {
+  static const bool avx2 = cpu_has_avx2_fma();
+  const char* e = getenv("MOE_HOST_SIMD");
+  if (e && strcmp(e, "sse2") == 0) return record_rows4_sse2;
+  return avx2 ? record_rows4_avx2 : record_rows4_sse2;
+}
+
+// Rows row0 .. row0 + 3 (row0 % 4 == 0) of a matrix stored from `base` as
+// 16-row groups of octet records (reduction length K), dotted with the
+// record-order vector v; out[r] gets row row0 + r.
+void matrix_rows4_dot(RowDot dot, const uint8_t* base, int fmt, int row0, int K, const RecVec& v,
+                      float* out) {
   const int oK = (K + 255) / 256, rb = rec_bytes(fmt);
-  const uint8_t* grp = base + (size_t)(row / 16) * oK * rb;
-  float s = 0.f;
-  for (int o = 0; o < oK; ++o)
-    s += record_row_dot(grp + (size_t)o * rb, fmt, row % 16, &v.v[(size_t)o * 256], &v.sum[(size_t)o * 8]);
-  return s;
+  const uint8_t* grp = base + (size_t)(row0 / 16) * oK * rb;
+  float s[4] = {0.f, 0.f, 0.f, 0.f}, p[4];
+  for (int o = 0; o < oK; ++o) {
+    dot(grp + (size_t)o * rb, fmt, row0 % 16, &v.v[(size_t)o * 256], &v.sum[(size_t)o * 8], p);
+    for (int r = 0; r < 4; ++r) s[r] += p[r];
+  }
+  for (int r = 0; r < 4; ++r) out[r] = s[r];
 }
 
 }  // namespace
@@ -246,6 +339,7 @@ hipError_t launch_add_rows(void* out, int out_bf16, const float* y, size_t n, hi
 void host_miss_ffn(int D, int F, int fmt, int T, const float* xhat, const MissRec* miss, int nm,
                    const uint8_t* const* experts, float* y, moe_host_pool* pool) {
   const int ng = F / 16, oD = D / 256, rb = rec_bytes(fmt);
+  const RowDot dot = row_dot_impl();
   std::vector<RecVec> xr(T);
   for (int t = 0; t < T; ++t) xr[t].set(xhat + (size_t)t * D, D);
   std::vector<float> h((size_t)nm * F, 0.f);
@@ -256,13 +350,16 @@ void host_miss_ffn(int D, int F, int fmt, int T, const float* xhat, const MissRe
     const RecVec& x = xr[miss[m].token];
     const uint8_t* gate = ex + (size_t)(2 * g) * oD * rb;
     const uint8_t* up = ex + (size_t)(2 * g + 1) * oD * rb;
-    for (int n = 0; n < 16; ++n) {
-      float a = 0.f, b = 0.f;
+    for (int n0 = 0; n0 < 16; n0 += 4) {
+      float a[4] = {0.f, 0.f, 0.f, 0.f}, b[4] = {0.f, 0.f, 0.f, 0.f}, p[4];
       for (int o = 0; o < oD; ++o) {
-        a += record_row_dot(gate + (size_t)o * rb, fmt, n, &x.v[(size_t)o * 256], &x.sum[(size_t)o * 8]);
-        b += record_row_dot(up + (size_t)o * rb, fmt, n, &x.v[(size_t)o * 256], &x.sum[(size_t)o * 8]);
+        dot(gate + (size_t)o * rb, fmt, n0, &x.v[(size_t)o * 256], &x.sum[(size_t)o * 8], p);
+        for (int r = 0; r < 4; ++r) a[r] += p[r];
+        dot(up + (size_t)o * rb, fmt, n0, &x.v[(size_t)o * 256], &x.sum[(size_t)o * 8], p);
+        for (int r = 0; r < 4; ++r) b[r] += p[r];
       }
-      h[(size_t)m * F + 16 * g + n] = a / (1.0f + expf(-a)) * b;
+      for (int r = 0; r < 4; ++r)
+        h[(size_t)m * F + 16 * g + n0 + r] = a[r] / (1.0f + expf(-a[r])) * b[r];
     }
   };
   if (pool) pool->run(nm * ng, gateup);
@@ -276,8 +373,11 @@ void host_miss_ffn(int D, int F, int fmt, int T, const float* xhat, const MissRe
     for (int m = 0; m < nm; ++m) {
       const uint8_t* dn = experts[miss[m].expert] + down_offset(D, F, fmt);
       float* yt = y + (size_t)miss[m].token * D;
-      for (int r = 16 * rg; r < 16 * rg + 16; ++r)
-        yt[r] += miss[m].gate * matrix_row_dot(dn, fmt, r, F, hr[m]);
+      for (int r0 = 16 * rg; r0 < 16 * rg + 16; r0 += 4) {
+        float p[4];
+        matrix_rows4_dot(dot, dn, fmt, r0, F, hr[m], p);
+        for (int r = 0; r < 4; ++r) yt[r0 + r] += miss[m].gate * p[r];
+      }
     }
   };
   if (pool) pool->run(D / 16, down);
