@@ -27,35 +27,53 @@
 #include "kernels.hpp"
 
 // ---------------------------------------------------------------------------
-// Thread pool (caller-owned; see moe_host_pool_create).
+// Thread pool (caller-owned; see moe_host_pool_create).  A layer call runs two
+// short parallel phases, so waking sleeping threads would cost more than the
+// work: workers poll for a new job for a while (about 100 us) before they
+// sleep on the condition variable, and the caller waits for the items, not
+// for every worker.  Items are claimed by compare-and-swap on (generation,
+// next item), so a worker that arrives after its job has finished claims
+// nothing and never touches the next job.
 struct moe_host_pool {
+  static constexpr int kSpin = 1 << 16;  // polls of the generation before sleeping
   std::vector<std::thread> threads;
   std::mutex mu;
-  std::condition_variable cv_work, cv_done;
-  std::function<void(int)> job;
-  int n_items = 0;
-  std::atomic<int> next{0};
-  int busy = 0;
-  uint64_t gen = 0;
-  bool stop = false;
+  std::condition_variable cv;
+  std::function<void(int)> job;        // written only while no item is claimable
+  std::atomic<uint64_t> state{0};      // generation << 32 | next item
+  std::atomic<int> n_items{0};
+  std::atomic<int> done{0};
+  std::atomic<uint32_t> gen{0};
+  bool stop = false;                   // under mu
 
-  void drain() {
-    for (int i = next.fetch_add(1); i < n_items; i = next.fetch_add(1)) job(i);
+  // Claims and runs items of generation g until none is left.
+  void drain(uint32_t g) {
+    const int n = n_items.load(std::memory_order_acquire);
+    uint64_t v = state.load(std::memory_order_acquire);
+    for (;;) {
+      if ((uint32_t)(v >> 32) != g || (int)(uint32_t)v >= n) return;
+      if (state.compare_exchange_weak(v, v + 1, std::memory_order_acq_rel,
+                                      std::memory_order_acquire)) {
+        job((int)(uint32_t)v);
+        done.fetch_add(1, std::memory_order_release);
+        v = state.load(std::memory_order_acquire);
+      }
+    }
   }
   void worker() {
-    uint64_t seen = 0;
+    uint32_t seen = 0;
     for (;;) {
-      {
+      uint32_t g;
+      int polls = 0;
+      while ((g = gen.load(std::memory_order_acquire)) == seen) {
+        if (++polls < kSpin) continue;
         std::unique_lock<std::mutex> lk(mu);
-        cv_work.wait(lk, [&] { return stop || gen != seen; });
+        cv.wait(lk, [&] { return stop || gen.load(std::memory_order_acquire) != seen; });
         if (stop) return;
-        seen = gen;
+        polls = 0;
       }
-      drain();
-      {
-        std::lock_guard<std::mutex> lk(mu);
-        if (--busy == 0) cv_done.notify_all();
-      }
+      seen = g;
+      drain(g);
     }
   }
   // Items 0..n-1 of fn over the workers and the calling thread; returns when
@@ -65,18 +83,19 @@ struct moe_host_pool {
       for (int i = 0; i < n; ++i) fn(i);
       return;
     }
+    job = std::move(fn);
+    n_items.store(n, std::memory_order_relaxed);
+    done.store(0, std::memory_order_relaxed);
+    const uint32_t g = gen.load(std::memory_order_relaxed) + 1;
+    state.store((uint64_t)g << 32, std::memory_order_release);
     {
-      std::lock_guard<std::mutex> lk(mu);
-      job = std::move(fn);
-      n_items = n;
-      next.store(0);
-      busy = (int)threads.size();
-      ++gen;
+      std::lock_guard<std::mutex> lk(mu);  // a worker about to sleep sees g or is woken
+      gen.store(g, std::memory_order_release);
     }
-    cv_work.notify_all();
-    drain();
-    std::unique_lock<std::mutex> lk(mu);
-    cv_done.wait(lk, [&] { return busy == 0; });
+    cv.notify_all();
+    drain(g);
+    while (done.load(std::memory_order_acquire) < n) {
+    }
   }
 };
 
@@ -414,7 +433,7 @@ void moe_host_pool_delete(moe_host_pool* p) {
     std::lock_guard<std::mutex> lk(p->mu);
     p->stop = true;
   }
-  p->cv_work.notify_all();
+  p->cv.notify_all();  // polling workers see stop once they go to sleep
   for (auto& t : p->threads) t.join();
   delete p;
 }
