@@ -245,7 +245,9 @@ moe_status moe_layer_forward(const moe_shape* shape, int32_t tokens,
 
 /* Opaque pool of worker threads for moe_host_miss_ffn, owned by the caller
  * (n_threads counts the calling thread: n_threads - 1 workers are started).
- * Destroy joins the workers. */
+ * One moe_host_miss_ffn call at a time may use a pool.  Between calls the
+ * workers poll for new work for about 100 us, then sleep.  Destroy joins the
+ * workers. */
 typedef struct moe_host_pool moe_host_pool;
 moe_status moe_host_pool_create(int32_t n_threads, moe_host_pool** pool);
 void moe_host_pool_destroy(moe_host_pool* pool);
