@@ -721,13 +721,27 @@ __global__ __launch_bounds__(kGuThreads, 2) void decode_gateup_kernel(DecodeArgs
 }
 
 // ----------------------------------------------------------------------------
+// Direct global -> LDS load: lane l's 16 bytes land at lds + 16 l (`lds` the
+// same for the whole wave); counts in vmcnt.
+typedef __attribute__((address_space(3))) void dn_lds_t;
+__device__ __forceinline__ void dn_dma16(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds(src, (dn_lds_t*)lds, 16, 0, 0);
+}
+// Wait until no vector-memory operation of this wave is in flight.
+__device__ __forceinline__ void dn_wait_vm0() {
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0); expcnt, lgkmcnt not waited
+}
+
+// ----------------------------------------------------------------------------
 // decode_down.  Grid: D/16 blocks of 1024 threads; wave w handles list
 // entries u = w, w + 16, ...; outputs are summed over waves in a fixed order.
-// The h rows (bf16 hi and lo) and block sums of entry u sit at a place that
-// does not depend on the list, so each wave issues those of its first entry
-// together with the list loads; its weight loads follow as soon as the
-// entry's expert is known.  h and sums are staged in a wave-private LDS
-// region for the MFMA operands.
+// Per entry a wave issues, back to back: the entry's weight records, its h
+// rows (bf16 hi and lo of its T tokens) by direct global -> LDS loads into
+// the wave's own LDS region, its block sums, and the list slot of its next
+// entry; then it waits once.  So an entry costs one HBM round trip (the
+// weights), with h (an L2 read: every block reads every entry's h) under it.
+// Staging h through registers instead, its second half could only be read
+// after the first was stored, behind the weights.
 template <int T, int FMT>
 __global__ __launch_bounds__(1024) void decode_down_kernel(DecodeArgs a, DecodeWs w) {
   extern __shared__ uint4 s_dyn[];
@@ -742,27 +756,19 @@ __global__ __launch_bounds__(1024) void decode_down_kernel(DecodeArgs a, DecodeW
   float2* s_hs = reinterpret_cast<float2*>(s_hw + nh);  // [T][Fp/32], halves combined
   const DqConsts kc = dq_consts();
 
-  // h of one entry is staged in chunks of 64 * HV uint4 per wave; the first
-  // chunk (all of it for up to two tokens at d_ff <= 512) is prefetched.
-  constexpr int HV = T <= 2 ? 2 * T : 4;
-  uint4 hv[HV], sv;
-  auto load_h = [&](int u, int c0) {
+  // h of entry u, [T][hi row, lo row] (nh uint4, a multiple of 64 since Fp is
+  // a multiple of 256), to this wave's LDS region: one direct load per 64
+  // uint4, lane l taking element c0 + l.
+  auto dma_h = [&](int u) {
     const uint4* gh = reinterpret_cast<const uint4*>(w.hh) + (size_t)u * T * hrow;
     const uint4* gl = reinterpret_cast<const uint4*>(w.hl) + (size_t)u * T * hrow;
-#pragma unroll
-    for (int j = 0; j < HV; ++j) {
-      const int i0 = c0 + lane + 64 * j;
-      const int i = i0 < nh ? i0 : 0;
+    for (int c0 = 0; c0 < nh; c0 += 64) {
+      const int i = c0 + lane;
       const int t = i / (2 * hrow), rem = i % (2 * hrow);
-      const uint4 v = rem < hrow ? gh[t * hrow + rem] : gl[t * hrow + rem - hrow];
-      hv[j] = i0 < nh ? v : make_uint4(0, 0, 0, 0);
+      dn_dma16(rem < hrow ? gh + t * hrow + rem : gl + t * hrow + rem - hrow, s_hw + c0);
     }
   };
-  auto store_h = [&](int c0) {
-#pragma unroll
-    for (int j = 0; j < HV; ++j)
-      if (c0 + lane + 64 * j < nh) s_hw[c0 + lane + 64 * j] = hv[j];
-  };
+  uint4 sv;
   auto load_s = [&](int u) {
     const uint4* gs = reinterpret_cast<const uint4*>(w.hs) + (size_t)u * nsum;
     const uint4 v = gs[lane < nsum ? lane : 0];
@@ -772,22 +778,14 @@ __global__ __launch_bounds__(1024) void decode_down_kernel(DecodeArgs a, DecodeW
   const int nwork = *w.nwork;
   int ref = 0;
   float4 gt = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (wv < w.Wmax) {
+  if (wv < nwork) {
     ref = w.work_ref[wv];
     gt = reinterpret_cast<const float4*>(w.work_gate)[wv];
-    load_h(wv, 0);
-    load_s(wv);
   }
   float oacc[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) oacc[t] = 0.f;
   for (int u = wv; u < nwork; u += kDnWaves) {
-    if (u != wv) {
-      ref = w.work_ref[u];
-      gt = reinterpret_cast<const float4*>(w.work_gate)[u];
-      load_h(u, 0);
-      load_s(u);
-    }
     const bool sh = ref < 0;
     const int Fu = sh ? a.Fs : a.F;
     const int oF = octets(Fu), nb = Fu / 32;
@@ -798,12 +796,15 @@ __global__ __launch_bounds__(1024) void decode_down_kernel(DecodeArgs a, DecodeW
 #pragma unroll
     for (int o = 0; o < kMaxDecodeFOct; ++o)
       if (o < oF) load_record<FMT>(base + (size_t)o * rec_bytes(FMT), lane, cw[o], hw[o], pa[o], pb[o]);
-    // h and sums to this wave's LDS region
-    store_h(0);
-    for (int c0 = 64 * HV; c0 < nh; c0 += 64 * HV) {
-      load_h(u, c0);
-      store_h(c0);
+    dma_h(u);
+    load_s(u);
+    int ref_n = 0;
+    float4 gt_n = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (u + kDnWaves < nwork) {
+      ref_n = w.work_ref[u + kDnWaves];
+      gt_n = reinterpret_cast<const float4*>(w.work_gate)[u + kDnWaves];
     }
+    dn_wait_vm0();  // weights, h (in LDS), sums and the next slot have arrived
     if (lane < nsum)
       s_hs[lane] = make_float2(__uint_as_float(sv.x) + __uint_as_float(sv.z),
                                __uint_as_float(sv.y) + __uint_as_float(sv.w));
@@ -831,7 +832,9 @@ __global__ __launch_bounds__(1024) void decode_down_kernel(DecodeArgs a, DecodeW
       mt[t] += __shfl_xor(mt[t], 32, 64);
       oacc[t] += gg[t] * (acc[t] + mt[t]);
     }
-    wave_lds_fence();  // LDS region reused by the next entry
+    wave_lds_fence();  // this entry's LDS reads are done before the next entry's h lands
+    ref = ref_n;
+    gt = gt_n;
   }
   if (lane < 16) {
 #pragma unroll
