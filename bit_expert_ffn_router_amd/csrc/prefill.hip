@@ -355,19 +355,41 @@ __device__ __forceinline__ void pf_tile(const PfArgs& a, PfA& sa0, PfA& sa1, PfA
 #pragma unroll
     for (int j = 0; j < 4; ++j) cwo[j] = lds128(&B.code[wv][j][lane]);
   };
+  // The 4-entry bf16 tables of the octet, once per (tile, row, block) rather
+  // than once per lane that uses them: lane l builds the 8 tables of tile
+  // l / 16, row l % 16 into the wave's code region, which load_codes has
+  // just read out (the wave's LDS operations run in order).  Layout
+  // [tile][block][row] x (lo, hi) words, 4 KB per wave: the 16 rows a
+  // k-step reads are 128 contiguous bytes.
+  auto build_tables = [&](PfB& B) __attribute__((always_inline)) {
+    const int jt = lane >> 4, nt = lane & 15;
+    const uint32_t* smw = reinterpret_cast<const uint32_t*>(&B.sm[wv][0][0]) + (jt >> 1) * 256;
+    uint32_t lo[8], hi[8];
+    if constexpr (FMT == kQ2) {
+      const u32x4_t a0 = *reinterpret_cast<const u32x4_t*>(smw + ((jt & 1) * 32 + nt) * 4);
+      const u32x4_t a1 = *reinterpret_cast<const u32x4_t*>(smw + ((jt & 1) * 32 + 16 + nt) * 4);
+      const uint32_t wsm[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+      for (int b = 0; b < 8; ++b) q2_table(wsm[b], lo[b], hi[b]);
+    } else {
+      const u32x4_t a0 = *reinterpret_cast<const u32x4_t*>(smw + ((jt & 1) * 32 + nt) * 4);
+      const uint32_t wsc[4] = {a0.x, a0.y, a0.z, a0.w};
+#pragma unroll
+      for (int b = 0; b < 8; ++b) q2s_table(wsc[b >> 1], b & 1, lo[b], hi[b]);
+    }
+    uint2* tb = reinterpret_cast<uint2*>(&B.code[wv][0][0]) + jt * 128 + nt;
+#pragma unroll
+    for (int b = 0; b < 8; ++b) tb[16 * b] = make_uint2(lo[b], hi[b]);
+  };
   // fragments of block b = 2 wd + kk (wd, kk compile-time) of the octet in B
   auto dequant = [&](const PfB& B, auto WD, auto KK, uint4 (&bf)[4]) __attribute__((always_inline)) {
     constexpr int wd = decltype(WD)::value, kk = decltype(KK)::value, b = 2 * wd + kk;
-    const uint32_t* smw = reinterpret_cast<const uint32_t*>(&B.sm[wv][0][0]);
+    const uint2* tbl = reinterpret_cast<const uint2*>(&B.code[wv][0][0]);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t w = wd == 0 ? cwo[j].x : (wd == 1 ? cwo[j].y : (wd == 2 ? cwo[j].z : cwo[j].w));
-      uint32_t lo, hi;
-      if constexpr (FMT == kQ2)
-        q2_table(smw[(j >> 1) * 256 + ((j & 1) * 32 + (b >> 2) * 16 + n) * 4 + (b & 3)], lo, hi);
-      else
-        q2s_table(smw[(j >> 1) * 256 + ((j & 1) * 32 + n) * 4 + (b >> 1)], b & 1, lo, hi);
-      bf[j] = q2_frag(w, 8 * kk, lo, hi);
+      const uint2 t = tbl[(j * 8 + b) * 16 + n];
+      bf[j] = q2_frag(w, 8 * kk, t.x, t.y);
     }
   };
   auto mfmas = [&](const PfA& A, int kk, const uint4 (&bf)[4]) __attribute__((always_inline)) {
@@ -417,6 +439,7 @@ __device__ __forceinline__ void pf_tile(const PfArgs& a, PfA& sa0, PfA& sa1, PfA
       uint4 bfn[4];
       if constexpr (wd == 3) {
         load_codes(bn);
+        build_tables(bn);
         dequant(bn, std::integral_constant<int, 0>(), std::integral_constant<int, 0>(), bfn);
       } else {
         dequant(bc, std::integral_constant<int, wd + 1>(), std::integral_constant<int, 0>(), bfn);
@@ -449,6 +472,7 @@ __device__ __forceinline__ void pf_tile(const PfArgs& a, PfA& sa0, PfA& sa1, PfA
   issue_a(sa2, 2);
   wait_vm<3 * kPfDmaA>();  // B(0) has landed (this wave's own weight buffer)
   load_codes(sb0);
+  build_tables(sb0);
   dequant(sb0, std::integral_constant<int, 0>(), std::integral_constant<int, 0>(), bfa);
 #pragma unroll 1
   for (int s = 0; s < nst; s += 8) {  // one exit: the register allocator keeps acc in place
