@@ -360,8 +360,10 @@ __device__ __forceinline__ void pf_tile(const PfArgs& a, PfA& sa0, PfA& sa1, PfA
   // l / 16, row l % 16 into the wave's code region, which load_codes has
   // just read out (the wave's LDS operations run in order).  Layout
   // [tile][block][row] x (lo, hi) words, 4 KB per wave: the 16 rows a
-  // k-step reads are 128 contiguous bytes.
-  auto build_tables = [&](PfB& B) __attribute__((always_inline)) {
+  // k-step reads are 128 contiguous bytes.  Blocks of octet o past the
+  // reduction length get all-zero tables, so their k-steps (an odd last one,
+  // the clamped loads past the end) add exact zeros without a mask.
+  auto build_tables = [&](PfB& B, int o) __attribute__((always_inline)) {
     const int jt = lane >> 4, nt = lane & 15;
     const uint32_t* smw = reinterpret_cast<const uint32_t*>(&B.sm[wv][0][0]) + (jt >> 1) * 256;
     uint32_t lo[8], hi[8];
@@ -379,7 +381,10 @@ __device__ __forceinline__ void pf_tile(const PfArgs& a, PfA& sa0, PfA& sa1, PfA
     }
     uint2* tb = reinterpret_cast<uint2*>(&B.code[wv][0][0]) + jt * 128 + nt;
 #pragma unroll
-    for (int b = 0; b < 8; ++b) tb[16 * b] = make_uint2(lo[b], hi[b]);
+    for (int b = 0; b < 8; ++b) {
+      const bool in = 8 * o + b < nkb;
+      tb[16 * b] = make_uint2(in ? lo[b] : 0u, in ? hi[b] : 0u);
+    }
   };
   // fragments of block b = 2 wd + kk (wd, kk compile-time) of the octet in B
   auto dequant = [&](const PfB& B, auto WD, auto KK, uint4 (&bf)[4]) __attribute__((always_inline)) {
@@ -429,17 +434,11 @@ __device__ __forceinline__ void pf_tile(const PfArgs& a, PfA& sa0, PfA& sa1, PfA
       // k-step 2s (fragments in bfa) || fragments of k-step 2s+1
       dequant(bc, std::integral_constant<int, wd>(), std::integral_constant<int, 1>(), bfb);
       mfmas(A, 0, bfa);
-      {  // odd number of k-steps: the last one is empty (a mask, not a branch)
-        const uint32_t keep = 2 * s + 1 < nkb ? 0xFFFFFFFFu : 0u;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          bfb[j] = make_uint4(bfb[j].x & keep, bfb[j].y & keep, bfb[j].z & keep, bfb[j].w & keep);
-      }
       // k-step 2s+1 (bfb) || fragments of k-step 2s+2 (next stage, maybe next octet)
       uint4 bfn[4];
       if constexpr (wd == 3) {
         load_codes(bn);
-        build_tables(bn);
+        build_tables(bn, s / 4 + 1);
         dequant(bn, std::integral_constant<int, 0>(), std::integral_constant<int, 0>(), bfn);
       } else {
         dequant(bc, std::integral_constant<int, wd + 1>(), std::integral_constant<int, 0>(), bfn);
@@ -472,7 +471,7 @@ __device__ __forceinline__ void pf_tile(const PfArgs& a, PfA& sa0, PfA& sa1, PfA
   issue_a(sa2, 2);
   wait_vm<3 * kPfDmaA>();  // B(0) has landed (this wave's own weight buffer)
   load_codes(sb0);
-  build_tables(sb0);
+  build_tables(sb0, 0);
   dequant(sb0, std::integral_constant<int, 0>(), std::integral_constant<int, 0>(), bfa);
 #pragma unroll 1
   for (int s = 0; s < nst; s += 8) {  // one exit: the register allocator keeps acc in place
