@@ -27,8 +27,10 @@
 // tiles, a whole 256-column octet of packed code words and (scale, min)
 // pairs at a time, double-buffered and issued one octet ahead.  Each wave
 // dequantises its tiles in registers -- per (row, block) a 4-entry bf16
-// table s*u + m and v_perm byte selects, two weights per select -- straight
-// into MFMA B fragments, so every weight is dequantised once per block.
+// table s*u + m, built once per octet into LDS, and v_perm byte selects, two
+// weights per select -- straight into MFMA B fragments, so every weight is
+// dequantised once per block.  Tiles of at most 64 rows skip the MFMAs of
+// their empty row groups.
 #include <type_traits>
 
 #include "route_common.hpp"
