@@ -76,11 +76,17 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
 template <int VPL>
 __device__ __forceinline__ void load_keys(const float* __restrict__ row, int E, int lane,
                                           uint32_t (&key)[VPL]) {
+  // Every load is issued (slots past E read entry 0) and the slot test is a
+  // select afterwards: as a guarded load, each one sat in its own branch with
+  // a wait for it before the next was issued.
+  float v[VPL];
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     const int e = i * 64 + lane;
-    key[i] = e < E ? ord_key(row[e]) : 0u;
+    v[i] = row[e < E ? e : 0];
   }
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) key[i] = i * 64 + lane < E ? ord_key(v[i]) : 0u;
 }
 
 // Exact top-k by a tournament (any k <= 64): each lane keeps its head, its
