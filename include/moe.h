@@ -104,7 +104,7 @@ typedef struct ihipStream_t* moe_stream_t; /* the same type as hipStream_t */
 typedef enum {
   MOE_OK = 0,
   MOE_EINVAL = -1,       /* bad argument: null pointer, bad size or shape, conflict */
-  MOE_EUNSUPPORTED = -2, /* valid request this build does not implement */
+  MOE_EUNSUPPORTED = -2, /* valid request the library does not implement */
   MOE_EHIP = -3,         /* a HIP runtime call or kernel launch failed */
   MOE_ENOSPACE = -4      /* workspace or miss-list capacity too small */
 } moe_status;
