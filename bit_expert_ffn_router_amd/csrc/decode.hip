@@ -652,6 +652,8 @@ __device__ __forceinline__ void gateup_body(const DecodeArgs& a, const DecodeWs&
 // miss list and usage counts).  The gate/up blocks read their entry
 // instead of each routing every token and building the list itself, work
 // that at four tokens took as long as their GEMV and ran on the same SIMDs.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));  // stays in registers
+
 template <int T>
 __global__ __launch_bounds__(2 * kGuThreads) void decode_list_kernel(DecodeArgs a, DecodeWs w) {
   extern __shared__ int32_t s_first[];  // [E]
@@ -677,24 +679,34 @@ __global__ __launch_bounds__(2 * kGuThreads) void decode_list_kernel(DecodeArgs 
     const int tl = tid - kGuThreads, D = a.D;
     const int ppt = (a.x_bf16 ? 1 : 2) * (D / 8);  // pieces per token
     constexpr int kPP = 2 * 4096 / 8 / kGuThreads;  // pieces per thread and token, max
+    // Every piece is requested before any is used: pieces past the token
+    // read its piece 0 and are dropped by a select.  (Read under a bounds
+    // test, each load sat in its own branch behind a wait for the previous
+    // one.)
+    u32x4_t v[T][kPP];
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int j = 0; j < kPP; ++j) {
+        const int i = tl + kGuThreads * j;
+        v[t][j] = reinterpret_cast<const u32x4_t*>(a.x)[(size_t)t * ppt + (i < ppt ? i : 0)];
+      }
     float ss[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       ss[t] = 0.f;
 #pragma unroll
       for (int j = 0; j < kPP; ++j) {
-        const int i = tl + kGuThreads * j;
-        if (i < ppt) {
-          const uint4 v = reinterpret_cast<const uint4*>(a.x)[(size_t)t * ppt + i];
-          const uint32_t qq[4] = {v.x, v.y, v.z, v.w};
+        const uint32_t qq[4] = {v[t][j].x, v[t][j].y, v[t][j].z, v[t][j].w};
+        float q2 = 0.f;
 #pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) {
-            if (a.x_bf16)
-              ss[t] += bf16_lo(qq[e2]) * bf16_lo(qq[e2]) + bf16_hi(qq[e2]) * bf16_hi(qq[e2]);
-            else
-              ss[t] += __uint_as_float(qq[e2]) * __uint_as_float(qq[e2]);
-          }
+        for (int e2 = 0; e2 < 4; ++e2) {
+          if (a.x_bf16)
+            q2 += bf16_lo(qq[e2]) * bf16_lo(qq[e2]) + bf16_hi(qq[e2]) * bf16_hi(qq[e2]);
+          else
+            q2 += __uint_as_float(qq[e2]) * __uint_as_float(qq[e2]);
         }
+        ss[t] += tl + kGuThreads * j < ppt ? q2 : 0.f;
       }
     }
 #pragma unroll
