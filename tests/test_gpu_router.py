@@ -8,7 +8,11 @@ most 64 terms in sequence, so 2^-17 * sum |w xhat| bounds it.  Under the RMS
 rule the GPU's fp32 mean square may put a bf16 input value one unit in the
 last place away from the oracle's fp64 one in rare ties; those tests use
 2^-11 * sum |w xhat|.  Inside the layer, the ids are decided on the GPU's
-fp32 logits on both sides (the oracle routes on the logits the layer wrote).
+fp32 logits on both sides (the oracle routes on the logits the layer wrote);
+in addition, ranking the oracle's own fp64 logits must give the same experts
+for every token whose k-th and (k+1)-th fp64 logits are further apart than
+twice the logit bound (and the same order where every gap among the first
+k + 1 is).
 """
 import numpy as np
 import pytest
@@ -50,6 +54,31 @@ def _check_logits(got, x_seen, w, rms, bound):
     return worst
 
 
+def _check_routing_decision(gpu_logits, x_seen, w, rms, bound, k, min_checked=0.75):
+    """The experts chosen on the GPU's fp32 logits against a ranking of the
+    oracle's fp64 logits (descending, ties to the lower id), per token, where
+    the logit error bound cannot reorder them.  Returns the share checked."""
+    ref = O.router_logits(x_seen, w, rms=rms)
+    xh = O.bf16_to_f64(O.rms_chain(x_seen)) if rms else x_seen
+    mag = np.abs(xh) @ np.abs(O.bf16_to_f64(w)).T
+    gidx, _ = O.route(gpu_logits, k)
+    T, E = ref.shape
+    checked = 0
+    for t in range(T):
+        order = np.lexsort((np.arange(E), -ref[t]))
+        v = ref[t, order]
+        slack = 2.0 * bound * float(np.max(mag[t]))
+        if k < E and not v[k - 1] - v[k] > slack:
+            continue
+        checked += 1
+        assert sorted(gidx[t].tolist()) == sorted(order[:k].tolist()), t
+        if np.all(-np.diff(v[:min(k + 1, E)]) > slack):
+            assert gidx[t].tolist() == order[:k].tolist(), t
+    share = checked / T
+    assert share >= min_checked, "only %d of %d tokens have a clear k-th gap" % (checked, T)
+    return share
+
+
 @pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 64, 131])
 @pytest.mark.parametrize("D,E", [(256, 16), (3072, 512), (512, 300)])
 @pytest.mark.parametrize("x_f32", [False, True])
@@ -62,8 +91,11 @@ def test_router_logits_match_oracle(g, T, D, E, x_f32):
     g.moe.moe_router_logits(shape, T, x_dev, xdt, 0, g.u16_to_dev(w), lg)
     torch.cuda.synchronize()
     got = lg.cpu().numpy().astype(np.float64).reshape(T, E)
-    worst = _check_logits(got, x_small if T <= 4 else x_big, w, False, TIGHT)
-    print("router T=%d D=%d E=%d f32=%s worst=%.3g" % (T, D, E, x_f32, worst))
+    x_seen = x_small if T <= 4 else x_big
+    worst = _check_logits(got, x_seen, w, False, TIGHT)
+    share = _check_routing_decision(got, x_seen, w, False, TIGHT, min(10, E),
+                                    min_checked=0.75 if T >= 64 else 0.0)
+    print("router T=%d D=%d E=%d f32=%s worst=%.3g decided=%.2f" % (T, D, E, x_f32, worst, share))
 
 
 @pytest.mark.parametrize("T", [1, 4, 70])
@@ -117,6 +149,8 @@ def test_tiny_layer_with_router(g, tiny, T):
     got, logits = _layer_with_router(g, w, shape, L, T, g.u16_to_dev(xb), g.moe.MOE_BF16, x64, wr,
                                      out_bf16=False)
     _check_logits(logits.astype(np.float64), x64, wr, False, TIGHT)
+    _check_routing_decision(logits, x64, wr, False, TIGHT, w["top_k"],
+                            min_checked=0.75 if T >= 64 else 0.0)
     ow = OracleWeights(0, 0, D, w["d_ff"], w["d_ff_shared"], E, w["fmt"])
     ref, _, _ = O.layer_forward(x64, logits, w["top_k"], ow, ow.shared)
     err = rel_l2(got, ref)
@@ -147,6 +181,11 @@ def test_full_width_layer_with_router(g, full, T, rms):
         x_dev, xdt, x_seen, flags = g.u16_to_dev(xb), g.moe.MOE_BF16, O.bf16_to_f64(xb), 0
     got, logits = _layer_with_router(g, w, shape, L, T, x_dev, xdt, x_seen, wr, flags=flags)
     _check_logits(logits.astype(np.float64), x_seen, wr, False, RMS_BOUND if rms else TIGHT)
+    # the RMS bound is 16x looser, so about half of the tokens stay undecided
+    share = _check_routing_decision(logits, x_seen, wr, False, RMS_BOUND if rms else TIGHT,
+                                    w["top_k"],
+                                    min_checked=(0.4 if rms else 0.75) if T >= 64 else 0.0)
+    print("routing decided on fp64 logits for %.2f of the tokens" % share)
     ow = OracleWeights(0, 0, D, w["d_ff"], w["d_ff_shared"], E, w["fmt"])
     ref, _, _ = O.layer_forward(x_seen, logits, w["top_k"], ow, ow.shared)
     err = rel_l2(got, ref)
@@ -167,4 +206,6 @@ def test_router_8192_tokens_sampled_rows(g):
     got = lg.cpu().numpy().reshape(T, E).astype(np.float64)
     rows = [0, 63, 64, 4095, 8191] + list(np.random.default_rng(1).choice(T, 11, replace=False))
     _check_logits(got[rows], O.bf16_to_f64(xb[rows]), w, False, TIGHT)
+    _check_routing_decision(got[rows], O.bf16_to_f64(xb[rows]), w, False, TIGHT, 10,
+                            min_checked=0.75)
     assert np.all(np.isfinite(got))

@@ -40,6 +40,12 @@ def test_bf16_rounding_ties_to_even_and_library():
 
 # ---------------------------------------------------------------- dequant
 
+def _finite_f16_bits(rng, n):
+    """Random finite fp16 bit patterns: magnitude 0..0x7BFF (subnormals
+    included) with a random sign bit (0x7C00 and above are inf and NaN)."""
+    return (rng.integers(0, 0x7C00, n) | (rng.integers(0, 2, n) << 15)).astype(np.uint16)
+
+
 def test_dequant_unit_scale_returns_codes():
     c, _, _ = synth.expert_weights(0, 0, 0, 256, 64, synth.FMT_Q2SM)
     one = np.full(256 * 64 // 32, 0x3C00, np.uint16)
@@ -61,7 +67,7 @@ def test_dequant_q2s_brute_force_blocks():
     rng = np.random.default_rng(2)
     R, K = 3, 96
     u = rng.integers(0, 4, R * K).astype(np.uint8)
-    s = rng.integers(0, 0xFBFF, R * K // 32).astype(np.uint16)   # both signs, subnormals
+    s = _finite_f16_bits(rng, R * K // 32)                       # both signs, subnormals
     w = O.dequant_q2s(u, s, R, K)
     for r in range(R):
         for c in range(K):
@@ -70,12 +76,36 @@ def test_dequant_q2s_brute_force_blocks():
             assert w[r, c] == sv * (int(u[r * K + c]) - 2)
 
 
+def test_dequant_q3s_brute_force_blocks():
+    """Q3S: w[r, c] = s[r, c // 32] * q[r, c], checked weight by weight.
+
+    R = 5 rows and K = 128 columns give 4 blocks per row, so a transposed
+    [K/32][rows] scale layout or a tiled (instead of repeated) scale row
+    assigns scales to the wrong weights; the scale bits span both signs,
+    subnormals and the largest finite fp16 values.
+    """
+    rng = np.random.default_rng(4)
+    R, K = 5, 128
+    q = rng.integers(-4, 4, R * K).astype(np.int8)
+    s = _finite_f16_bits(rng, R * K // 32)
+    s[:3] = [0x0001, 0x83FF, 0x7BFF]               # smallest subnormal, negative subnormal, max
+    w = O.dequant_q3s(q.view(np.uint8), s, R, K)
+    assert w.shape == (R, K)
+    for r in range(R):
+        for c in range(K):
+            blk = r * (K // 32) + c // 32
+            sv = float(np.uint16(s[blk]).view(np.float16))
+            assert w[r, c] == sv * int(q[r * K + c])
+    # every code of -4..3 occurs, and the extremes carry their sign
+    assert set(q.tolist()) == set(range(-4, 4))
+
+
 def test_dequant_brute_force_blocks():
     rng = np.random.default_rng(1)
     R, K = 3, 96
     u = rng.integers(0, 4, R * K).astype(np.uint8)
     s = rng.integers(0, 0x7BFF, R * K // 32).astype(np.uint16)
-    m = rng.integers(0, 0xFBFF, R * K // 32).astype(np.uint16)
+    m = _finite_f16_bits(rng, R * K // 32)
     w = O.dequant_q2sm(u, s, m, R, K)
     for r in range(R):
         for c in range(K):

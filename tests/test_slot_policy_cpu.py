@@ -22,6 +22,36 @@ def test_plan_hand_worked():
     assert O.slot_policy_plan([3, 1, 0, 2], [0, 1, -1, -1], [0, 1, -1], 2, 1) == ([], [], [])
 
 
+def test_simulation_schedule_hand_worked():
+    """Six periods of two one-expert tokens, worked by hand.
+
+    Four experts, two slots (expert 0 resident in slot 0, slot 1 spare),
+    one swap per plan, margin 0.  A plan made after period p is copied while
+    period p + 1 runs and installed after it, so it first serves period
+    p + 2: applied one period early, expert 1 would hit in period 1; one
+    period late, it would miss in period 2.  Likewise the victim of the plan
+    after period 3 (expert 1) still hits in period 4, and its admitted
+    expert 2 first hits in period 5.
+
+      period  tokens   hits   counts after  snapshot  plan (admit, evict, slot)
+      0       1, 1     F, F   [0,2,0,0]     same      (1, 0, 1): 2 > 0
+      1       2, 1     F, F   [0,2,1,0]     same      none: 1 > 2 fails
+      2       1, 2     T, F   [0,2,1,0]     same      none
+      3       2, 2     F, F   [0,1,2,0]     same      (2, 1, 0): 2 > 1
+      4       1, 2     T, F   [0,1,2,0]     same      none: 1 > 2 fails
+      5       2, 1     T, F   ...
+    (counts are halved after each snapshot: [0,1,0,0] after periods 0-2,
+    [0,0,1,0] after periods 3-4.)
+    """
+    stream = [[1], [1], [2], [1], [1], [2], [2], [2], [1], [2], [2], [1]]
+    hits, plans, so, es = O.slot_policy_simulate(stream, [0, -1, -1, -1], [0, -1], 2, 1, 0)
+    assert [h[0] for h in hits] == [False, False, False, False, True, False,
+                                    False, False, True, False, True, False]
+    assert [tuple(p) for p in plans] == [([1], [0], [1]), ([], [], []), ([], [], []),
+                                         ([2], [1], [0]), ([], [], []), ([], [], [])]
+    assert so == [-1, -1, 0, -1] and es == [2, -1]
+
+
 def test_simulation_converges_to_the_most_used_experts():
     # a stationary stream with four clearly hotter experts (ten times the
     # rate of the others): the resident set settles on them and stays put
