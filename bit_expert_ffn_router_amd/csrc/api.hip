@@ -155,7 +155,7 @@ size_t moe_workspace_bytes(const moe_shape* shape, int32_t tokens) {
 }
 
 moe_status moe_layer_forward(const moe_shape* shape, int32_t tokens, const void* x,
-                             int32_t x_dtype, uint32_t flags, const float* router_logits,
+                             int32_t x_dtype, uint32_t flags, float* router_logits,
                              const moe_expert_table* table, void* out, int32_t out_dtype,
                              moe_miss* miss, int32_t miss_cap, int32_t* miss_count, void* ws,
                              size_t ws_bytes, moe_stream_t stream) {
@@ -225,7 +225,7 @@ moe_status moe_layer_forward(const moe_shape* shape, int32_t tokens, const void*
     const moe::DecodeWs w = moe::decode_ws_carve(ws, T, a.D, a.F, a.Fs, a.E, a.k);
     if (table->router) {
       moe::RouterArgs r{T, a.D, a.E, x, a.x_bf16, a.rmsnorm, (const uint16_t*)table->router,
-                        const_cast<float*>(router_logits)};
+                        router_logits};
       moe_status rs = hip_status(moe::launch_router(r, (hipStream_t)stream), "router launch");
       if (rs != MOE_OK) return rs;
     }
@@ -327,12 +327,9 @@ moe_status moe_slot_table_commit(moe_slot_table* t, int32_t n, const int32_t* sl
     if (evict && evict[i] >= 0) edits.push_back({t->host_slot_of[evict[i]], -1, evict[i], 0});
     edits.push_back({slots[i], experts[i], -1, 0});
   }
-  // Evictions and installs touch distinct slots and experts, so chunking the
-  // batch keeps the result of applying it at once.
-  for (size_t i0 = 0; i0 < edits.size(); i0 += moe::kSlotEditsPerLaunch) {
-    const int m = (int)std::min<size_t>(edits.size() - i0, moe::kSlotEditsPerLaunch);
-    hipError_t e = moe::launch_slot_edits(t->slot_of, t->expert_of_slot, edits.data() + i0, m,
-                                          (hipStream_t)stream);
+  {
+    hipError_t e = moe::launch_slot_edits(t->slot_of, t->expert_of_slot, edits.data(),
+                                          (int)edits.size(), (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e, "slot edit launch");
   }
   for (const auto& ed : edits) {
@@ -531,9 +528,8 @@ moe_status moe_slot_table_update(moe_slot_table* t, int32_t n, const int32_t* sl
       if (e != hipSuccess) return hip_status(e, "slot copy");
     }
   }
-  for (int i0 = 0; i0 < n; i0 += moe::kSlotEditsPerLaunch) {
-    const int m = n - i0 < moe::kSlotEditsPerLaunch ? n - i0 : moe::kSlotEditsPerLaunch;
-    hipError_t e = moe::launch_slot_edits(t->slot_of, t->expert_of_slot, edits.data() + i0, m,
+  {
+    hipError_t e = moe::launch_slot_edits(t->slot_of, t->expert_of_slot, edits.data(), n,
                                           (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e, "slot edit launch");
   }

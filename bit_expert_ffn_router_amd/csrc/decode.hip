@@ -866,21 +866,9 @@ __global__ __launch_bounds__(1024) void decode_down_kernel(DecodeArgs a, DecodeW
   }
 }
 
-// ----------------------------------------------------------------------------
-// Raise a kernel's dynamic-LDS limit when a launch needs more than the
-// default 64 KiB (gfx950 has 160 KiB per CU).  `cur` caches the value set.
-template <typename K>
-static hipError_t allow_lds(K kernel, size_t bytes, size_t& cur) {
-  if (bytes <= 65536 || bytes <= cur) return hipSuccess;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-  if (e == hipSuccess) cur = bytes;
-  return e;
-}
-
 template <int T, int FMT, int XM>
 static hipError_t launch_decode_x(const DecodeArgs& a, const DecodeWs& w, hipStream_t st) {
-  static size_t lds_gu = 0, lds_dn = 0;
+  static std::atomic<size_t> lds_gu[kMaxDevices], lds_dn[kMaxDevices];  // per device (allow_lds)
   const int D8 = a.D / 8, nbD = a.D / 32;
   const int D8p = D8 + (T > 1 ? 1 : 0);  // padded token rows (see gateup_body)
   const size_t lds = (size_t)T * D8p * 16 * (XM == kXF32 ? 2 : 1) + (size_t)T * nbD * 8;

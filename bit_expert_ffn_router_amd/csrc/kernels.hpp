@@ -3,6 +3,8 @@
 
 #include <hip/hip_ext.h>
 
+#include <atomic>
+
 #include "common.hpp"
 
 namespace moe {
@@ -49,6 +51,29 @@ hipError_t launch_timed(void (*kernel)(P...), dim3 grid, dim3 block, uint32_t ld
   return launch_timed_by(kernel_timer(), kernel, grid, block, lds, st, args...);
 }
 
+// ---------------------------------------------------------------- LDS limit
+// Raise `kernel`'s dynamic-LDS limit on the current device to at least
+// `bytes` when a launch needs more than the default 64 KiB (gfx950 has
+// 160 KiB per CU).  `cur` remembers, per device, the largest value set;
+// two threads that race on a first call may both set it, which is harmless.
+constexpr int kMaxDevices = 64;
+template <typename K>
+hipError_t allow_lds(K kernel, size_t bytes, std::atomic<size_t> (&cur)[kMaxDevices]) {
+  if (bytes <= 65536) return hipSuccess;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  if (bytes <= cur[dev].load(std::memory_order_acquire)) return hipSuccess;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e != hipSuccess) return e;
+  size_t v = cur[dev].load(std::memory_order_relaxed);
+  while (v < bytes && !cur[dev].compare_exchange_weak(v, bytes, std::memory_order_acq_rel)) {
+  }
+  return hipSuccess;
+}
+
 // ---------------------------------------------------------------- packing
 hipError_t launch_pack(int fmt, int D, int F, int n, const void* codes, const uint16_t* scale,
                        const uint16_t* mins, void* dst, size_t dst_stride, hipStream_t st);
@@ -93,7 +118,7 @@ struct DecodeArgs {
   const void* x;
   int x_bf16;       // 1: x is bf16, 0: fp32
   int rmsnorm;      // MOE_FLAG_RMSNORM_INPUT
-  const float* logits;
+  const float* logits;  // read by the routing (written first by the router, if any)
   const uint8_t* routed;
   size_t stride;
   const int32_t* slot_of;  // NULL = all resident
@@ -139,7 +164,7 @@ struct PrefillArgs {
   const void* x;
   int x_bf16;
   int rmsnorm;
-  const float* logits;
+  float* logits;           // input, or the router's output when `router` is set
   const uint8_t* routed;
   size_t stride;
   const uint8_t* shared;
@@ -155,6 +180,8 @@ struct SlotEdit {
   int32_t slot, expert, old_expert, pad;
 };
 constexpr int kSlotEditsPerLaunch = 32;
+// Applies all n edits (any n): the evictions of every edit first, then the
+// installs, in launches of kSlotEditsPerLaunch edits.
 hipError_t launch_slot_edits(int32_t* slot_of, int32_t* expert_of_slot, const SlotEdit* edits,
                              int n, hipStream_t st);
 hipError_t launch_counts_halve(uint32_t* counts, int n, hipStream_t st);

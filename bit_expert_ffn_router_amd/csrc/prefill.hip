@@ -632,7 +632,7 @@ hipError_t launch_prefill(const PrefillArgs& pa, void* ws, hipStream_t st) {
     xb = w.xb;
   }
   if (pa.router) {  // logits of the activations the experts see (bf16, after the RMS rule)
-    RouterArgs r{T, D, E, xb, 1, 0, pa.router, const_cast<float*>(pa.logits)};
+    RouterArgs r{T, D, E, xb, 1, 0, pa.router, pa.logits};
     if ((e = launch_router(r, st)) != hipSuccess) return e;
   }
   if ((e = launch_route(pa.logits, T, E, k, w.idx, w.gate, st)) != hipSuccess) return e;

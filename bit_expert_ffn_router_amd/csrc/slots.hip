@@ -12,14 +12,18 @@ struct SlotEditBatch {
   SlotEdit e[kSlotEditsPerLaunch];
 };
 
-// One thread per edit.  Evictions are applied before installs (a slot's old
-// expert may be installed elsewhere by the same batch).
+// One thread per edit.  Phase 0 evicts: the slot's previous occupant stops
+// being resident.  Phase 1 installs: the slot takes its new expert (or
+// becomes empty).  The host runs phase 0 over every batch of a call before
+// phase 1 over any, so an expert moved from a slot that a later batch edits
+// keeps its new slot.
 __global__ void slot_edit_kernel(int32_t* slot_of, int32_t* expert_of_slot, SlotEditBatch b,
-                                 int n) {
+                                 int n, int phase) {
   const int i = threadIdx.x;
-  if (i < n && b.e[i].old_expert >= 0) slot_of[b.e[i].old_expert] = -1;
-  __syncthreads();
-  if (i < n) {
+  if (i >= n) return;
+  if (phase == 0) {
+    if (b.e[i].old_expert >= 0) slot_of[b.e[i].old_expert] = -1;
+  } else {
     expert_of_slot[b.e[i].slot] = b.e[i].expert;
     if (b.e[i].expert >= 0) slot_of[b.e[i].expert] = b.e[i].slot;
   }
@@ -44,10 +48,16 @@ __global__ void slot_init_kernel(int32_t* slot_of, int E, int32_t* expert_of_slo
 
 hipError_t launch_slot_edits(int32_t* slot_of, int32_t* expert_of_slot, const SlotEdit* edits,
                              int n, hipStream_t st) {
-  SlotEditBatch b;
-  for (int i = 0; i < n; ++i) b.e[i] = edits[i];
-  slot_edit_kernel<<<1, kSlotEditsPerLaunch, 0, st>>>(slot_of, expert_of_slot, b, n);
-  return hipGetLastError();
+  for (int phase = 0; phase < 2; ++phase)
+    for (int i0 = 0; i0 < n; i0 += kSlotEditsPerLaunch) {
+      const int m = n - i0 < kSlotEditsPerLaunch ? n - i0 : kSlotEditsPerLaunch;
+      SlotEditBatch b;
+      for (int i = 0; i < m; ++i) b.e[i] = edits[i0 + i];
+      slot_edit_kernel<<<1, kSlotEditsPerLaunch, 0, st>>>(slot_of, expert_of_slot, b, m, phase);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  return hipSuccess;
 }
 
 hipError_t launch_slot_init(int32_t* slot_of, int E, int32_t* expert_of_slot, int S,

@@ -25,8 +25,14 @@
  * Conventions for every entry point:
  *   - Pointers named "device" are HIP device (HBM) addresses; "host" are
  *     CPU addresses.  The caller allocates and frees every buffer, including
- *     the workspace; the library allocates no memory and keeps no state
- *     between calls (moe_last_error's per-thread message aside).
+ *     the workspace.  The GPU entry points allocate no device memory and
+ *     keep no state between calls, except: moe_last_error's per-thread
+ *     message; the per-thread event pairs of the profiling aids; and, per
+ *     device, the largest dynamic-LDS limit already set on a kernel (set
+ *     once with hipFuncSetAttribute, thread-safe).  The host half of the
+ *     slot-mode layer is different: moe_host_pool_create starts threads,
+ *     and moe_host_miss_ffn allocates and frees its own host scratch (the
+ *     rearranged activations and the h rows) within each call.
  *   - All device work is enqueued on the caller's stream (NULL = the null
  *     stream); nothing waits on the host.  Device-resident results (outputs,
  *     miss lists, counts) are valid after the caller synchronises the stream.
@@ -194,10 +200,23 @@ moe_status moe_unpack_weights(const moe_shape* shape, int32_t n, int32_t d_ff,
                               void* codes, uint16_t* scale, uint16_t* min,
                               moe_stream_t stream);
 
-/* Workspace bytes moe_layer_forward needs for `tokens` tokens. */
+/* Workspace bytes moe_layer_forward needs for `tokens` tokens (device
+ * scratch of the steps the pages' layer runs: the routing of each token,
+ * the list of the distinct selected experts and their h rows for decode;
+ * the routing, the stable permutation and the H and Y rows of the grouped
+ * GEMMs for prefill, [AF] sections "1250 亿参数，每个词只用得上 2%" and
+ * "等最久的，是它读完你的代码").  0 for an invalid shape or tokens < 0. */
 size_t moe_workspace_bytes(const moe_shape* shape, int32_t tokens);
 
-/* One MoE FFN layer.
+/* One MoE FFN layer: each token's input goes to the 10 (top_k) experts its
+ * router logits rank highest plus the shared expert, and their outputs are
+ * summed with the renormalised gates ([AF] section "1250 亿参数，每个词只
+ * 用得上 2%"; [SL] section "12GB 显存装下 1250 亿参数"); decode (1 token,
+ * or 1 + 3 drafts verified together, [AF] section "命中率七成，代价是答案会
+ * 变") streams each selected expert's weights once ([JD] section "为什么从
+ * 18t/s 变成 60-90t/s"); prefill runs chunks of up to 8192 tokens ([AF]
+ * section "等最久的，是它读完你的代码").  The formula is the one in the
+ * preamble of this header.
  *   tokens:        T >= 0 (T == 0: nothing is launched, *miss_count is not
  *                  touched).
  *   x:             device [T][d_model], dtype x_dtype (MOE_BF16 or MOE_F32),
@@ -231,7 +250,7 @@ size_t moe_workspace_bytes(const moe_shape* shape, int32_t tokens);
  * Results are deterministic: the same inputs give the same output bits. */
 moe_status moe_layer_forward(const moe_shape* shape, int32_t tokens,
                              const void* x, int32_t x_dtype, uint32_t flags,
-                             const float* router_logits, const moe_expert_table* table,
+                             float* router_logits, const moe_expert_table* table,
                              void* out, int32_t out_dtype,
                              moe_miss* miss, int32_t miss_cap, int32_t* miss_count,
                              void* ws, size_t ws_bytes, moe_stream_t stream);
@@ -389,12 +408,21 @@ moe_status moe_slot_table_commit(moe_slot_table* t, int32_t n, const int32_t* sl
                                  moe_stream_t stream);
 
 
-/* Routing alone (the first step of the layer): device fp32 logits [T][E] ->
- * device int32 idx [T][k] and fp32 gates [T][k], as defined above. */
+/* Routing alone (the first step of the layer; each token keeps the k
+ * experts its router ranks highest, [AF] section "1250 亿参数，每个词只用得
+ * 上 2%"; the pages give no gate formula, the reading is in the preamble):
+ * device fp32 logits [T][E] (finite) -> device int32 idx [T][k] (descending
+ * logit, ties to the lower id, -0.0 == +0.0) and fp32 gates [T][k] (softmax
+ * over the k selected logits).  Rejects T < 0, E outside 1..2048, k outside
+ * 1..min(32, E) and NULL buffers (T > 0) with MOE_EINVAL before any launch.
+ * The caller owns all three buffers. */
 moe_status moe_route(const float* logits, int32_t tokens, int32_t n_experts, int32_t top_k,
                      int32_t* idx, float* gate, moe_stream_t stream);
 
-/* Stable token-to-expert permutation of routed pairs p = t*k + j:
+/* Stable token-to-expert permutation of routed pairs p = t*k + j: the step
+ * that groups a prefill chunk's rows by expert so that each expert's weights
+ * are read once for all its tokens ([AF] section "等最久的，是它读完你的代码";
+ * the pages give no algorithm: histogram, prefix scans, stable scatter):
  *   offsets [E+1]: offsets[e] = number of pairs routed to experts < e;
  *   sorted_pairs [T*k]: pair ids grouped by expert, ascending within a group;
  *   inv [T*k]: inv[p] = position of p in sorted_pairs.
@@ -425,7 +453,7 @@ moe_status moe_set_router_timer(void* before, void* after);
 const char* moe_last_error(void);
 
 /* ABI version of this header. */
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 int32_t moe_abi_version(void);
 
 #ifdef __cplusplus

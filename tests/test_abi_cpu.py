@@ -35,7 +35,29 @@ def test_every_header_function_is_exported():
     lib = ctypes.CDLL(moe.LIB_PATH)
     for n in names:
         getattr(lib, n)
-    assert moe.moe_abi_version() == 3
+    assert moe.moe_abi_version() == 4
+
+
+def test_header_compiles_and_router_logits_is_writable(tmp_path):
+    """moe.h is plain C (no HIP types needed), and moe_layer_forward takes a
+    writable logits pointer: it writes the router's logits there when the
+    table carries a router, so the signature must not promise const."""
+    import os
+    from helpers import ROOT
+    inc = os.path.join(ROOT, "include")
+    c_src = tmp_path / "h.c"
+    c_src.write_text('#include "moe.h"\nint main(void) { return moe_abi_version() == MOE_ABI_VERSION ? 0 : 1; }\n')
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-I", inc, str(c_src)],
+                   check=True)
+    cc_src = tmp_path / "h.cc"
+    cc_src.write_text(
+        '#include "moe.h"\n'
+        'moe_status (*f)(const moe_shape*, int32_t, const void*, int32_t, uint32_t, float*,\n'
+        '                const moe_expert_table*, void*, int32_t, moe_miss*, int32_t, int32_t*,\n'
+        '                void*, size_t, moe_stream_t) = moe_layer_forward;\n'
+        'int main() { return f ? 0 : 1; }\n')
+    subprocess.run(["g++", "-std=c++17", "-Wall", "-Werror", "-fsyntax-only", "-I", inc,
+                    str(cc_src)], check=True)
 
 
 def test_packed_bytes_formula():

@@ -223,3 +223,27 @@ def test_slot_table_update_moves_and_evicts(g, q3_layer):
     assert np.array_equal(so, hs) and np.array_equal(eos.cpu().numpy(), he)
     assert np.array_equal(storage[3 * L.stride:3 * L.stride + 4096].cpu().numpy(),
                           L.routed[9 * L.stride:9 * L.stride + 4096].cpu().numpy())
+
+
+def test_slot_table_update_many_edits_across_launches(g, q3_layer):
+    """An update with more edits than one launch carries (32): edit 0 moves
+    expert 139 from slot 39 into slot 0, and edit 39 -- in the second launch --
+    empties slot 39.  The move must survive: every eviction of the call is
+    applied before any install, so the device maps equal the host mirror."""
+    import torch
+    w, shape, L = q3_layer
+    moe = g.moe
+    t, slot_of, eos, storage, hs, he = _slot_storage(g, L, shape, list(range(100, 140)))
+    slots = list(range(40))
+    experts = [139] + [200 + i for i in range(1, 39)] + [-1]
+    src = [None if e < 0 else L.routed.data_ptr() + e * L.stride for e in experts]
+    moe.moe_slot_table_update(t, slots, experts, src)
+    torch.cuda.synchronize()
+    so, es = slot_of.cpu().numpy(), eos.cpu().numpy()
+    assert np.array_equal(so, hs) and np.array_equal(es, he)
+    assert so[139] == 0 and es[39] == -1
+    assert all(so[e] == -1 for e in range(100, 139))
+    assert all(so[200 + i] == i for i in range(1, 39))
+    assert es.tolist() == [139] + [200 + i for i in range(1, 39)] + [-1]
+    assert np.array_equal(storage[0:4096].cpu().numpy(),
+                          L.routed[139 * L.stride:139 * L.stride + 4096].cpu().numpy())
