@@ -20,7 +20,8 @@ __all__ = [
     "MOE_Q2SM32", "MOE_Q3S32", "MOE_Q2S32", "MOE_F32", "MOE_BF16", "MOE_FLAG_RMSNORM_INPUT",
     "MoeError", "MoeShape", "MoeExpertTable", "MoeMiss", "MoeSlotTable",
     "moe_packed_expert_bytes", "moe_pack_weights", "moe_unpack_weights",
-    "moe_workspace_bytes", "moe_layer_forward", "moe_slot_table_init",
+    "moe_workspace_bytes", "moe_layer_forward", "moe_layer_forward_noalloc",
+    "moe_slot_table_init",
     "moe_slot_table_update", "moe_route", "moe_router_logits", "moe_permute_workspace_bytes",
     "moe_permute",
     "moe_last_error", "moe_abi_version", "moe_set_kernel_timer", "moe_set_router_timer",
@@ -97,6 +98,8 @@ _sigs = {
     "moe_workspace_bytes": (_Z, [ctypes.POINTER(MoeShape), _I]),
     "moe_layer_forward": (_I, [ctypes.POINTER(MoeShape), _I, _P, _I, ctypes.c_uint32, _P,
                                ctypes.POINTER(MoeExpertTable), _P, _I, _P, _I, _P, _P, _Z, _P]),
+    "moe_layer_forward_noalloc": (_I, [ctypes.POINTER(MoeShape), _I, _P, _I, ctypes.c_uint32, _P,
+                                       ctypes.POINTER(MoeExpertTable), _P, _I, _P, _I, _P, _P]),
     "moe_slot_table_init": (_I, [ctypes.POINTER(MoeSlotTable), _P]),
     "moe_slot_table_update": (_I, [ctypes.POINTER(MoeSlotTable), _I, _P, _P, _P, _P]),
     "moe_route": (_I, [_P, _I, _I, _I, _P, _P, _P]),
@@ -177,6 +180,14 @@ def moe_layer_forward(shape, tokens, x, x_dtype, flags, router_logits, table, ou
                                   _ptr(router_logits), ctypes.byref(table), _ptr(out), out_dtype,
                                   _ptr(miss), miss_cap, _ptr(miss_count), _ptr(ws), ws_bytes,
                                   _stream(stream)))
+
+
+def moe_layer_forward_noalloc(shape, tokens, x, x_dtype, flags, router_logits, table, out,
+                              out_dtype, miss, miss_cap, miss_count, stream=None):
+    _check(_lib.moe_layer_forward_noalloc(ctypes.byref(shape), tokens, _ptr(x), x_dtype, flags,
+                                          _ptr(router_logits), ctypes.byref(table), _ptr(out),
+                                          out_dtype, _ptr(miss), miss_cap, _ptr(miss_count),
+                                          _stream(stream)))
 
 
 def moe_slot_table_init(table: MoeSlotTable, stream=None):

@@ -154,11 +154,17 @@ size_t moe_workspace_bytes(const moe_shape* shape, int32_t tokens) {
   return forward_ws_bytes(shape, tokens);
 }
 
-moe_status moe_layer_forward(const moe_shape* shape, int32_t tokens, const void* x,
-                             int32_t x_dtype, uint32_t flags, float* router_logits,
-                             const moe_expert_table* table, void* out, int32_t out_dtype,
-                             moe_miss* miss, int32_t miss_cap, int32_t* miss_count, void* ws,
-                             size_t ws_bytes, moe_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The layer call behind both entry points.  ws == nullptr with noalloc:
+// the decode path's workspace is the library's per-device static scratch.
+moe_status layer_forward_impl(const moe_shape* shape, int32_t tokens, const void* x,
+                              int32_t x_dtype, uint32_t flags, float* router_logits,
+                              const moe_expert_table* table, void* out, int32_t out_dtype,
+                              moe_miss* miss, int32_t miss_cap, int32_t* miss_count, void* ws,
+                              size_t ws_bytes, bool noalloc, moe_stream_t stream) {
   moe_status s = check_shape(shape);
   if (s != MOE_OK) return s;
   const int T = tokens;
@@ -190,12 +196,25 @@ moe_status moe_layer_forward(const moe_shape* shape, int32_t tokens, const void*
       return fail(MOE_ENOSPACE, "miss_cap %d < tokens*top_k = %lld", (int)miss_cap,
                   (long long)T * shape->top_k);
   }
+  if (noalloc && !use_decode_path(T))
+    return fail(MOE_EUNSUPPORTED,
+                "moe_layer_forward_noalloc runs the decode path only (tokens <= %d), got %d",
+                moe::kDecodeMaxT, T);
   if (T == 0) return ok();
-  if (!x || !router_logits || !out || !ws) return fail(MOE_EINVAL, "x, router_logits, out, ws are required");
-  if (!aligned256(ws)) return fail(MOE_EINVAL, "ws must be 256-byte aligned");
+  if (!x || !router_logits || !out) return fail(MOE_EINVAL, "x, router_logits and out are required");
   if (((uintptr_t)x & 15u) || ((uintptr_t)router_logits & 3u) || ((uintptr_t)out & 15u))
     return fail(MOE_EINVAL, "x and out must be 16-byte aligned, router_logits 4-byte aligned");
   const size_t need_ws = forward_ws_bytes(shape, T);
+  if (noalloc) {
+    if (need_ws > moe::kNoAllocScratchBytes)
+      return fail(MOE_ENOSPACE, "workspace of %zu bytes exceeds the static scratch (%zu bytes)",
+                  need_ws, moe::kNoAllocScratchBytes);
+    moe_status ss = hip_status(moe::noalloc_scratch(&ws), "static scratch address");
+    if (ss != MOE_OK) return ss;
+    ws_bytes = moe::kNoAllocScratchBytes;
+  }
+  if (!ws) return fail(MOE_EINVAL, "ws is required");
+  if (!aligned256(ws)) return fail(MOE_EINVAL, "ws must be 256-byte aligned");
   if (ws_bytes < need_ws) return fail(MOE_ENOSPACE, "ws_bytes %zu < %zu", ws_bytes, need_ws);
   if (use_decode_path(T)) {
     if (shape->d_model > 4096 || shape->d_ff > 512 || shape->d_ff_shared > 512)
@@ -252,6 +271,28 @@ moe_status moe_layer_forward(const moe_shape* shape, int32_t tokens, const void*
   a.out_bf16 = out_dtype == MOE_BF16;
   a.router = (const uint16_t*)table->router;
   return hip_status(moe::launch_prefill(a, ws, (hipStream_t)stream), "prefill launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_layer_forward(const moe_shape* shape, int32_t tokens, const void* x,
+                             int32_t x_dtype, uint32_t flags, float* router_logits,
+                             const moe_expert_table* table, void* out, int32_t out_dtype,
+                             moe_miss* miss, int32_t miss_cap, int32_t* miss_count, void* ws,
+                             size_t ws_bytes, moe_stream_t stream) {
+  return layer_forward_impl(shape, tokens, x, x_dtype, flags, router_logits, table, out, out_dtype,
+                            miss, miss_cap, miss_count, ws, ws_bytes, false, stream);
+}
+
+moe_status moe_layer_forward_noalloc(const moe_shape* shape, int32_t tokens, const void* x,
+                                     int32_t x_dtype, uint32_t flags, float* router_logits,
+                                     const moe_expert_table* table, void* out, int32_t out_dtype,
+                                     moe_miss* miss, int32_t miss_cap, int32_t* miss_count,
+                                     moe_stream_t stream) {
+  return layer_forward_impl(shape, tokens, x, x_dtype, flags, router_logits, table, out, out_dtype,
+                            miss, miss_cap, miss_count, nullptr, 0, true, stream);
 }
 
 // Validation shared by stage and commit: `slots` name distinct empty slots,

@@ -132,6 +132,13 @@ struct DecodeArgs {
 };
 
 size_t decode_ws_bytes(int T, int D, int F, int Fs, int E, int k);
+
+// Static per-device scratch of moe_layer_forward_noalloc (noalloc.hip): the
+// decode workspace of the largest decode request (4 tokens, top-32, d_ff
+// 512) is about 1.2 MiB.
+constexpr size_t kNoAllocScratchBytes = (size_t)2 << 20;
+// Device address of the current device's scratch (looked up once per device).
+hipError_t noalloc_scratch(void** ptr);
 DecodeWs decode_ws_carve(void* ws, int T, int D, int F, int Fs, int E, int k);
 hipError_t launch_decode(const DecodeArgs& a, const DecodeWs& w, hipStream_t st);
 

@@ -255,6 +255,28 @@ moe_status moe_layer_forward(const moe_shape* shape, int32_t tokens,
                              moe_miss* miss, int32_t miss_cap, int32_t* miss_count,
                              void* ws, size_t ws_bytes, moe_stream_t stream);
 
+/* moe_layer_forward without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, results and errors as
+ * moe_layer_forward (the same kernels run), minus ws and ws_bytes.
+ *   Decode path only: tokens <= 4; larger tokens return MOE_EUNSUPPORTED
+ *   before any launch.  Its workspace is a fixed device array of 2 MiB
+ *   inside the library (one per GPU, held until the process ends), enough
+ *   for every decode request moe_layer_forward accepts (at most about
+ *   1.2 MiB: 4 tokens, top-32, d_ff 512); a request needing more returns
+ *   MOE_ENOSPACE.  Allocates nothing: on its first call on a device it looks
+ *   up that device's copy of the array (hipGetSymbolAddress).
+ *   Every call on one GPU shares that array and finds the last call's
+ *   contents there (nothing needs to start cleared): calls that overlap in
+ *   time on one GPU -- on different streams or from different threads --
+ *   race, and must be ordered by the caller (e.g. one stream). */
+moe_status moe_layer_forward_noalloc(const moe_shape* shape, int32_t tokens,
+                                     const void* x, int32_t x_dtype, uint32_t flags,
+                                     float* router_logits, const moe_expert_table* table,
+                                     void* out, int32_t out_dtype,
+                                     moe_miss* miss, int32_t miss_cap, int32_t* miss_count,
+                                     moe_stream_t stream);
+
 /* Host half of the slot-mode layer.  The pages compute the experts that are
  * not on the GPU with the CPU, at the same time as the GPU computes its own,
  * and add both into the same layer ([AF] section "命中率七成，代价是答案会
