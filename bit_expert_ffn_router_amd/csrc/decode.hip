@@ -46,6 +46,10 @@ constexpr int kGuThreads = 64 * kGuWaves;
 constexpr int kDnWaves = 16;       // down block: waves share the expert list
 constexpr int kMaxOctPerWave = 8;  // d_model <= 4096 on the decode path (16 octets / 2 halves)
 constexpr int kMaxDecodeFOct = 2;  // d_ff, d_ff_shared <= 512 on the decode path
+// Down-record prefetch loads per gate/up thread (one 64-byte line each):
+// 32 KiB per block, a block's whole share up to d_model 4096 in every
+// format (at most 28 KiB).
+constexpr int kDnPrefetchPerThread = 2;
 
 // Activation modes of the gate/up kernel.
 constexpr int kXBf16 = 0;  // bf16 input, used as is
@@ -242,23 +246,30 @@ __device__ __forceinline__ void build_list(const DecodeArgs& a, const DecodeWs& 
 // Block parameter helpers.  Q2SM: the two 16-byte parameter loads of a record
 // row hold (scale, min) for blocks 0..3 and 4..7.  Q3S and Q2S: one 16-byte
 // load holds the 8 scales.
-__device__ __forceinline__ uint32_t sel4(const uint4& v, int i) {
+__device__ __forceinline__ uint32_t sel4(const uint4 v, int i) {
+  // word i of v by three byte permutes whose selectors depend only on i
+  // (loop-invariant per lane): with a lane-dependent index a chain of
+  // compares became divergent branches, and a select could become a load
+  // from a stack copy of v
+  const uint32_t s1 = (i & 1) ? 0x07060504u : 0x03020100u;
+  const uint32_t s2 = (i & 2) ? 0x07060504u : 0x03020100u;
+  const uint32_t lo = __builtin_amdgcn_perm(v.y, v.x, s1), hi = __builtin_amdgcn_perm(v.w, v.z, s1);
+  return __builtin_amdgcn_perm(hi, lo, s2);
+}
+// Word i of v for an index known at compile time (after unrolling): a plain
+// register pick.
+__device__ __forceinline__ uint32_t sel4c(const uint4& v, int i) {
   return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
 }
 template <int FMT>
 __device__ __forceinline__ float blk_scale(const uint4& pa, const uint4& pb, int beta) {
   if (FMT == kQ2) {
-    const uint32_t v = beta < 4 ? sel4(pa, beta) : sel4(pb, beta - 4);
+    const uint32_t v = beta < 4 ? sel4c(pa, beta) : sel4c(pb, beta - 4);
     return f16_to_f32((uint16_t)(v & 0xFFFFu));
   } else {
-    const uint32_t v = sel4(pa, beta >> 1);
+    const uint32_t v = sel4c(pa, beta >> 1);
     return f16_to_f32((uint16_t)((beta & 1) ? (v >> 16) : (v & 0xFFFFu)));
   }
-}
-template <int FMT>
-__device__ __forceinline__ float blk_min(const uint4& pa, const uint4& pb, int beta) {
-  const uint32_t v = beta < 4 ? sel4(pa, beta) : sel4(pb, beta - 4);
-  return f16_to_f32((uint16_t)(v >> 16));
 }
 
 // One record (16 rows x 8 blocks) of one wave: MFMA over the 8 blocks with
@@ -392,6 +403,82 @@ __device__ __forceinline__ float oct_sum(float v) {
 }
 
 // ----------------------------------------------------------------------------
+// Direct global -> LDS load: lane l's 16 bytes land at lds + 16 l (`lds` the
+// same for the whole wave); counts in vmcnt.
+typedef __attribute__((address_space(3))) void dn_lds_t;
+__device__ __forceinline__ void dn_dma16(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds(src, (dn_lds_t*)lds, 16, 0, 0);
+}
+// Wait until no vector-memory operation of this wave is in flight.
+__device__ __forceinline__ void dn_wait_vm0() {
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0); expcnt, lgkmcnt not waited
+}
+// Workgroup barrier over LDS: this wave's LDS stores complete (lgkmcnt(0)),
+// then s_barrier, without the release/acquire fences of __syncthreads, which
+// count direct global -> LDS loads as LDS writes and would drain the down-
+// record prefetch in flight.  The compiler barriers keep LDS accesses on
+// their side of it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // lgkmcnt(0) only
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Cache warm-up of an expert's down-projection records for decode_down.
+// Down block rt (16 output rows) runs on the XCD of its block index modulo
+// 8: every launch sends block i to XCD (i + c) mod 8 with the same c for
+// all launches of a stream (measured: c = 0 for launches, c = 7 inside a
+// graph replay), so blocks of two launches whose indices agree modulo 8
+// share an XCD and its L2.  The gate/up block vb of expert u therefore reads
+// the records of the down rows rt with rt = vb (mod 8), shared out among the
+// expert's gate/up blocks of that residue class: one 4-byte load per 64-byte
+// line, which leaves the line in that XCD's L2 for the down kernel launched
+// next.  The loaded words are only kept alive to the end of the block (see
+// keep_alive), so nothing waits for them before then.  Only where the bytes
+// are cached depends on this placement, never a result.
+struct DnPrefetch {
+  uint32_t v[kDnPrefetchPerThread];
+};
+__device__ __forceinline__ DnPrefetch prefetch_down_rows(const uint8_t* expert, int D, int Fu,
+                                                         int fmt_rec, size_t down_off, int vb,
+                                                         int base, int ngroups, int tid,
+                                                         int threads) {
+  DnPrefetch p;
+  const int c = vb & 7;
+  const int g = vb - base;                  // this block's 16-row group of the expert
+  const int g0 = (c - base % 8 + 8) % 8;    // first group of residue class c
+  const int nG = ngroups > g0 ? (ngroups - g0 + 7) / 8 : 0;
+  const int j = (g - g0) / 8;               // this block's index in its class
+  const int nRt = D / 16, nR = nRt > c ? (nRt - c + 7) / 8 : 0;
+  const int mine = nG > 0 && nR > j ? (nR - j + nG - 1) / nG : 0;  // row groups j, j + nG, ...
+  const int oF = octets(Fu);
+  const int lines = oF * fmt_rec / 64;      // 64-byte lines of one row group's records
+  const int total = mine * lines;
+  // A fixed number of loads per thread (so the compiler can count them);
+  // lines past the block's share repeat its last line, a share larger than
+  // kDnPrefetchPerThread * threads lines is cut (this is only a warm-up),
+  // and a block without a share reads its own expert's first down line.
+  const uint32_t* dn = reinterpret_cast<const uint32_t*>(expert + down_off);
+#pragma unroll
+  for (int r = 0; r < kDnPrefetchPerThread; ++r) {
+    int q = tid + threads * r;
+    q = total == 0 ? 0 : (q < total ? q : total - 1);
+    const int rt = total == 0 ? 0 : c + 8 * (j + nG * (q / lines));
+    p.v[r] = dn[((size_t)rt * oF * fmt_rec + 64 * (q % lines)) / 4];
+  }
+  return p;
+}
+// Hold the prefetched words until here, so their loads are waited for at
+// the end of the block and nowhere earlier.
+__device__ __forceinline__ void keep_alive(const DnPrefetch& p) {
+#pragma unroll
+  for (int r = 0; r < kDnPrefetchPerThread; ++r) asm volatile("" ::"v"(p.v[r]));
+}
+
+// ----------------------------------------------------------------------------
 // decode_gateup.  Grid: d_ff_shared/16 shared-expert blocks, then
 // (routed list capacity x d_ff/16) blocks, of 256 threads, two blocks per
 // CU.  A routed block first routes (see above) and drops out when its list
@@ -464,20 +551,9 @@ __device__ __forceinline__ void gateup_body(const DecodeArgs& a, const DecodeWs&
     eb = a.routed + (size_t)ref * a.stride;
   }
 
-  // 1. Weight loads of this wave.
-  const int mat = wv >> 1, kh = wv & 1;
-  const int n = lane & 15, q = lane >> 4;
-  const uint8_t* tile = eb + (size_t)(g * 2 + mat) * oD * rec_bytes(FMT);
-  uint4 cw[kMaxOctPerWave], pa[kMaxOctPerWave], pb[kMaxOctPerWave];
-  uint2 hw[kMaxOctPerWave];
-#pragma unroll
-  for (int i = 0; i < kMaxOctPerWave; ++i) {
-    const int o = kh + 2 * i;
-    if (o < oD) load_record<FMT>(tile + (size_t)o * rec_bytes(FMT), lane, cw[i], hw[i], pa[i], pb[i]);
-  }
-
-  // 2. Activations (16-byte pieces; every element defined, so the array
-  // stays in registers).
+  // 1. Activations first (16-byte pieces; every element defined, so the
+  // array stays in registers): loads complete in the order they are issued,
+  // so the staging below waits for these and not for the weights.
   constexpr bool in_bf16 = XM == kXBf16 || XM == kXRms;
   constexpr bool RMS = XM == kXRms || XM == kXRmsF32;
   const int nin = in_bf16 ? T * D8 : 2 * T * D8;
@@ -495,7 +571,26 @@ __device__ __forceinline__ void gateup_body(const DecodeArgs& a, const DecodeWs&
   if (RMS && T > 1) {  // published by decode_list_kernel
 #pragma unroll
     for (int t = 0; t < T; ++t) rinv[t] = w.rinv[t];
-  } else if (RMS) {
+  }
+
+  // 2. Weight loads of this wave.
+  const int mat = wv >> 1, kh = wv & 1;
+  const int n = lane & 15, q = lane >> 4;
+  const uint8_t* tile = eb + (size_t)(g * 2 + mat) * oD * rec_bytes(FMT);
+  uint4 cw[kMaxOctPerWave], pa[kMaxOctPerWave], pb[kMaxOctPerWave];
+  uint2 hw[kMaxOctPerWave];
+#pragma unroll
+  for (int i = 0; i < kMaxOctPerWave; ++i) {
+    const int o = kh + 2 * i;
+    if (o < oD) load_record<FMT>(tile + (size_t)o * rec_bytes(FMT), lane, cw[i], hw[i], pa[i], pb[i]);
+  }
+  // 3. The expert's down records for the down blocks of this XCD, last, so
+  // that no wait for the loads above covers them.
+  const int Fu_pf = vb < nsh ? a.Fs : a.F;
+  const DnPrefetch dpf = prefetch_down_rows(eb, D, Fu_pf, rec_bytes(FMT),
+                                            down_offset(D, Fu_pf, FMT), vb, vb - g, Fu_pf / 16,
+                                            tid, kGuThreads);
+  if (RMS && T == 1) {
     float ss[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) ss[t] = 0.f;
@@ -520,7 +615,7 @@ __device__ __forceinline__ void gateup_body(const DecodeArgs& a, const DecodeWs&
       const float r = wave_sum_f32(ss[t]);
       if (lane == 0) s_ss[wv][t] = r;
     }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       float ssum = 0.f;
@@ -592,21 +687,24 @@ __device__ __forceinline__ void gateup_body(const DecodeArgs& a, const DecodeWs&
       if (ok && (pc & 7) == 0) s_xs[t * nbD + b] = make_float2(X, Xc);
     }
   }
-  __syncthreads();
+  lds_barrier();
 
-  // 3. Dequantising MFMA GEMV over this wave's octets.
+  // 4. Dequantising MFMA GEMV over this wave's octets.  The MFMA output rows
+  // are tokens; rows past T are computed from a copy of token 0's
+  // activations and never read (only lanes 0..15 are kept), so the A operand
+  // needs no zeroing.
   const DqConsts kc = dq_consts();
   float acc[T], mt[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) acc[t] = mt[t] = 0.f;
+  const int xrow = (n < T ? n : 0) * D8p + q;  // this lane's A-operand row
 #pragma unroll
   for (int i = 0; i < kMaxOctPerWave; ++i) {
     const int o = kh + 2 * i;
     if (o < oD) {
-      auto xfrag = [&](int beta, bool lo) -> uint4 {  // rows n >= T are zero (a select)
-        const int idx = (n < T ? n : 0) * D8p + 4 * (8 * o + beta) + q;
-        const uint4 v = lo ? s_xlo[idx] : s_xhi[idx];
-        return n < T ? v : make_uint4(0, 0, 0, 0);
+      auto xfrag = [&](int beta, bool lo) -> uint4 {
+        const int idx = xrow + 4 * (8 * o + beta);
+        return lo ? s_xlo[idx] : s_xhi[idx];
       };
       auto xsum = [&](int beta, int t) -> float2 { return s_xs[t * nbD + 8 * o + beta]; };
       record_gemv<T, FMT, HAS_LO, true>(cw[i], hw[i], pa[i], pb[i], 8, kc, xfrag, xsum, acc, mt, q);
@@ -621,9 +719,9 @@ __device__ __forceinline__ void gateup_body(const DecodeArgs& a, const DecodeWs&
 #pragma unroll
     for (int t = 0; t < T; ++t) s_red[wv][t][n] = acc[t] + mt[t];
   }
-  __syncthreads();
+  lds_barrier();
 
-  // 4. SwiGLU over 16 FFN rows x T tokens; h in bf16 hi + lo; half-block sums.
+  // 5. SwiGLU over 16 FFN rows x T tokens; h in bf16 hi + lo; half-block sums.
   if (tid < 16 * T) {
     const int t = tid >> 4, nn = tid & 15;
     const float ga = s_red[0][t][nn] + s_red[1][t][nn];
@@ -644,6 +742,7 @@ __device__ __forceinline__ void gateup_body(const DecodeArgs& a, const DecodeWs&
     }
     if (nn == 0) w.hs[(((size_t)u * T + t) * (w.Fp / 32) + (g >> 1)) * 2 + (g & 1)] = make_float2(X, Xc);
   }
+  keep_alive(dpf);
 }
 
 // 2..4 tokens: the routing and the expert list, once per layer call.  One
@@ -732,17 +831,6 @@ __global__ __launch_bounds__(kGuThreads, 2) void decode_gateup_kernel(DecodeArgs
   gateup_body<T, FMT, XM>(a, w, (int)blockIdx.x, L, s_dyn);
 }
 
-// ----------------------------------------------------------------------------
-// Direct global -> LDS load: lane l's 16 bytes land at lds + 16 l (`lds` the
-// same for the whole wave); counts in vmcnt.
-typedef __attribute__((address_space(3))) void dn_lds_t;
-__device__ __forceinline__ void dn_dma16(const void* src, void* lds) {
-  __builtin_amdgcn_global_load_lds(src, (dn_lds_t*)lds, 16, 0, 0);
-}
-// Wait until no vector-memory operation of this wave is in flight.
-__device__ __forceinline__ void dn_wait_vm0() {
-  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0); expcnt, lgkmcnt not waited
-}
 
 // ----------------------------------------------------------------------------
 // decode_down.  Grid: D/16 blocks of 1024 threads; wave w handles list
@@ -828,9 +916,9 @@ __global__ __launch_bounds__(1024) void decode_down_kernel(DecodeArgs a, DecodeW
     for (int o = 0; o < kMaxDecodeFOct; ++o) {
       if (o < oF) {
         const int nvalid = nb - 8 * o < 8 ? nb - 8 * o : 8;
-        auto xfrag = [&](int beta, bool lo) -> uint4 {  // rows n >= T are zero (a select)
-          const uint4 v = s_hw[((n < T ? n : 0) * 2 + (lo ? 1 : 0)) * hrow + (32 * (8 * o + beta) + 8 * q) / 8];
-          return n < T ? v : make_uint4(0, 0, 0, 0);
+        // rows past T read token 0's h: those output rows are never used
+        auto xfrag = [&](int beta, bool lo) -> uint4 {
+          return s_hw[((n < T ? n : 0) * 2 + (lo ? 1 : 0)) * hrow + (32 * (8 * o + beta) + 8 * q) / 8];
         };
         auto xsum = [&](int beta, int t) -> float2 { return s_hs[t * nbF + 8 * o + beta]; };
         record_gemv<T, FMT, true, false, 1>(cw[o], hw[o], pa[o], pb[o], nvalid, kc, xfrag, xsum, acc,
