@@ -249,6 +249,28 @@ def layer_forward(x, logits, k: int, get_expert, shared):
     return out, idx, gate
 
 
+def layer_forward_grouped(x, logits, k: int, get_expert, shared):
+    """The layer of ``layer_forward``, with the products grouped by expert.
+
+    Same definition, out_t = sum_j gate_tj * FFN_{idx[t][j]}(x_t) +
+    FFN_shared(x_t): each routed expert's FFN runs once, on all the rows
+    routed to it, and every row is added to its token's output with its
+    gate, experts taken in ascending id as in ``layer_forward``.  A token
+    names an expert at most once, so no output row receives two rows of one
+    product.  Only the batching of the matrix products differs, so the two
+    agree up to fp64 rounding; this form is what makes whole chunks of
+    thousands of tokens affordable.  Returns (out [T][D], idx, gate).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    idx, gate = route(logits, k)
+    out = expert_ffn(x, *shared)
+    for e in np.unique(idx):
+        t, j = np.nonzero(idx == e)                  # the rows routed to expert e
+        y = expert_ffn(x[t], *get_expert(int(e)))
+        out[t] += gate[t, j][:, None] * y
+    return out, idx, gate
+
+
 def slot_layer_forward(x, logits, k: int, get_expert, shared, slot_of):
     """Layer with only some experts resident ("slot table").
 

@@ -80,8 +80,14 @@ def test_full_width_prefill_256_tokens(g, full):
     assert err <= RTOL_L2
 
 
-def test_full_chunk_8192_sampled_tokens(g, full):
-    """The 8192-token chunk at full size: 12 sampled tokens checked one by one."""
+@pytest.mark.timeout(900)
+def test_full_chunk_8192_whole_output(g, full):
+    """The 8192-token chunk at full size, every output element: relative L2
+    error over the whole [8192, 3072] output (the bar), with the largest
+    per-token error reported beside it; bitwise deterministic over two runs.
+    The oracle runs each expert's FFN once on all its rows
+    (layer_forward_grouped), on weights from the device side of the seeded
+    generator."""
     w, shape, L = full
     T, D, E, k = w["tokens"], w["d_model"], w["n_experts"], w["top_k"]
     logits = synth.router_logits(0, 0, T, E, zipf_s=w["zipf_s"], alpha=w["alpha"])
@@ -91,15 +97,13 @@ def test_full_chunk_8192_sampled_tokens(g, full):
     out2 = run(L.table(), g.u16_to_dev(xb), g.moe.MOE_BF16, g.f32_to_dev(logits), g.moe.MOE_BF16)
     assert np.array_equal(out.cpu().numpy(), out2.cpu().numpy())   # deterministic
     got = g.out_to_f64(out, True).reshape(T, D)
-    sample = [0, 1, 127, 128, 4095, 8191] + list(np.random.default_rng(0).choice(T, 6, replace=False))
-    ow = OracleWeights(0, 0, D, w["d_ff"], w["d_ff_shared"], E, w["fmt"])
-    x64 = O.bf16_to_f64(xb)
-    errs = []
-    for t in sample:
-        ref, _, _ = O.layer_forward(x64[t:t + 1], logits[t:t + 1], k, ow, ow.shared)
-        errs.append(rel_l2(got[t:t + 1], ref))
-    print("8192-chunk sampled rel_l2 max=%.3g" % max(errs))
-    assert max(errs) <= RTOL_L2
+    ow = g.DeviceOracleWeights(0, 0, D, w["d_ff"], w["d_ff_shared"], E, w["fmt"])
+    ref, _, _ = O.layer_forward_grouped(O.bf16_to_f64(xb), logits, k, ow, ow.shared)
+    err = rel_l2(got, ref)
+    per_token = np.linalg.norm(got - ref, axis=1) / np.linalg.norm(ref, axis=1)
+    print("8192-token chunk: whole-output rel_l2=%.3g, per-token max %.3g (token %d), median %.3g"
+          % (err, per_token.max(), int(per_token.argmax()), float(np.median(per_token))))
+    assert err <= RTOL_L2
 
 
 def test_prefill_rmsnorm_input(g, full):

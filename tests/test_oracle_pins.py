@@ -399,3 +399,19 @@ def test_packed_size_full_width_matches_page_accounting():
     assert O.packed_expert_bytes(3072, 512, 1) == 3 * 3072 * 512 * 3 // 8
     assert O.packed_expert_bytes(3072, 512, 2) == 3 * 3072 * 512 * 7 // 16
     assert O.packed_expert_bytes(3072, 512, 3) == 3 * 3072 * 512 * 5 // 16
+
+
+def test_grouped_layer_equals_per_token_layer():
+    """layer_forward_grouped (one product per expert over all its rows)
+    against layer_forward (one product per routed pair), on the tiny case and
+    on a case where experts take many tokens: equal up to fp64 rounding."""
+    from helpers import OracleWeights
+    w = synth.WORKLOADS["tiny"]
+    ow = OracleWeights(0, 0, w["d_model"], w["d_ff"], w["d_ff_shared"], w["n_experts"], w["fmt"])
+    for T, tag in ((4, 0), (96, 5)):
+        x = O.bf16_to_f64(synth.activations_bf16(0, tag, T, w["d_model"]))
+        lg = synth.router_logits(0, tag, T, w["n_experts"], zipf_s=1.1, alpha=1.0)
+        a, ia, ga = O.layer_forward(x, lg, w["top_k"], ow, ow.shared)
+        b, ib, gb = O.layer_forward_grouped(x, lg, w["top_k"], ow, ow.shared)
+        assert np.array_equal(ia, ib) and np.array_equal(ga, gb)
+        assert np.max(np.abs(a - b)) <= 1e-12 * np.max(np.abs(a))
