@@ -258,7 +258,11 @@ def bench_decode_t1(ctx, stack, K, W, use_graph):
 
 
 def bench_chain(ctx, stack, K, W, use_graph, T, slot=None):
-    """T tokens through all layers of the stack, chained (RMS input rule)."""
+    """T tokens through all layers of the stack, chained (RMS input rule).
+
+    Besides the timed graph replays, an eager pass launches the same steps
+    behind a device-side spin with a HIP event pair on every layer's gate/up
+    kernel, for that kernel's roofline."""
     torch, moe, synth = ctx.torch, ctx.moe, ctx.synth
     w, shape, layers = stack
     L, D = len(layers), w["d_model"]
@@ -273,25 +277,44 @@ def bench_chain(ctx, stack, K, W, use_graph, T, slot=None):
     mcount = torch.zeros(L, dtype=torch.int32, device=ctx.dev)
     tables = [ly.table() if slot is None else slot[l] for l, ly in enumerate(layers)]
 
+    def layer(l):
+        x = x0 if l == 0 else acts[l - 1]
+        fl = 0 if l == 0 else moe.MOE_FLAG_RMSNORM_INPUT
+        if slot is None:
+            moe.moe_layer_forward(shape, T, x, moe.MOE_BF16, fl, logits[l], tables[l], acts[l],
+                                  moe.MOE_BF16, None, 0, None, ws, wsb)
+        else:
+            moe.moe_layer_forward(shape, T, x, moe.MOE_BF16, fl, logits[l], tables[l], acts[l],
+                                  moe.MOE_BF16, miss.data_ptr() + l * kcap * 16, kcap,
+                                  mcount.data_ptr() + 4 * l, ws, wsb)
+
     def launch(i):
         for l in range(L):
-            x = x0 if l == 0 else acts[l - 1]
-            fl = 0 if l == 0 else moe.MOE_FLAG_RMSNORM_INPUT
-            if slot is None:
-                moe.moe_layer_forward(shape, T, x, moe.MOE_BF16, fl, logits[l], tables[l], acts[l],
-                                      moe.MOE_BF16, None, 0, None, ws, wsb)
-            else:
-                moe.moe_layer_forward(shape, T, x, moe.MOE_BF16, fl, logits[l], tables[l], acts[l],
-                                      moe.MOE_BF16, miss.data_ptr() + l * kcap * 16, kcap,
-                                      mcount.data_ptr() + 4 * l, ws, wsb)
+            layer(l)
 
     launch(0)
     torch.cuda.synchronize()
     dt, _ = run_steps(ctx, launch, K, W, use_graph)
-    res = dict(tokens=K * T, seconds=dt)
-    if slot is not None:
-        res["misses_per_layer"] = float(mcount.float().mean().item())
+    # the gate/up kernel of every layer call, event-timed in an eager pass
+    evs = HipEvents(K * L)
+    torch.cuda._sleep(int(2.0e5 * K * L // 10 + 1000000))
+    for i in range(K):
+        for l in range(L):
+            moe.moe_set_kernel_timer(*evs.pairs[i * L + l])
+            layer(l)
+    torch.cuda.synchronize()
+    kms = evs.elapsed_ms()
+    evs.close()
+    res = dict(tokens=K * T, seconds=dt, gu_kernel_s=sum(kms) / len(kms) * 1e-3)
+    if slot is None:
+        res["experts_per_layer"] = [u + 1 for u in unique_counts(ctx, shape, logits, T)]
+    else:
+        m = mcount.cpu().tolist()
+        res["misses"] = m
+        res["misses_per_layer"] = sum(m) / L
         res["hit_rate"] = 1.0 - res["misses_per_layer"] / w["top_k"] / T
+        # resident experts touched (each hit in this one-token chain is a distinct expert) + shared
+        res["experts_per_layer"] = [w["top_k"] * T - mi + 1 for mi in m]
     return res
 
 
@@ -654,35 +677,120 @@ def bench_slot_host(ctx, n_tokens=16, name="slot_host_q3s_t1_8l"):
 
 
 # ----------------------------------------------------------------------------
-def cpu_baseline_decode(budget_s=15.0):
-    """The fp64 oracle on single-token, single-layer decode: a bounded sample."""
-    import numpy as np
-    import synth
-    from oracle import moe_oracle as O
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] + [1]))
     except Exception:
-        cores = os.cpu_count()
+        return os.cpu_count()
+
+
+def _logical_weights(ctx, layer, ids, D, F, Fs, E, fmt):
+    """Logical weights of experts `ids` of one layer as host arrays, made by
+    the device side of the seeded generator (bit-identical to the host side;
+    this is input generation, never timed)."""
+    import numpy as np
+    import torch
+    from synth.device import fill_expert_weights
+    out = {}
+    for e in ids:
+        f = Fs if e == E else F
+        codes = torch.empty(3 * f * D, dtype=torch.uint8, device=ctx.dev)
+        scale = torch.empty(3 * f * D // 32, dtype=torch.int16, device=ctx.dev)
+        mins = torch.empty_like(scale)
+        fill_expert_weights(0, layer, int(e), 1, D, f, fmt, codes, scale, mins)
+        out[int(e)] = (codes.cpu().numpy(), scale.cpu().numpy().view(np.uint16),
+                       mins.cpu().numpy().view(np.uint16) if fmt == ctx.synth.FMT_Q2SM else None, f)
+    return out
+
+
+def cpu_baseline_decode(ctx, budget_s=8.0):
+    """The fp64 oracle on single-token, single-layer decode: a bounded sample."""
+    import numpy as np
+    from oracle import moe_oracle as O
+    synth = ctx.synth
     w = synth.WORKLOADS["decode_t1"]
-    D, F, E, k = w["d_model"], w["d_ff"], w["n_experts"], w["top_k"]
+    D, F, E, k, fmt = w["d_model"], w["d_ff"], w["n_experts"], w["top_k"], w["fmt"]
     done, t_compute = 0, 0.0
     for l in range(48):
         lg = synth.router_logits(0, l, 1, E, zipf_s=w["zipf_s"], alpha=w["alpha"])
         x = O.bf16_to_f64(synth.activations_bf16(0, l, 1, D))
         idx, _ = O.route(lg, k)
-        logical = {e: synth.expert_weights(0, l, e, D, F, 1) for e in list(idx[0]) + [E]}
+        logical = _logical_weights(ctx, l, list(np.unique(idx)) + [E], D, F, w["d_ff_shared"], E, fmt)
         t0 = time.perf_counter()
-        mats = {e: O.expert_matrices(c, s, m, D, F, 1) for e, (c, s, m) in logical.items()}
+        mats = {e: O.expert_matrices(c, s, m, D, f, fmt) for e, (c, s, m, f) in logical.items()}
         O.layer_forward(x, lg, k, lambda e: mats[e], mats[E])
         t_compute += time.perf_counter() - t0
         done += 1
         if t_compute > budget_s:
             break
-    return dict(value=done / t_compute, unit="tokens/s", cores=int(cores), kind="oracle",
+    return dict(value=done / t_compute, unit="tokens/s", cores=_blas_threads(), kind="oracle",
                 sample="%d single-token layer passes (layers 0..%d of the decode stack), "
                        "fp64 numpy: dequantisation of the 11 touched experts + routing + SwiGLU "
                        "FFNs; weight generation not timed" % (done, done - 1))
+
+
+def cpu_baseline_chain(ctx, name, T, budget_s=8.0):
+    """The fp64 oracle on the first layers of a chained 48-layer workload
+    (the RMS rule between layers), as tokens through all 48 layers per
+    second, extrapolated from the layers it finished."""
+    import numpy as np
+    from oracle import moe_oracle as O
+    synth = ctx.synth
+    w = synth.WORKLOADS[name]
+    D, F, Fs, E, k, fmt = w["d_model"], w["d_ff"], w["d_ff_shared"], w["n_experts"], w["top_k"], w["fmt"]
+    slot = "n_slots" in w
+    x = O.bf16_to_f64(synth.activations_bf16(0, 0, T, D))
+    done, t_compute = 0, 0.0
+    for l in range(48):
+        lg = synth.router_logits(0, l, T, E, zipf_s=w["zipf_s"], alpha=w["alpha"])
+        idx, _ = O.route(lg, k)
+        slot_of = None
+        if slot:                                   # the most popular n_slots experts resident
+            res = np.argsort(synth.expert_ranks(0, l, E))[:w["n_slots"]]
+            slot_of = np.full(E, -1)
+            slot_of[res] = np.arange(len(res))
+        logical = _logical_weights(ctx, l, list(np.unique(idx)) + [E], D, F, Fs, E, fmt)
+        t0 = time.perf_counter()
+        mats = {e: O.expert_matrices(c, s, m, D, f, fmt) for e, (c, s, m, f) in logical.items()}
+        if slot:
+            y, _, _, _ = O.slot_layer_forward(x, lg, k, lambda e: mats[e], mats[E], slot_of)
+        else:
+            y, _, _ = O.layer_forward(x, lg, k, lambda e: mats[e], mats[E])
+        x = O.bf16_to_f64(O.rms_chain(O.bf16_to_f64(O.f64_to_bf16(y))))
+        t_compute += time.perf_counter() - t0
+        done += 1
+        if t_compute > budget_s:
+            break
+    per_layer = t_compute / done
+    return dict(value=T / (48 * per_layer), unit="tokens/s", cores=_blas_threads(), kind="oracle",
+                sample="layers 0..%d of the 48 (%d tokens, RMS rule between layers%s), fp64 numpy: "
+                       "dequantisation of the touched experts + routing + SwiGLU FFNs, "
+                       "%.2f s per layer, extrapolated to 48 layers; weight generation not timed"
+                       % (done - 1, T, ", slot-table partials" if slot else "", per_layer))
+
+
+def cpu_baseline_prefill(ctx, budget_tokens=1024):
+    """The fp64 oracle on the first tokens of the 8192-token prefill chunk."""
+    import numpy as np
+    from oracle import moe_oracle as O
+    synth = ctx.synth
+    w = synth.WORKLOADS["prefill_8192"]
+    D, F, Fs, E, k, fmt = w["d_model"], w["d_ff"], w["d_ff_shared"], w["n_experts"], w["top_k"], w["fmt"]
+    S = budget_tokens
+    lg = synth.router_logits(0, 0, w["tokens"], E, zipf_s=w["zipf_s"], alpha=w["alpha"])[:S]
+    x = O.bf16_to_f64(synth.activations_bf16(0, 0, w["tokens"], D)[:S])
+    idx, _ = O.route(lg, k)
+    logical = _logical_weights(ctx, 0, list(np.unique(idx)) + [E], D, F, Fs, E, fmt)
+    t0 = time.perf_counter()
+    mats = {e: O.expert_matrices(c, s, m, D, f, fmt) for e, (c, s, m, f) in logical.items()}
+    O.layer_forward_grouped(x, lg, k, lambda e: mats[e], mats[E])
+    dt = time.perf_counter() - t0
+    return dict(value=S / dt, unit="tokens/s", cores=_blas_threads(), kind="oracle",
+                sample="the first %d of the chunk's 8192 tokens through the layer (%d experts "
+                       "touched), fp64 numpy: dequantisation + routing + one SwiGLU product per "
+                       "expert over its rows; weight generation not timed"
+                       % (S, len(np.unique(idx))))
 
 
 # ----------------------------------------------------------------------------
@@ -696,6 +804,33 @@ def copy_calibration():
         b.copy_(a)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes_per_launch": n, "launches": 4}), flush=True)
+
+
+def chain_rooflines(ctx, w, r, K, T):
+    """HBM rooflines of a chained 48-layer step: the whole step (every layer's
+    distinct experts, shared expert included, read once: the sum over layers
+    of (U_l + 1) x packed expert bytes, over the step time) and its dominant
+    kernel, the gate/up GEMV (its share of those experts' bytes plus the
+    activations in and h out, per launch, over its event-timed duration)."""
+    shape = ctx.shape(w)
+    e_bytes = ctx.moe.moe_packed_expert_bytes(shape, w["d_ff"])
+    gu_bytes = e_bytes * 2 // 3
+    n = r["experts_per_layer"]
+    step_bytes = float(sum(n)) * e_bytes
+    step_s = r["seconds"] / K
+    gu_per_launch = sum(u * gu_bytes + T * w["d_model"] * 2 + u * T * w["d_ff"] * 4
+                        for u in n) / len(n)
+    ach_step = step_bytes / step_s / 1e9
+    ach_k = gu_per_launch / r["gu_kernel_s"] / 1e9
+    return dict(
+        experts_per_layer=sum(n) / len(n),
+        roofline={"bound": "hbm", "scope": "whole step (48 layers)", "achieved": ach_step,
+                  "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach_step / HBM_PEAK_GBS,
+                  "traffic": None, "bytes_per_step": step_bytes},
+        kernel_roofline={"bound": "hbm", "kernel": "decode_gateup_kernel (every layer's launch)",
+                         "achieved": ach_k, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": ach_k / HBM_PEAK_GBS, "traffic": None,
+                         "bytes_per_launch": gu_per_launch, "kernel_us": r["gu_kernel_s"] * 1e6})
 
 
 def main():
@@ -713,6 +848,7 @@ def main():
     torch, moe = ctx.torch, ctx.moe
     K = args.steps if args.steps is not None else 960
     W = args.warmup if args.warmup is not None else 48
+    K2 = max(K, 240)    # steps of the other single-layer decode workloads (not the primary line)
     results = {}
 
     stack = None
@@ -728,18 +864,23 @@ def main():
         print("decode_t1: %.1f us/step, gate/up kernel %.2f us" %
               (r["seconds"] / K * 1e6, r["kernel_s"] * 1e6), file=sys.stderr, flush=True)
     if "mtp_verify_t4_48l" in wl:
-        Kc = max(1, K // 48)
+        Kc = max(10, K // 48)
         r = bench_chain(ctx, stack, Kc, 2, use_graph, T=4)
+        w = ctx.synth.WORKLOADS["mtp_verify_t4_48l"]
         results["mtp_verify_t4_48l"] = dict(
             value=r["tokens"] / r["seconds"], unit="tokens/s", steps=Kc,
             ms_per_step=r["seconds"] / Kc * 1e3,
-            config="4 tokens x 48 chained layers (RMS input rule), Q2SM, 43.6 GB resident")
+            config="4 tokens x 48 chained layers (RMS input rule), Q2SM, 43.6 GB resident",
+            **chain_rooflines(ctx, w, r, Kc, 4))
+        if not args.no_cpu:
+            results["mtp_verify_t4_48l"]["cpu_baseline"] = cpu_baseline_chain(
+                ctx, "mtp_verify_t4_48l", 4)
         print("mtp_verify_t4_48l: %.3f ms/step" % (r["seconds"] / Kc * 1e3), file=sys.stderr,
               flush=True)
     if "prefill_8192" in wl:
         if stack is None:
             stack = decode_stack(ctx, "prefill_8192", 4)
-        Kp = max(2, K // 48)
+        Kp = max(10, K // 48)
         r = bench_prefill(ctx, stack, Kp, 2, use_graph)
         sps = r["seconds"] / Kp
         achieved = r["flops_per_launch"] / r["kernel_s"] / 1e12
@@ -755,16 +896,18 @@ def main():
                                                       ["prefill.hip", "common.hpp", "kernels.hpp"], None),
                       "flops_per_launch": r["flops_per_launch"],
                       "kernel_us": r["kernel_s"] * 1e6})
+        if not args.no_cpu:
+            results["prefill_8192"]["cpu_baseline"] = cpu_baseline_prefill(ctx)
         print("prefill_8192: %.3f ms/step, gate/up kernel %.1f us (%.1f TFLOP/s)" %
               (sps * 1e3, r["kernel_s"] * 1e6, achieved), file=sys.stderr, flush=True)
     if "decode_router_t1" in wl:
         if stack is None or len(stack[2]) < 48:
             stack = decode_stack(ctx, "mtp_verify_t4_48l", 48)
-        r = bench_router(ctx, stack, K, W, use_graph, T=1, n_layers=48)
+        r = bench_router(ctx, stack, K2, W, use_graph, T=1, n_layers=48)
         achieved = r["router_bytes"] / r["router_s"] / 1e9
         results["decode_router_t1"] = dict(
-            value=r["tokens"] / r["seconds"], unit="tokens/s", steps=K,
-            ms_per_step=r["seconds"] / K * 1e3,
+            value=r["tokens"] / r["seconds"], unit="tokens/s", steps=K2,
+            ms_per_step=r["seconds"] / K2 * 1e3,
             config="decode_t1 with the router projection on the GPU (bf16 W_r 512 x 3072 per "
                    "layer, 48 layers rotated)",
             roofline={"bound": "hbm", "kernel": "router_gemv_kernel (bf16 W_r GEMV)",
@@ -774,11 +917,11 @@ def main():
                                                       ["router.hip", "common.hpp", "kernels.hpp"], None),
                       "bytes_per_launch": r["router_bytes"], "kernel_us": r["router_s"] * 1e6})
         print("decode_router_t1: %.1f us/step, router kernel %.2f us" %
-              (r["seconds"] / K * 1e6, r["router_s"] * 1e6), file=sys.stderr, flush=True)
+              (r["seconds"] / K2 * 1e6, r["router_s"] * 1e6), file=sys.stderr, flush=True)
     if "prefill_router_8192" in wl:
         if stack is None:
             stack = decode_stack(ctx, "prefill_8192", 4)
-        Kp = max(2, K // 48)
+        Kp = max(10, K // 48)
         r = bench_router(ctx, stack, Kp, 2, use_graph, T=8192, n_layers=4)
         achieved = r["router_flops"] / r["router_s"] / 1e12
         results["prefill_router_8192"] = dict(
@@ -799,26 +942,31 @@ def main():
         torch.cuda.empty_cache()
     if "slot_q3s_t1_48l" in wl:
         sstack, tables, keep = build_slot_stack(ctx, "slot_q3s_t1_48l")
-        Kc = max(1, K // 48)
+        Kc = max(10, K // 48)
         r = bench_chain(ctx, sstack, Kc, 2, use_graph, T=1, slot=tables)
+        w = ctx.synth.WORKLOADS["slot_q3s_t1_48l"]
         results["slot_q3s_t1_48l"] = dict(
             value=r["tokens"] / r["seconds"], unit="tokens/s", steps=Kc,
             ms_per_step=r["seconds"] / Kc * 1e3, hit_rate=r["hit_rate"],
-            config="1 token x 48 chained layers, Q3S, 128/512 experts resident per layer")
+            config="1 token x 48 chained layers, Q3S, 128/512 experts resident per layer",
+            **chain_rooflines(ctx, w, r, Kc, 1))
+        if not args.no_cpu:
+            results["slot_q3s_t1_48l"]["cpu_baseline"] = cpu_baseline_chain(
+                ctx, "slot_q3s_t1_48l", 1)
         print("slot_q3s_t1_48l: %.3f ms/step hit %.3f" % (r["seconds"] / Kc * 1e3, r["hit_rate"]),
               file=sys.stderr, flush=True)
         del keep, tables, sstack
         torch.cuda.empty_cache()
     if "decode_q2s_t1" in wl:
         qstack = decode_stack(ctx, "decode_q2s_t1", 48)
-        r = bench_decode_t1(ctx, qstack, K, W, use_graph)
+        r = bench_decode_t1(ctx, qstack, K2, W, use_graph)
         achieved = r["bytes_per_launch"] / r["kernel_s"] / 1e9
         results["decode_q2s_t1"] = dict(
-            value=r["tokens"] / r["seconds"], unit="tokens/s", steps=K,
-            ms_per_step=r["seconds"] / K * 1e3,
+            value=r["tokens"] / r["seconds"], unit="tokens/s", steps=K2,
+            ms_per_step=r["seconds"] / K2 * 1e3,
             config="1 token x 1 layer rotated over 48 resident layers, Q2S (scale-only 2-bit, "
                    "2.5 bits/weight, 36.3 GB), bf16 in/out",
-            layer_hbm_frac=r["layer_bytes"] / (r["seconds"] / K) / 1e9 / HBM_PEAK_GBS,
+            layer_hbm_frac=r["layer_bytes"] / (r["seconds"] / K2) / 1e9 / HBM_PEAK_GBS,
             roofline={"bound": "hbm", "kernel": "decode_gateup_kernel (Q2S)",
                       "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                       "frac": achieved / HBM_PEAK_GBS,
@@ -827,7 +975,7 @@ def main():
                           ["decode.hip", "common.hpp", "route_common.hpp", "kernels.hpp"], None),
                       "bytes_per_launch": r["bytes_per_launch"], "kernel_us": r["kernel_s"] * 1e6})
         print("decode_q2s_t1: %.1f us/step, gate/up kernel %.2f us" %
-              (r["seconds"] / K * 1e6, r["kernel_s"] * 1e6), file=sys.stderr, flush=True)
+              (r["seconds"] / K2 * 1e6, r["kernel_s"] * 1e6), file=sys.stderr, flush=True)
         del qstack
         torch.cuda.empty_cache()
 
@@ -890,7 +1038,7 @@ def main():
         }
         line["layer_hbm_frac"] = prim["layer_bytes"] / (prim["seconds"] / K) / 1e9 / HBM_PEAK_GBS
     if not args.no_cpu and prim is not None:
-        line["cpu_baseline"] = cpu_baseline_decode()
+        line["cpu_baseline"] = cpu_baseline_decode(ctx)
     line["workloads"] = results
     print(json.dumps(line), flush=True)
 
