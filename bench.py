@@ -635,6 +635,19 @@ def bench_slot_host(ctx, n_tokens=16, name="slot_host_q3s_t1_8l"):
     pool = moe.HostPool(threads)
     host_s = 0.0
     nmiss = 0
+    # The host starts on a layer's misses as soon as the GPU has written the
+    # miss list (moe_set_route_event), while the GPU still computes the hits:
+    # the list, its count and the layer input are copied on a side stream
+    # that waits for that event.
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+    hip.hipStreamWaitEvent.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    ev_route = ctypes.c_void_p()
+    if hip.hipEventCreateWithFlags(ctypes.byref(ev_route), 2):     # hipEventDisableTiming
+        raise RuntimeError("hipEventCreateWithFlags failed")
+    side = torch.cuda.Stream()
 
     def token(i):
         nonlocal host_s, nmiss
@@ -642,13 +655,17 @@ def bench_slot_host(ctx, n_tokens=16, name="slot_host_q3s_t1_8l"):
             fl = 0 if l == 0 else moe.MOE_FLAG_RMSNORM_INPUT
             x = x0_d[i * D:(i + 1) * D] if l == 0 else outs[l - 1]
             xdt = moe.MOE_BF16 if l == 0 else moe.MOE_F32
+            moe.moe_set_route_event(ev_route.value)
             moe.moe_layer_forward(shape, 1, x, xdt, fl, logits[l].data_ptr() + 4 * i * E,
                                   st[l]["table"], outs[l], moe.MOE_F32, miss, k, mcount, ws, wsb)
-            miss_h[: 4 * k].copy_(miss, non_blocking=True)
-            miss_h[4 * k:].copy_(mcount, non_blocking=True)
-            if l > 0:
-                xin_h.copy_(outs[l - 1], non_blocking=True)   # the layer input, for the host rows
-            torch.cuda.current_stream().synchronize()
+            if hip.hipStreamWaitEvent(side.cuda_stream, ev_route.value, 0):
+                raise RuntimeError("hipStreamWaitEvent failed")
+            with torch.cuda.stream(side):
+                miss_h[: 4 * k].copy_(miss, non_blocking=True)
+                miss_h[4 * k:].copy_(mcount, non_blocking=True)
+                if l > 0:
+                    xin_h.copy_(outs[l - 1], non_blocking=True)   # the layer input
+            side.synchronize()
             nm = int(miss_h[4 * k].item())
             nmiss += nm
             h0 = time.perf_counter()
@@ -671,9 +688,11 @@ def bench_slot_host(ctx, n_tokens=16, name="slot_host_q3s_t1_8l"):
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     pool.close()
+    hip.hipEventDestroy(ev_route)
     n = n_tokens - 1
     return dict(tokens=n, seconds=dt, host_s=host_s, misses_per_layer=nmiss / (n * L),
-                hit_rate=1.0 - nmiss / (n * L * k), threads=threads, layers=L)
+                hit_rate=1.0 - nmiss / (n * L * k), threads=threads, layers=L,
+                host_simd=moe.moe_host_simd())
 
 
 # ----------------------------------------------------------------------------
@@ -1003,10 +1022,11 @@ def main():
             value=n / r["seconds"], unit="tokens/s", steps=n, ms_per_step=r["seconds"] / n * 1e3,
             host_ms_per_layer=r["host_s"] / (n * L) * 1e3,
             layer_ms=r["seconds"] / (n * L) * 1e3, misses_per_layer=r["misses_per_layer"],
-            hit_rate=r["hit_rate"], host_threads=r["threads"],
+            hit_rate=r["hit_rate"], host_threads=r["threads"], host_simd=r["host_simd"],
             config="1 token x 8 chained Q3S slot layers, 128/512 resident (Zipf 1.2, alpha "
-                   "0.331); misses computed on the host (fp32, %d threads) and added into "
-                   "each layer's output" % r["threads"])
+                   "0.331); misses computed on the host (fp32, %d threads, %s) while the GPU "
+                   "computes the hits, then added into each layer's output"
+                   % (r["threads"], r["host_simd"]))
         print("slot_host_q3s_t1_8l: %.2f ms/token, host %.3f ms/layer, %.2f misses/layer" %
               (r["seconds"] / n * 1e3, r["host_s"] / (n * L) * 1e3, r["misses_per_layer"]),
               file=sys.stderr, flush=True)

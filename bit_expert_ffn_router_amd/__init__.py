@@ -27,6 +27,7 @@ __all__ = [
     "moe_last_error", "moe_abi_version", "moe_set_kernel_timer", "moe_set_router_timer",
     "moe_slot_counts_take", "moe_slot_policy_plan", "moe_slot_table_stage",
     "moe_slot_table_commit", "HostPool", "moe_host_miss_ffn", "moe_add_rows",
+    "moe_set_route_event", "moe_host_simd",
     "LIB_PATH",
 ]
 
@@ -118,6 +119,8 @@ _sigs = {
     "moe_host_miss_ffn": (_I, [ctypes.POINTER(MoeShape), _I, _P, _I, ctypes.c_uint32, _P, _I, _P,
                                _P, _P]),
     "moe_add_rows": (_I, [_P, _I, _P, _I, _I, _P]),
+    "moe_set_route_event": (_I, [_P]),
+    "moe_host_simd": (ctypes.c_char_p, []),
 }
 for _name, (_res, _args) in _sigs.items():
     _f = getattr(_lib, _name)
@@ -319,3 +322,16 @@ def moe_set_router_timer(before, after):
             return ev
         return ev.cuda_event
     _check(_lib.moe_set_router_timer(h(before), h(after)))
+
+
+def moe_set_route_event(event):
+    """Record `event` (a torch.cuda.Event, a raw hipEvent_t address, or None
+    to clear) once this thread's next decode-path forward call has written its
+    routing and miss list."""
+    if event is not None and not isinstance(event, int):
+        event = event.cuda_event
+    _check(_lib.moe_set_route_event(event))
+
+
+def moe_host_simd() -> str:
+    return _lib.moe_host_simd().decode()

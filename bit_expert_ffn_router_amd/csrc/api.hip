@@ -75,6 +75,10 @@ KernelTimer& router_timer() {
   thread_local KernelTimer t;
   return t;
 }
+KernelTimer& route_event() {
+  thread_local KernelTimer t;
+  return t;
+}
 
 }  // namespace moe
 
@@ -97,6 +101,13 @@ moe_status moe_set_router_timer(void* before, void* after) {
   moe::router_timer().after = (hipEvent_t)after;
   return ok();
 }
+
+moe_status moe_set_route_event(void* event) {
+  moe::route_event().before = (hipEvent_t)event;
+  return ok();
+}
+
+const char* moe_host_simd(void) { return moe::host_simd_name(); }
 
 const char* moe_last_error(void) { return g_err; }
 

@@ -966,13 +966,26 @@ static hipError_t launch_decode_x(const DecodeArgs& a, const DecodeWs& w, hipStr
   if ((e = allow_lds(decode_gateup_kernel<T, FMT, XM>, lds, lds_gu)) != hipSuccess) return e;
   if ((e = allow_lds(decode_down_kernel<T, FMT>, lds_down, lds_dn)) != hipSuccess) return e;
   const int nblk = (a.shared ? a.Fs / 16 : 0) + (w.Wmax - 1) * (a.F / 16);
+  // The caller's route event (moe_set_route_event), recorded as soon as the
+  // kernel that writes the routing, the list and the miss list has run.
+  auto route_done = [&]() -> hipError_t {
+    KernelTimer& re = route_event();
+    if (re.before == nullptr) return hipSuccess;
+    const hipEvent_t ev = re.before;
+    re.before = nullptr;
+    return hipEventRecord(ev, st);
+  };
   if constexpr (T > 1) {
     decode_list_kernel<T><<<1, 2 * kGuThreads, (size_t)a.E * 4, st>>>(a, w);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = route_done()) != hipSuccess) return e;
   }
   if ((e = launch_timed(decode_gateup_kernel<T, FMT, XM>, dim3(nblk), dim3(kGuThreads),
                         (uint32_t)lds, st, a, w)) != hipSuccess)
     return e;
+  if constexpr (T == 1) {
+    if ((e = route_done()) != hipSuccess) return e;
+  }
   decode_down_kernel<T, FMT><<<a.D / 16, 1024, lds_down, st>>>(a, w);
   return hipGetLastError();
 }

@@ -205,33 +205,105 @@ __attribute__((target("avx2,fma"))) void record_rows4_avx2(const uint8_t* rec, i
   }
 }
 
+// The same four rows with AVX-512F.  One code word (lane 16 q + n, word wd)
+// holds row n's codes of column quarter q for both blocks 2 wd and 2 wd + 1
+// (block 2 wd in bits 0..7 and 16..23, block 2 wd + 1 in bits 8..15 and
+// 24..31), so one broadcast word shifted per lane gives 16 codes: lanes 0..7
+// block 2 wd, lanes 8..15 block 2 wd + 1, each in the record order of the
+// activation vector.  A word pair takes four multiply-adds per row (one per
+// quarter) instead of AVX2's eight, and the two blocks' scales multiply the
+// two halves of one accumulator.
+typedef float v16f __attribute__((vector_size(64)));
+typedef uint32_t v16u __attribute__((vector_size(64)));
+typedef float v8f_ __attribute__((vector_size(32)));
+__attribute__((target("avx512f"))) void record_rows4_avx512(const uint8_t* rec, int fmt, int n0,
+                                                            const float* xv, const float* xs,
+                                                            float* out) {
+  const uint32_t* lo = reinterpret_cast<const uint32_t*>(rec);
+  const uint32_t* hi = reinterpret_cast<const uint32_t*>(rec + 1024);
+  const v16u lanes = {0, 2, 4, 6, 16, 18, 20, 22, 8, 10, 12, 14, 24, 26, 28, 30};
+  const v16f zero = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  v16f tot[4] = {zero, zero, zero, zero};
+  float offs[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int wd = 0; wd < 4; ++wd) {
+    const int extra = (wd % 2 == 0) ? 1 : 0;  // Q3S: the third bit's position in the high word
+    const v16u shb = lanes + (uint32_t)extra;
+    v16f acc[4] = {zero, zero, zero, zero};
+    for (int q = 0; q < 4; ++q) {
+      v8f_ x0, x1;
+      __builtin_memcpy(&x0, xv + 32 * (2 * wd) + 8 * q, sizeof x0);
+      __builtin_memcpy(&x1, xv + 32 * (2 * wd + 1) + 8 * q, sizeof x1);
+      const v16f x = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13,
+                                             14, 15);
+      for (int r = 0; r < 4; ++r) {
+        const int L = 16 * q + n0 + r;
+        const uint32_t W = lo[4 * L + wd];
+        v16u c = ((v16u){W, W, W, W, W, W, W, W, W, W, W, W, W, W, W, W} >> lanes) & 3u;
+        if (fmt == kQ3) {  // u3 = u + 4 * (third bit)
+          const uint32_t H = hi[2 * L + wd / 2];
+          c += (((v16u){H, H, H, H, H, H, H, H, H, H, H, H, H, H, H, H} >> shb) & 1u) << 2;
+        }
+        acc[r] = __builtin_convertvector(c, v16f) * x + acc[r];
+      }
+    }
+    for (int r = 0; r < 4; ++r) {
+      float s0, o0, s1, o1;
+      block_params(rec, fmt, n0 + r, 2 * wd, s0, o0);
+      block_params(rec, fmt, n0 + r, 2 * wd + 1, s1, o1);
+      const v16f sv = {s0, s0, s0, s0, s0, s0, s0, s0, s1, s1, s1, s1, s1, s1, s1, s1};
+      tot[r] = sv * acc[r] + tot[r];
+      offs[r] += o0 * xs[2 * wd] + o1 * xs[2 * wd + 1];
+    }
+  }
+  for (int r = 0; r < 4; ++r) {
+    const v16f t = tot[r];
+    float s8[8];
+    for (int i = 0; i < 8; ++i) s8[i] = t[i] + t[i + 8];
+    out[r] = (((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]))) + offs[r];
+  }
+}
+
 // Four rows with the SSE2 row dot product.
 void record_rows4_sse2(const uint8_t* rec, int fmt, int n0, const float* xv, const float* xs,
                        float* out) {
   for (int r = 0; r < 4; ++r) out[r] = record_row_dot_sse2(rec, fmt, n0 + r, xv, xs);
 }
 
-// The row dot products this process uses: AVX2 + FMA where the CPU has them,
-// else SSE2.  MOE_HOST_SIMD=sse2 in the environment selects SSE2 (read at
-// every host layer call).  The two differ only in fp32 rounding order.
+// The row dot products this process uses: AVX-512F, else AVX2 + FMA, where
+// the CPU has them, else SSE2.  MOE_HOST_SIMD=avx2 or =sse2 in the
+// environment caps the choice (read at every host layer call).  They differ
+// only in fp32 rounding order.
 typedef void (*RowDot)(const uint8_t*, int, int, const float*, const float*, float*);
 // The CPU's features come from the flags line of /proc/cpuinfo, which lists
 // only what the kernel has enabled (AVX state included).
-bool cpu_has_avx2_fma() {
+struct CpuSimd {
+  bool avx2_fma = false, avx512f = false;
+};
+CpuSimd cpu_simd() {
+  CpuSimd c;
   std::ifstream f("/proc/cpuinfo");
   std::string line;
   while (std::getline(f, line)) {
     if (line.compare(0, 5, "flags") != 0) continue;
     const std::string l = " " + line + " ";
-    return l.find(" avx2 ") != std::string::npos && l.find(" fma ") != std::string::npos;
+    c.avx2_fma = l.find(" avx2 ") != std::string::npos && l.find(" fma ") != std::string::npos;
+    c.avx512f = l.find(" avx512f ") != std::string::npos;
+    break;
   }
-  return false;
+  return c;
 }
 RowDot row_dot_impl() {
-  static const bool avx2 = cpu_has_avx2_fma();
+  static const CpuSimd cpu = cpu_simd();
   const char* e = getenv("MOE_HOST_SIMD");
-  if (e && strcmp(e, "sse2") == 0) return record_rows4_sse2;
-  return avx2 ? record_rows4_avx2 : record_rows4_sse2;
+  const bool cap_sse2 = e && strcmp(e, "sse2") == 0, cap_avx2 = e && strcmp(e, "avx2") == 0;
+  if (cap_sse2) return record_rows4_sse2;
+  if (cpu.avx512f && !cap_avx2) return record_rows4_avx512;
+  return cpu.avx2_fma ? record_rows4_avx2 : record_rows4_sse2;
+}
+// Which implementation row_dot_impl picks (for the callers' reports).
+const char* row_dot_name() {
+  const RowDot d = row_dot_impl();
+  return d == record_rows4_avx512 ? "avx512" : (d == record_rows4_avx2 ? "avx2" : "sse2");
 }
 
 // Rows row0 .. row0 + 3 (row0 % 4 == 0) of a matrix stored from `base` as
@@ -252,6 +324,8 @@ void matrix_rows4_dot(RowDot dot, const uint8_t* base, int fmt, int row0, int K,
 }  // namespace
 
 hipError_t launch_add_rows(void* out, int out_bf16, const float* y, size_t n, hipStream_t st);
+
+const char* host_simd_name() { return row_dot_name(); }
 
 }  // namespace moe
 

@@ -22,6 +22,7 @@ struct KernelTimer {
 };
 KernelTimer& kernel_timer();  // the layer's dominant kernel
 KernelTimer& router_timer();  // the router projection kernel
+KernelTimer& route_event();   // `before` only: recorded once the routing and miss list are written
 
 // Launch `kernel` on st.  When the calling thread has armed the timer `tm`,
 // the launch carries its two events (hipExtLaunchKernel), which then take the
@@ -152,6 +153,7 @@ void host_prepare_x(int T, int D, const void* x, bool x_bf16, bool rms, float* o
 void host_miss_ffn(int D, int F, int fmt, int T, const float* xhat, const MissRec* miss, int nm,
                    const uint8_t* const* experts, float* y, moe_host_pool* pool);
 hipError_t launch_add_rows(void* out, int out_bf16, const float* y, size_t n, hipStream_t st);
+const char* host_simd_name();  // "avx512", "avx2" or "sse2"
 
 // ---------------------------------------------------------------- router projection
 struct RouterArgs {

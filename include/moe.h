@@ -293,6 +293,25 @@ typedef struct moe_host_pool moe_host_pool;
 moe_status moe_host_pool_create(int32_t n_threads, moe_host_pool** pool);
 void moe_host_pool_destroy(moe_host_pool* pool);
 
+/* Event for overlapping the host half with the GPU half.  `event` is a
+ * hipEvent_t created by the caller (NULL clears a pending one).  The calling
+ * thread's next moe_layer_forward call on the decode path records it on its
+ * stream as soon as the routing, the miss list and its count are written --
+ * after the first kernel (one token) or the routing kernel (2..4 tokens),
+ * before the experts' FFNs finish -- and then forgets it.  A caller that
+ * waits for the event can copy the miss list and run moe_host_miss_ffn while
+ * the GPU still computes the resident experts, as the pages' CPU and GPU
+ * work on one layer at the same time ([AF] section "命中率七成，代价是答案会
+ * 变").  Thread-local; no device work is done by this call itself. */
+moe_status moe_set_route_event(void* event);
+
+/* The row kernel moe_host_miss_ffn uses on this CPU: "avx512" (AVX-512F),
+ * "avx2" (AVX2 + FMA) or "sse2", chosen from the CPU flags the kernel
+ * reports; the environment variable MOE_HOST_SIMD=avx2 or =sse2 caps the
+ * choice (read at every call).  The pages' CPU side uses AVX-512/AVX2 ([SL]
+ * section "12GB 显存装下 1250 亿参数"). */
+const char* moe_host_simd(void);
+
 /* y[t] = sum over the misses of token t, in list order, of
  * gate * FFN_expert(xhat_t), for t < tokens (rows without misses are zero).
  *   x:        host [tokens][d_model], x_dtype MOE_BF16 or MOE_F32; flags as

@@ -138,3 +138,60 @@ def test_host_rows_do_not_depend_on_the_pool_size(g):
         outs.append(y)
     assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
     del torch
+
+
+@pytest.mark.parametrize("T", [1, 3])
+def test_route_event_marks_a_complete_miss_list(g, T):
+    """moe_set_route_event: the event completes once the miss list and its
+    count are final -- a copy taken on another stream right after the event
+    equals the list after the whole layer -- and the layer output does not
+    change with the event armed.  (The down kernel may still be running
+    when the copy is taken; that is the overlap the event is for.)"""
+    import ctypes
+    import torch
+    moe = g.moe
+    w = synth.WORKLOADS["slot_q3s_t1_48l"]
+    D, E, k = w["d_model"], w["n_experts"], w["top_k"]
+    shape = moe.MoeShape(D, w["d_ff"], E, k, w["d_ff_shared"], w["fmt"])
+    L = g.build_layer(shape, 0, 4, g.DEV)
+    resident = [int(e) for e in np.argsort(synth.expert_ranks(0, 4, E))[:128]]
+    slot_of = torch.full((E,), -1, dtype=torch.int32, device=g.DEV)
+    storage = torch.empty(len(resident) * L.stride, dtype=torch.uint8, device=g.DEV)
+    for s_, e in enumerate(resident):
+        slot_of[e] = s_
+        storage[s_ * L.stride:(s_ + 1) * L.stride].copy_(L.routed[e * L.stride:(e + 1) * L.stride])
+    table = L.table(slot_of=slot_of, n_slots=len(resident), routed=storage)
+    xb = synth.activations_bf16(0, 40 + T, T, D)
+    logits = g.f32_to_dev(synth.router_logits(0, 4, T, E, zipf_s=w["zipf_s"], alpha=w["alpha"]))
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+    hip.hipStreamWaitEvent.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    ev = ctypes.c_void_p()
+    assert hip.hipEventCreateWithFlags(ctypes.byref(ev), 2) == 0
+    side = torch.cuda.Stream()
+    run = g.LayerRun(shape, T, slots=True)
+    ref_out = run(table, g.u16_to_dev(xb), moe.MOE_BF16, logits, moe.MOE_F32)
+    ref_miss = run.misses()
+    assert len(ref_miss) > 0
+    for rep in range(3):
+        run.miss.fill_(-9)
+        run.miss_count.fill_(-7)
+        torch.cuda.synchronize()
+        out = torch.empty_like(ref_out)
+        moe.moe_set_route_event(ev.value)
+        moe.moe_layer_forward(shape, T, g.u16_to_dev(xb), moe.MOE_BF16, 0, logits, table, out,
+                              moe.MOE_F32, run.miss, T * k, run.miss_count, run.ws, run.ws_bytes)
+        assert hip.hipStreamWaitEvent(side.cuda_stream, ev.value, 0) == 0
+        with torch.cuda.stream(side):
+            m_early = run.miss.to("cpu", non_blocking=False)
+            c_early = run.miss_count.to("cpu", non_blocking=False)
+        side.synchronize()
+        n = int(c_early.item())
+        m = m_early[: 4 * n].numpy().reshape(n, 4)
+        gg = m[:, 3].copy().view(np.float32)
+        early = [(int(a), int(b), int(c), float(d)) for (a, b, c, _), d in zip(m, gg)]
+        torch.cuda.synchronize()
+        assert early == ref_miss, rep
+        assert torch.equal(out, ref_out)
+    hip.hipEventDestroy(ev)

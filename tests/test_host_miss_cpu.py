@@ -3,9 +3,9 @@
 Packed experts come from the oracle's packer (the GPU tests check the
 library's packer against it byte for byte) and the miss list is written out
 by hand in (token, rank) order.  The host rows are fp32 arithmetic on exact
-weights, so they must match the fp64 oracle to 1e-5 (relative L2) with either
-row-dot implementation: AVX2 + FMA where the CPU has them, and SSE2
-(MOE_HOST_SIMD=sse2).
+weights, so they must match the fp64 oracle to 1e-5 (relative L2) with every
+row-dot implementation: AVX-512F and AVX2 + FMA where the CPU has them, and
+SSE2 (MOE_HOST_SIMD caps the choice).
 """
 import numpy as np
 import pytest
@@ -36,9 +36,19 @@ def _experts(fmt, D, F):
     return _CACHE[key]
 
 
+def _cpu_flags():
+    for line in open("/proc/cpuinfo"):
+        if line.startswith("flags"):
+            return set(line.split(":", 1)[1].split())
+    return set()
+
+
+_FLAGS = _cpu_flags()
+
+
 @pytest.mark.parametrize("fmt", [synth.FMT_Q2SM, synth.FMT_Q3S, synth.FMT_Q2S])
 @pytest.mark.parametrize("D,F", [(256, 64), (3072, 512)])
-@pytest.mark.parametrize("simd", ["auto", "sse2"])
+@pytest.mark.parametrize("simd", ["avx512", "avx2", "sse2"])
 @pytest.mark.parametrize("threads", [1, 4])
 def test_host_miss_rows_match_the_oracle(monkeypatch, fmt, D, F, simd, threads):
     E = 16
@@ -49,10 +59,15 @@ def test_host_miss_rows_match_the_oracle(monkeypatch, fmt, D, F, simd, threads):
     rec = np.array([[t, j, e, np.array(g, np.float32).view(np.int32)] for (t, j, e, g) in _MISSES],
                    np.int32)
     y = np.full((_T, D), np.nan, np.float32)
-    if simd == "sse2":
-        monkeypatch.setenv("MOE_HOST_SIMD", "sse2")
-    else:
+    if simd == "avx512" and "avx512f" not in _FLAGS:
+        pytest.skip("this CPU has no AVX-512F")
+    if simd == "avx2" and not {"avx2", "fma"} <= _FLAGS:
+        pytest.skip("this CPU has no AVX2 + FMA")
+    if simd == "avx512":
         monkeypatch.delenv("MOE_HOST_SIMD", raising=False)
+    else:
+        monkeypatch.setenv("MOE_HOST_SIMD", simd)
+    assert moe.moe_host_simd() == simd
     pool = moe.HostPool(threads) if threads > 1 else None
     try:
         moe.moe_host_miss_ffn(shape, _T, x.ctypes.data, moe.MOE_F32, 0, rec.ctypes.data,
