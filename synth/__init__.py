@@ -34,15 +34,10 @@ reduction dimension of one output row):
   draw(key(field=2), block); the scale is drawn as for Q2SM.
 * Q2S (2-bit codes u in {0..3}, fp16 scale per block): codes and scale as
   for Q2SM, no min.
-* TAB_SCALE[i] = fp16_RNE(Phi^-1((i + 0.5) / 65536) * 0.02) and
+* TAB_SCALE[i] = fp16_RNE(|Phi^-1((i + 0.5) / 65536)| * 0.02) and
   TAB_MIN[i] = fp16_RNE(Phi^-1((i + 0.5) / 65536) * 0.01): 65536-point
-  inverse-CDF tables of N(0, 0.02) and N(0, 0.01) (standard deviations),
-  computed once in fp64.  fp16 subnormals are kept.  The scale is signed so
-  that every block's weights have zero mean in expectation in all three
-  formats (the codes alone have mean 1.5 for Q2SM and -0.5 for Q3S and Q2S),
-  as trained weights do; with one-signed scales every weight row shares a
-  bias, and a stack of layers then drives each token's output along one
-  common direction until the gates saturate or the values underflow.
+  inverse-CDF tables of |N(0, 0.02)| and N(0, 0.01) (standard deviations),
+  computed once in fp64.  fp16 subnormals are kept.
 
 Logical weight arrays of one expert with model width D and FFN width F:
 ``codes[3][F*D]`` (matrix 0 = W_gate [F][D], 1 = W_up [F][D], 2 = W_down
@@ -111,7 +106,7 @@ def tables():
         from scipy.special import ndtri
         p = (np.arange(65536, dtype=np.float64) + 0.5) / 65536.0
         z = ndtri(p)
-        ts = (z * 0.02).astype(np.float16).view(np.uint16)
+        ts = (np.abs(z) * 0.02).astype(np.float16).view(np.uint16)
         tm = (z * 0.01).astype(np.float16).view(np.uint16)
         _TABLES = (np.ascontiguousarray(ts), np.ascontiguousarray(tm))
     return _TABLES
