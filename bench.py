@@ -318,6 +318,54 @@ def bench_chain(ctx, stack, K, W, use_graph, T, slot=None):
     return res
 
 
+def bench_stack(ctx, stack, K, W, use_graph, T, slot=None):
+    """The same chained step as bench_chain, as one moe_decode_stack_forward
+    call: every layer's logits are inputs, so all 48 layers are routed by one
+    kernel at the head of the step and the layers run no routing step."""
+    torch, moe, synth = ctx.torch, ctx.moe, ctx.synth
+    w, shape, layers = stack
+    L, D, E = len(layers), w["d_model"], w["n_experts"]
+    logits = ctx.dev_f32(ctx.np.stack([synth.router_logits(0, l, T, E, zipf_s=w["zipf_s"],
+                                                           alpha=w["alpha"])
+                                       for l in range(L)])).reshape(-1)
+    x0 = ctx.dev_u16(synth.activations_bf16(0, 0, T, D))
+    wsb = moe.moe_decode_stack_workspace_bytes(shape, L, T)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=ctx.dev)
+    out = torch.empty(L * T * D, dtype=torch.int16, device=ctx.dev)
+    kcap = T * w["top_k"]
+    miss = torch.empty(L * kcap * 4, dtype=torch.int32, device=ctx.dev) if slot else None
+    mcount = torch.zeros(L, dtype=torch.int32, device=ctx.dev) if slot else None
+    tables = [ly.table() for ly in layers] if slot is None else list(slot)
+
+    def launch(i):
+        moe.moe_decode_stack_forward(shape, L, T, x0, moe.MOE_BF16, logits, tables, out,
+                                     moe.MOE_BF16, miss, mcount, ws, wsb)
+
+    launch(0)
+    torch.cuda.synchronize()
+    dt, _ = run_steps(ctx, launch, K, W, use_graph)
+    res = dict(tokens=K * T, seconds=dt)
+    if slot is None:
+        res["experts_per_layer"] = [u + 1 for u in unique_counts(
+            ctx, shape, [logits[l * T * E:(l + 1) * T * E] for l in range(L)], T)]
+    else:
+        m = mcount.cpu().tolist()
+        res["hit_rate"] = 1.0 - sum(m) / L / w["top_k"] / T
+        res["experts_per_layer"] = [w["top_k"] * T - mi + 1 for mi in m]
+    return res
+
+
+def stack_roofline(ctx, w, r, K):
+    shape = ctx.shape(w)
+    e_bytes = ctx.moe.moe_packed_expert_bytes(shape, w["d_ff"])
+    n = r["experts_per_layer"]
+    step_bytes = float(sum(n)) * e_bytes
+    ach = step_bytes / (r["seconds"] / K) / 1e9
+    return {"bound": "hbm", "scope": "whole step (48 layers)", "achieved": ach,
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": None,
+            "bytes_per_step": step_bytes}
+
+
 def bench_prefill(ctx, stack, K, W, use_graph, n_layers=4):
     """8192 tokens through one layer per step, rotating over n_layers layers."""
     torch, moe, synth = ctx.torch, ctx.moe, ctx.synth
@@ -896,6 +944,15 @@ def main():
                 ctx, "mtp_verify_t4_48l", 4)
         print("mtp_verify_t4_48l: %.3f ms/step" % (r["seconds"] / Kc * 1e3), file=sys.stderr,
               flush=True)
+        r = bench_stack(ctx, stack, Kc, 2, use_graph, T=4)
+        results["mtp_verify_t4_48l_stack"] = dict(
+            value=r["tokens"] / r["seconds"], unit="tokens/s", steps=Kc,
+            ms_per_step=r["seconds"] / Kc * 1e3,
+            config="mtp_verify_t4_48l as one moe_decode_stack_forward call: the 48 layers' "
+                   "logits are inputs, so all layers are routed at the head of the step",
+            roofline=stack_roofline(ctx, w, r, Kc))
+        print("mtp_verify_t4_48l_stack: %.3f ms/step" % (r["seconds"] / Kc * 1e3),
+              file=sys.stderr, flush=True)
     if "prefill_8192" in wl:
         if stack is None:
             stack = decode_stack(ctx, "prefill_8192", 4)
@@ -972,6 +1029,15 @@ def main():
         if not args.no_cpu:
             results["slot_q3s_t1_48l"]["cpu_baseline"] = cpu_baseline_chain(
                 ctx, "slot_q3s_t1_48l", 1)
+        r2 = bench_stack(ctx, sstack, Kc, 2, use_graph, T=1, slot=tables)
+        results["slot_q3s_t1_48l_stack"] = dict(
+            value=r2["tokens"] / r2["seconds"], unit="tokens/s", steps=Kc,
+            ms_per_step=r2["seconds"] / Kc * 1e3, hit_rate=r2["hit_rate"],
+            config="slot_q3s_t1_48l as one moe_decode_stack_forward call (all layers routed "
+                   "at the head of the step)",
+            roofline=stack_roofline(ctx, w, r2, Kc))
+        print("slot_q3s_t1_48l_stack: %.3f ms/step" % (r2["seconds"] / Kc * 1e3),
+              file=sys.stderr, flush=True)
         print("slot_q3s_t1_48l: %.3f ms/step hit %.3f" % (r["seconds"] / Kc * 1e3, r["hit_rate"]),
               file=sys.stderr, flush=True)
         del keep, tables, sstack

@@ -27,7 +27,8 @@ __all__ = [
     "moe_last_error", "moe_abi_version", "moe_set_kernel_timer", "moe_set_router_timer",
     "moe_slot_counts_take", "moe_slot_policy_plan", "moe_slot_table_stage",
     "moe_slot_table_commit", "HostPool", "moe_host_miss_ffn", "moe_add_rows",
-    "moe_set_route_event", "moe_host_simd",
+    "moe_set_route_event", "moe_host_simd", "moe_decode_stack_workspace_bytes",
+    "moe_decode_stack_forward",
     "LIB_PATH",
 ]
 
@@ -120,6 +121,9 @@ _sigs = {
                                _P, _P]),
     "moe_add_rows": (_I, [_P, _I, _P, _I, _I, _P]),
     "moe_set_route_event": (_I, [_P]),
+    "moe_decode_stack_workspace_bytes": (_Z, [ctypes.POINTER(MoeShape), _I, _I]),
+    "moe_decode_stack_forward": (_I, [ctypes.POINTER(MoeShape), _I, _I, _P, _I, _P, _P, _P, _I,
+                                      _P, _P, _P, _Z, _P]),
     "moe_host_simd": (ctypes.c_char_p, []),
 }
 for _name, (_res, _args) in _sigs.items():
@@ -335,3 +339,17 @@ def moe_set_route_event(event):
 
 def moe_host_simd() -> str:
     return _lib.moe_host_simd().decode()
+
+
+def moe_decode_stack_workspace_bytes(shape, layers, tokens) -> int:
+    return _lib.moe_decode_stack_workspace_bytes(ctypes.byref(shape), layers, tokens)
+
+
+def moe_decode_stack_forward(shape, layers, tokens, x, x_dtype, logits, tables, out, out_dtype,
+                             miss, miss_count, ws, ws_bytes, stream=None):
+    """tables: a sequence of `layers` MoeExpertTable (copied into one host array)."""
+    arr = (MoeExpertTable * max(layers, 1))(*tables)
+    _check(_lib.moe_decode_stack_forward(ctypes.byref(shape), layers, tokens, _ptr(x), x_dtype,
+                                         _ptr(logits), ctypes.cast(arr, _P), _ptr(out), out_dtype,
+                                         _ptr(miss), _ptr(miss_count), _ptr(ws), ws_bytes,
+                                         _stream(stream)))

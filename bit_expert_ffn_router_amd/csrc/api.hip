@@ -169,6 +169,36 @@ size_t moe_workspace_bytes(const moe_shape* shape, int32_t tokens) {
 
 namespace {
 
+// Checks of one expert table against the shape (shared by the layer and the
+// stack entry points).
+moe_status check_table(const moe_shape* shape, const moe_expert_table* table) {
+  if (!table) return fail(MOE_EINVAL, "table is NULL");
+  const size_t need_e = moe::packed_bytes(shape->d_model, shape->d_ff, shape->qfmt);
+  if (!table->routed) return fail(MOE_EINVAL, "table->routed is NULL");
+  if (table->expert_stride < need_e || table->expert_stride % 256 != 0)
+    return fail(MOE_EINVAL, "expert_stride %zu must be >= %zu and a multiple of 256",
+                table->expert_stride, need_e);
+  if (!aligned256(table->routed)) return fail(MOE_EINVAL, "table->routed must be 256-byte aligned");
+  if ((shape->d_ff_shared > 0) != (table->shared != nullptr))
+    return fail(MOE_EINVAL, "table->shared must be given iff d_ff_shared > 0");
+  if (table->shared && !aligned256(table->shared))
+    return fail(MOE_EINVAL, "table->shared must be 256-byte aligned");
+  if (table->router && ((uintptr_t)table->router & 15u))
+    return fail(MOE_EINVAL, "table->router must be 16-byte aligned");
+  if (table->use_count && ((uintptr_t)table->use_count & 3u))
+    return fail(MOE_EINVAL, "table->use_count must be 4-byte aligned");
+  if (table->slot_of && table->n_slots <= 0)
+    return fail(MOE_EINVAL, "n_slots must be > 0 with a slot table");
+  return ok();
+}
+
+size_t stack_ws_bytes(const moe_shape* s, int L, int T) {
+  if (L <= 0 || T <= 0) return 0;
+  const size_t plan = moe::decode_plan_bytes(T, s->n_experts, s->top_k);
+  return (size_t)L * plan +
+         moe::decode_ws_bytes(T, s->d_model, s->d_ff, s->d_ff_shared, s->n_experts, s->top_k);
+}
+
 // The layer call behind both entry points.  ws == nullptr with noalloc:
 // the decode path's workspace is the library's per-device static scratch.
 moe_status layer_forward_impl(const moe_shape* shape, int32_t tokens, const void* x,
@@ -230,7 +260,7 @@ moe_status layer_forward_impl(const moe_shape* shape, int32_t tokens, const void
   if (use_decode_path(T)) {
     if (shape->d_model > 4096 || shape->d_ff > 512 || shape->d_ff_shared > 512)
       return fail(MOE_EUNSUPPORTED, "decode path supports d_model <= 4096, d_ff <= 512");
-    moe::DecodeArgs a;
+    moe::DecodeArgs a = {};
     a.T = T;
     a.D = shape->d_model;
     a.F = shape->d_ff;
@@ -295,6 +325,112 @@ moe_status moe_layer_forward(const moe_shape* shape, int32_t tokens, const void*
                              size_t ws_bytes, moe_stream_t stream) {
   return layer_forward_impl(shape, tokens, x, x_dtype, flags, router_logits, table, out, out_dtype,
                             miss, miss_cap, miss_count, ws, ws_bytes, false, stream);
+}
+
+size_t moe_decode_stack_workspace_bytes(const moe_shape* shape, int32_t layers, int32_t tokens) {
+  if (check_shape(shape) != MOE_OK || layers < 0 || tokens < 0 || tokens > moe::kDecodeMaxT)
+    return 0;
+  return stack_ws_bytes(shape, layers, tokens);
+}
+
+moe_status moe_decode_stack_forward(const moe_shape* shape, int32_t layers, int32_t tokens,
+                                    const void* x, int32_t x_dtype, const float* logits,
+                                    const moe_expert_table* tables, void* out, int32_t out_dtype,
+                                    moe_miss* miss, int32_t* miss_count, void* ws,
+                                    size_t ws_bytes, moe_stream_t stream) {
+  moe_status s = check_shape(shape);
+  if (s != MOE_OK) return s;
+  const int L = layers, T = tokens;
+  if (L < 0 || T < 0) return fail(MOE_EINVAL, "layers %d and tokens %d must be >= 0", L, T);
+  if (T > moe::kDecodeMaxT)
+    return fail(MOE_EUNSUPPORTED, "the stack runs the decode path: tokens <= %d", moe::kDecodeMaxT);
+  if (x_dtype != MOE_BF16 && x_dtype != MOE_F32) return fail(MOE_EINVAL, "bad x_dtype %d", (int)x_dtype);
+  if (out_dtype != MOE_BF16 && out_dtype != MOE_F32)
+    return fail(MOE_EINVAL, "bad out_dtype %d", (int)out_dtype);
+  if (shape->d_model > 4096 || shape->d_ff > 512 || shape->d_ff_shared > 512)
+    return fail(MOE_EUNSUPPORTED, "decode path supports d_model <= 4096, d_ff <= 512");
+  if (L == 0 || T == 0) return ok();
+  if (!tables) return fail(MOE_EINVAL, "tables is NULL");
+  bool any_slots = false;
+  for (int l = 0; l < L; ++l) {
+    s = check_table(shape, &tables[l]);
+    if (s != MOE_OK) {
+      char msg[256];
+      snprintf(msg, sizeof msg, "%s", g_err);  // fail() rewrites g_err
+      return fail(s, "layer %d: %s", l, msg);
+    }
+    if (tables[l].router)
+      return fail(MOE_EUNSUPPORTED, "layer %d: the stack takes logits, not a router", l);
+    any_slots = any_slots || tables[l].slot_of != nullptr;
+  }
+  if (any_slots && (!miss || !miss_count))
+    return fail(MOE_EINVAL, "slot tables need miss ([layers][tokens*top_k]) and miss_count ([layers])");
+  if (!x || !logits || !out || !ws) return fail(MOE_EINVAL, "x, logits, out and ws are required");
+  if (!aligned256(ws)) return fail(MOE_EINVAL, "ws must be 256-byte aligned");
+  if (((uintptr_t)x & 15u) || ((uintptr_t)logits & 3u) || ((uintptr_t)out & 15u))
+    return fail(MOE_EINVAL, "x and out must be 16-byte aligned, logits 4-byte aligned");
+  const size_t need = stack_ws_bytes(shape, L, T);
+  if (ws_bytes < need) return fail(MOE_ENOSPACE, "ws_bytes %zu < %zu", ws_bytes, need);
+
+  const int D = shape->d_model, E = shape->n_experts, k = shape->top_k;
+  const size_t plan_bytes = moe::decode_plan_bytes(T, E, k);
+  uint8_t* plan = (uint8_t*)ws;
+  const moe::DecodeWs base = moe::decode_ws_carve(plan + (size_t)L * plan_bytes, T, D,
+                                                  shape->d_ff, shape->d_ff_shared, E, k);
+  hipStream_t st = (hipStream_t)stream;
+  // 1. The routing of every layer.
+  for (int l0 = 0; l0 < L; l0 += moe::kPlanLayers) {
+    moe::PlanArgs p = {};
+    p.T = T;
+    p.E = E;
+    p.k = k;
+    p.n = L - l0 < moe::kPlanLayers ? L - l0 : moe::kPlanLayers;
+    p.logits = logits + (size_t)l0 * T * E;
+    p.miss = any_slots ? (moe::MissRec*)miss + (size_t)l0 * T * k : nullptr;
+    p.miss_count = any_slots ? miss_count + l0 : nullptr;
+    p.plan = plan + (size_t)l0 * plan_bytes;
+    p.plan_bytes = plan_bytes;
+    for (int i = 0; i < p.n; ++i) {
+      const moe_expert_table& t = tables[l0 + i];
+      p.slot_of[i] = t.slot_of;
+      p.n_slots[i] = t.n_slots;
+      p.use_count[i] = t.slot_of ? t.use_count : nullptr;
+      p.has_shared[i] = t.shared != nullptr;
+    }
+    s = hip_status(moe::launch_decode_plan(p, st), "plan launch");
+    if (s != MOE_OK) return s;
+  }
+  // 2. The layers, each on its own list; layer l > 0 reads layer l - 1's
+  // output with the RMS rule.
+  const size_t out_row = (size_t)T * D * (out_dtype == MOE_BF16 ? 2 : 4);
+  for (int l = 0; l < L; ++l) {
+    const moe_expert_table& t = tables[l];
+    moe::DecodeArgs a = {};
+    a.T = T;
+    a.D = D;
+    a.F = shape->d_ff;
+    a.Fs = shape->d_ff_shared;
+    a.E = E;
+    a.k = k;
+    a.fmt = shape->qfmt;
+    a.x = l == 0 ? x : (const void*)((const uint8_t*)out + (size_t)(l - 1) * out_row);
+    a.x_bf16 = l == 0 ? x_dtype == MOE_BF16 : out_dtype == MOE_BF16;
+    a.rmsnorm = l > 0;
+    a.logits = logits + (size_t)l * T * E;
+    a.routed = (const uint8_t*)t.routed;
+    a.stride = t.expert_stride;
+    a.slot_of = t.slot_of;
+    a.n_slots = t.n_slots;
+    a.shared = (const uint8_t*)t.shared;
+    a.out = (uint8_t*)out + (size_t)l * out_row;
+    a.out_bf16 = out_dtype == MOE_BF16;
+    a.planned = 1;
+    moe::DecodeWs w = base;
+    moe::decode_plan_carve(plan + (size_t)l * plan_bytes, T, E, k, w);
+    s = hip_status(moe::launch_decode(a, w, st), "decode launch");
+    if (s != MOE_OK) return s;
+  }
+  return ok();
 }
 
 moe_status moe_layer_forward_noalloc(const moe_shape* shape, int32_t tokens, const void* x,

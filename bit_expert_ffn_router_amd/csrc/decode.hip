@@ -93,6 +93,12 @@ DecodeWs decode_ws_carve(void* ws, int T, int D, int F, int Fs, int E, int k) {
   return w;
 }
 
+size_t decode_plan_bytes(int T, int E, int k) {
+  const int Wmax = (E < T * k ? E : T * k) + 1;
+  return align256(4 * (size_t)T * k) * 2 + 256 + align256(4 * (size_t)Wmax) +
+         align256(16 * (size_t)Wmax);
+}
+
 // ----------------------------------------------------------------------------
 // Routing inside a decode block.
 
@@ -496,7 +502,7 @@ struct GuLds {
 
 // Gate/up work item vb (the block index of decode_gateup_kernel).  Returns
 // early, with the same decision in every wave, when its list entry is unused.
-template <int T, int FMT, int XM>
+template <int T, int FMT, int XM, bool PLANNED>
 __device__ __forceinline__ void gateup_body(const DecodeArgs& a, const DecodeWs& w, int vb,
                                             GuLds& L, uint4* s_dyn) {
   RouteLds& R = L.R;
@@ -530,7 +536,7 @@ __device__ __forceinline__ void gateup_body(const DecodeArgs& a, const DecodeWs&
     const int ui = rb / gpr;
     g = rb % gpr;
     int ref;
-    if (T == 1) {
+    if (T == 1 && !PLANNED) {
       int e;
       float gt;
       route_token(a, 0, lane, s_topk[wv], e, gt);
@@ -542,7 +548,7 @@ __device__ __forceinline__ void gateup_body(const DecodeArgs& a, const DecodeWs&
       const unsigned long long pick =
           __ballot(((hits >> lane) & 1ull) && __popcll(hits & below) == ui);
       ref = __builtin_amdgcn_readlane(rl, __builtin_ctzll(pick));
-    } else {  // the list was built by decode_list_kernel
+    } else {  // the list was built by decode_list_kernel or decode_plan_kernel
       const int nu = *w.nwork;
       if (has_sh + ui >= nu) return;
       ref = w.work_ref[has_sh + ui];
@@ -568,7 +574,7 @@ __device__ __forceinline__ void gateup_body(const DecodeArgs& a, const DecodeWs&
   float rinv[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) rinv[t] = 1.f;
-  if (RMS && T > 1) {  // published by decode_list_kernel
+  if (RMS && T > 1 && !PLANNED) {  // published by decode_list_kernel
 #pragma unroll
     for (int t = 0; t < T; ++t) rinv[t] = w.rinv[t];
   }
@@ -590,7 +596,13 @@ __device__ __forceinline__ void gateup_body(const DecodeArgs& a, const DecodeWs&
   const DnPrefetch dpf = prefetch_down_rows(eb, D, Fu_pf, rec_bytes(FMT),
                                             down_offset(D, Fu_pf, FMT), vb, vb - g, Fu_pf / 16,
                                             tid, kGuThreads);
-  if (RMS && T == 1) {
+  // The RMS factors of the input, in-block (one token, or a planned call).
+  // With 2..4 bf16 tokens of a planned call the raw pieces go to LDS first
+  // and come back after the block-wide sum, so they are not held in
+  // registers (beside the weight records in flight) across the barrier.
+  constexpr bool RMS_IN_BLOCK = RMS && (T == 1 || PLANNED);
+  constexpr bool TWO_PASS = RMS_IN_BLOCK && T > 1 && in_bf16;
+  if constexpr (RMS_IN_BLOCK) {
     float ss[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) ss[t] = 0.f;
@@ -609,6 +621,9 @@ __device__ __forceinline__ void gateup_body(const DecodeArgs& a, const DecodeWs&
       }
 #pragma unroll
       for (int tt = 0; tt < T; ++tt) ss[tt] += tt == t ? q2 : 0.f;  // invalid pieces are 0
+      if constexpr (TWO_PASS) {
+        if (i < nin) s_xhi[t * D8p + i % D8] = xr[j];  // raw, normalised in place below
+      }
     }
 #pragma unroll
     for (int t = 0; t < T; ++t) {
@@ -622,6 +637,13 @@ __device__ __forceinline__ void gateup_body(const DecodeArgs& a, const DecodeWs&
 #pragma unroll
       for (int w2 = 0; w2 < kGuWaves; ++w2) ssum += s_ss[w2][t];
       rinv[t] = 1.0f / sqrtf(ssum / (float)D + 1e-6f);
+    }
+    if constexpr (TWO_PASS) {
+#pragma unroll
+      for (int j = 0; j < XJ; ++j) {  // each thread reads back the pieces it wrote
+        const int i = tid + kGuThreads * j;
+        xr[j] = i < nin ? s_xhi[(i / D8) * D8p + i % D8] : make_uint4(0, 0, 0, 0);
+      }
     }
   }
   // bf16 operand(s) to LDS, and per-block sums X = sum x, X' = sum c x of the
@@ -707,7 +729,7 @@ __device__ __forceinline__ void gateup_body(const DecodeArgs& a, const DecodeWs&
         return lo ? s_xlo[idx] : s_xhi[idx];
       };
       auto xsum = [&](int beta, int t) -> float2 { return s_xs[t * nbD + 8 * o + beta]; };
-      record_gemv<T, FMT, HAS_LO, true>(cw[i], hw[i], pa[i], pb[i], 8, kc, xfrag, xsum, acc, mt, q);
+      record_gemv<T, FMT, HAS_LO, true, (T > 1 ? 4 : 8)>(cw[i], hw[i], pa[i], pb[i], 8, kc, xfrag, xsum, acc, mt, q);
     }
   }
 #pragma unroll
@@ -824,11 +846,46 @@ __global__ __launch_bounds__(2 * kGuThreads) void decode_list_kernel(DecodeArgs 
   if (wv == 0) build_list<T>(a, w, R, s_first, lane, true, a.shared != nullptr ? 1 : 0);
 }
 
-template <int T, int FMT, int XM>
+// One layer of a stack per block: wave t routes token t of the layer, then
+// wave 0 builds and publishes the layer's list, routing, miss list and usage
+// counts into the layer's plan area, exactly as decode_list_kernel (2..4
+// tokens) and the one-token gate/up kernel do for a single layer call.
+template <int T>
+__global__ __launch_bounds__(kGuThreads) void decode_plan_kernel(PlanArgs p) {
+  extern __shared__ int32_t s_first[];  // [E]
+  __shared__ RouteLds R;
+  __shared__ TopkScratch s_topk[kGuWaves];
+  const int l = blockIdx.x, lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  DecodeArgs a = {};
+  a.T = T;
+  a.E = p.E;
+  a.k = p.k;
+  a.logits = p.logits + (size_t)l * T * p.E;
+  a.slot_of = p.slot_of[l];
+  a.n_slots = p.n_slots[l];
+  a.use_count = p.use_count[l];
+  a.miss = p.miss ? p.miss + (size_t)l * T * p.k : nullptr;
+  a.miss_count = p.miss_count ? p.miss_count + l : nullptr;
+  DecodeWs w = {};
+  decode_plan_carve(p.plan + (size_t)l * p.plan_bytes, T, p.E, p.k, w);
+  if (wv < T) {
+    int e;
+    float gt;
+    route_token(a, wv, lane, s_topk[wv], e, gt);
+    if (lane < a.k) {
+      R.e[wv * a.k + lane] = e;
+      R.g[wv * a.k + lane] = gt;
+    }
+  }
+  __syncthreads();
+  if (wv == 0) build_list<T>(a, w, R, s_first, lane, true, p.has_shared[l]);
+}
+
+template <int T, int FMT, int XM, bool PLANNED>
 __global__ __launch_bounds__(kGuThreads, 2) void decode_gateup_kernel(DecodeArgs a, DecodeWs w) {
   extern __shared__ uint4 s_dyn[];
   __shared__ GuLds L;
-  gateup_body<T, FMT, XM>(a, w, (int)blockIdx.x, L, s_dyn);
+  gateup_body<T, FMT, XM, PLANNED>(a, w, (int)blockIdx.x, L, s_dyn);
 }
 
 
@@ -956,14 +1013,15 @@ __global__ __launch_bounds__(1024) void decode_down_kernel(DecodeArgs a, DecodeW
 
 template <int T, int FMT, int XM>
 static hipError_t launch_decode_x(const DecodeArgs& a, const DecodeWs& w, hipStream_t st) {
-  static std::atomic<size_t> lds_gu[kMaxDevices], lds_dn[kMaxDevices];  // per device (allow_lds)
+  static std::atomic<size_t> lds_gu[kMaxDevices], lds_gp[kMaxDevices], lds_dn[kMaxDevices];
   const int D8 = a.D / 8, nbD = a.D / 32;
   const int D8p = D8 + (T > 1 ? 1 : 0);  // padded token rows (see gateup_body)
   const size_t lds = (size_t)T * D8p * 16 * (XM == kXF32 ? 2 : 1) + (size_t)T * nbD * 8;
   const size_t lds_down =
       (size_t)kDnWaves * ((size_t)T * 2 * (w.Fp / 8) + (size_t)T * (w.Fp / 32) / 2) * 16;
   hipError_t e;
-  if ((e = allow_lds(decode_gateup_kernel<T, FMT, XM>, lds, lds_gu)) != hipSuccess) return e;
+  if ((e = allow_lds(decode_gateup_kernel<T, FMT, XM, false>, lds, lds_gu)) != hipSuccess) return e;
+  if ((e = allow_lds(decode_gateup_kernel<T, FMT, XM, true>, lds, lds_gp)) != hipSuccess) return e;
   if ((e = allow_lds(decode_down_kernel<T, FMT>, lds_down, lds_dn)) != hipSuccess) return e;
   const int nblk = (a.shared ? a.Fs / 16 : 0) + (w.Wmax - 1) * (a.F / 16);
   // The caller's route event (moe_set_route_event), recorded as soon as the
@@ -975,13 +1033,14 @@ static hipError_t launch_decode_x(const DecodeArgs& a, const DecodeWs& w, hipStr
     re.before = nullptr;
     return hipEventRecord(ev, st);
   };
-  if constexpr (T > 1) {
+  if (T > 1 && !a.planned) {
     decode_list_kernel<T><<<1, 2 * kGuThreads, (size_t)a.E * 4, st>>>(a, w);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = route_done()) != hipSuccess) return e;
   }
-  if ((e = launch_timed(decode_gateup_kernel<T, FMT, XM>, dim3(nblk), dim3(kGuThreads),
-                        (uint32_t)lds, st, a, w)) != hipSuccess)
+  if ((e = launch_timed(a.planned ? decode_gateup_kernel<T, FMT, XM, true>
+                                  : decode_gateup_kernel<T, FMT, XM, false>,
+                        dim3(nblk), dim3(kGuThreads), (uint32_t)lds, st, a, w)) != hipSuccess)
     return e;
   if constexpr (T == 1) {
     if ((e = route_done()) != hipSuccess) return e;
@@ -996,6 +1055,19 @@ static hipError_t launch_decode_t(const DecodeArgs& a, const DecodeWs& w, hipStr
                                  : launch_decode_x<T, FMT, kXRmsF32>(a, w, st);
   if (a.x_bf16) return launch_decode_x<T, FMT, kXBf16>(a, w, st);
   return launch_decode_x<T, FMT, kXF32>(a, w, st);
+}
+
+hipError_t launch_decode_plan(const PlanArgs& p, hipStream_t st) {
+  if (p.n <= 0) return hipSuccess;
+  const size_t lds = (size_t)p.E * 4;
+  switch (p.T) {
+    case 1: decode_plan_kernel<1><<<p.n, kGuThreads, lds, st>>>(p); break;
+    case 2: decode_plan_kernel<2><<<p.n, kGuThreads, lds, st>>>(p); break;
+    case 3: decode_plan_kernel<3><<<p.n, kGuThreads, lds, st>>>(p); break;
+    case 4: decode_plan_kernel<4><<<p.n, kGuThreads, lds, st>>>(p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeArgs& a, const DecodeWs& w, hipStream_t st) {

@@ -130,6 +130,8 @@ struct DecodeArgs {
   MissRec* miss;
   int32_t* miss_count;
   uint32_t* use_count;  // NULL, or [E]: +1 per routed pair (slot policy statistics)
+  int planned;          // 1: the routing and list are already in the workspace
+                        // (decode_plan_kernel); the RMS rule is applied in-block
 };
 
 size_t decode_ws_bytes(int T, int D, int F, int Fs, int E, int k);
@@ -142,6 +144,43 @@ constexpr size_t kNoAllocScratchBytes = (size_t)2 << 20;
 hipError_t noalloc_scratch(void** ptr);
 DecodeWs decode_ws_carve(void* ws, int T, int D, int F, int Fs, int E, int k);
 hipError_t launch_decode(const DecodeArgs& a, const DecodeWs& w, hipStream_t st);
+
+// Decode through a stack of layers whose logits are all known up front: one
+// launch routes every layer (decode_plan_kernel), then each layer runs its
+// gate/up and down kernels on its precomputed list.  Per layer the
+// workspace holds a plan area (routing, list, gates); the h buffers are
+// shared by the layers.
+constexpr int kPlanLayers = 64;  // layers per plan launch (kernel-argument size)
+struct PlanArgs {
+  int T, E, k, n;                // n: layers of this launch
+  const float* logits;           // [n][T][E]
+  MissRec* miss;                 // [n][T*k] or NULL (no slot tables)
+  int32_t* miss_count;           // [n] or NULL
+  uint8_t* plan;                 // [n][plan_bytes]
+  size_t plan_bytes;
+  const int32_t* slot_of[kPlanLayers];
+  uint32_t* use_count[kPlanLayers];
+  int n_slots[kPlanLayers];
+  int has_shared[kPlanLayers];
+};
+size_t decode_plan_bytes(int T, int E, int k);
+// The plan area of one layer as the routing part of a DecodeWs (idx, gate,
+// nwork, work_ref, work_gate); the other fields are left unset.
+__host__ __device__ inline void decode_plan_carve(void* plan, int T, int E, int k, DecodeWs& w) {
+  const int Wmax = (E < T * k ? E : T * k) + 1;
+  auto al = [](size_t v) { return (v + 255) / 256 * 256; };
+  uint8_t* q = (uint8_t*)plan;
+  w.idx = (int32_t*)q;
+  q += al(4 * (size_t)T * k);
+  w.gate = (float*)q;
+  q += al(4 * (size_t)T * k);
+  w.nwork = (int32_t*)q;
+  q += 256;
+  w.work_ref = (int32_t*)q;
+  q += al(4 * (size_t)Wmax);
+  w.work_gate = (float*)q;
+}
+hipError_t launch_decode_plan(const PlanArgs& p, hipStream_t st);
 
 // ---------------------------------------------------------------- host miss path
 }  // namespace moe

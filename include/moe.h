@@ -277,6 +277,40 @@ moe_status moe_layer_forward_noalloc(const moe_shape* shape, int32_t tokens,
                                      moe_miss* miss, int32_t miss_cap, int32_t* miss_count,
                                      moe_stream_t stream);
 
+/* Decode through `layers` chained layers in one call, for inputs whose
+ * router logits are known for every layer when the call is made (the pages
+ * verify 1 + 3 draft tokens through all 48 layers together, [AF] section
+ * "命中率七成，代价是答案会变"; here the logits of every layer are inputs).
+ * One kernel routes all layers at once (top-k, gates, the list of distinct
+ * resident experts, miss lists and usage counts); then each layer runs the
+ * same expert kernels as moe_layer_forward on its precomputed list, so a
+ * layer no longer starts with a routing step.
+ *   tokens:   1..4 (the decode path; 0 or layers == 0: nothing is launched).
+ *   x:        device [tokens][d_model], x_dtype, the input of layer 0 (taken
+ *             as it is).  Layer l > 0 takes layer l - 1's output with the
+ *             RMS rule of MOE_FLAG_RMSNORM_INPUT.
+ *   logits:   device fp32 [layers][tokens][n_experts], finite.
+ *   tables:   host array of `layers` expert tables (as for
+ *             moe_layer_forward; slot tables allowed, routers are not:
+ *             MOE_EUNSUPPORTED).
+ *   out:      device [layers][tokens][d_model], out_dtype: every layer's
+ *             output (with a slot table, its partial output).
+ *   miss, miss_count: required when any table has a slot table: device
+ *             [layers][tokens*top_k] and [layers], filled per layer as
+ *             moe_layer_forward fills them (NULL otherwise).
+ *   ws:       device, moe_decode_stack_workspace_bytes(shape, layers,
+ *             tokens) bytes, 256-byte aligned.
+ * Same results as chaining moe_layer_forward calls with the RMS flag: bit
+ * for bit with one token; with 2..4 the RMS factors are summed in another
+ * order (a bf16 input value may differ by one unit in rare ties).
+ * Validation, errors and determinism as for moe_layer_forward. */
+size_t moe_decode_stack_workspace_bytes(const moe_shape* shape, int32_t layers, int32_t tokens);
+moe_status moe_decode_stack_forward(const moe_shape* shape, int32_t layers, int32_t tokens,
+                                    const void* x, int32_t x_dtype, const float* logits,
+                                    const moe_expert_table* tables, void* out, int32_t out_dtype,
+                                    moe_miss* miss, int32_t* miss_count, void* ws,
+                                    size_t ws_bytes, moe_stream_t stream);
+
 /* Host half of the slot-mode layer.  The pages compute the experts that are
  * not on the GPU with the CPU, at the same time as the GPU computes its own,
  * and add both into the same layer ([AF] section "命中率七成，代价是答案会
