@@ -61,8 +61,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workloads",
                     default="decode_t1,mtp_verify_t4_48l,prefill_8192,slot_q3s_t1_48l,decode_q2s_t1,"
-                            "decode_router_t1,prefill_router_8192,slot_policy_q3s_t1_8l,"
-                            "slot_host_q3s_t1_8l")
+                            "prefill_q3s_8192,prefill_slot_q3s_8192,decode_router_t1,"
+                            "prefill_router_8192,slot_policy_q3s_t1_8l,slot_host_q3s_t1_8l")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-graph", action="store_true", help="launch steps eagerly")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -366,10 +366,12 @@ def stack_roofline(ctx, w, r, K):
             "bytes_per_step": step_bytes}
 
 
-def bench_prefill(ctx, stack, K, W, use_graph, n_layers=4):
-    """8192 tokens through one layer per step, rotating over n_layers layers."""
+def bench_prefill(ctx, stack, K, W, use_graph, n_layers=4, name="prefill_8192", slot=None):
+    """8192 tokens through one layer per step, rotating over n_layers layers
+    (with `slot`, the layers' slot tables: the partial layer and its miss
+    list)."""
     torch, moe, synth = ctx.torch, ctx.moe, ctx.synth
-    w = synth.WORKLOADS["prefill_8192"]
+    w = synth.WORKLOADS[name]
     _, shape, layers = stack
     L, T, D = min(n_layers, len(layers)), w["tokens"], w["d_model"]
     logits = [ctx.dev_f32(synth.router_logits(0, l, T, w["n_experts"], zipf_s=w["zipf_s"],
@@ -378,22 +380,33 @@ def bench_prefill(ctx, stack, K, W, use_graph, n_layers=4):
     wsb = moe.moe_workspace_bytes(shape, T)
     ws = torch.empty(wsb, dtype=torch.uint8, device=ctx.dev)
     out = torch.empty(T * D, dtype=torch.int16, device=ctx.dev)
-    tables = [layers[l].table() for l in range(L)]
+    tables = [layers[l].table() for l in range(L)] if slot is None else list(slot[:L])
+    kcap = T * w["top_k"]
+    miss = torch.empty(kcap * 4, dtype=torch.int32, device=ctx.dev) if slot else None
+    mcount = torch.zeros(L, dtype=torch.int32, device=ctx.dev) if slot else None
 
     def launch(i):
         l = i % L
         moe.moe_layer_forward(shape, T, xs[l], moe.MOE_BF16, 0, logits[l], tables[l], out,
-                              moe.MOE_BF16, None, 0, None, ws, wsb)
+                              moe.MOE_BF16, miss, kcap if slot else 0,
+                              mcount[l:l + 1] if slot else None, ws, wsb)
 
-    launch(0)
+    for l in range(L):
+        launch(l)
     torch.cuda.synchronize()
+    misses = mcount.cpu().tolist() if slot else [0] * L
     dt, kms = run_steps(ctx, launch, K, W, use_graph, timer_events=True)
-    rows = T * w["top_k"] + T                       # routed pairs + shared-expert rows
+    # rows of the grouped GEMMs: the computed pairs (all, or the hits) + the
+    # shared expert's T rows; FLOP averaged over the rotated layers
+    rows = T * w["top_k"] - sum(misses) / L + T
     flops_gu = 2.0 * rows * D * 2 * w["d_ff"]       # gate/up grouped GEMM
     flops_layer = flops_gu + 2.0 * rows * w["d_ff"] * D
     kavg = sum(kms) / len(kms) * 1e-3
-    return dict(tokens=K * T, seconds=dt, kernel_s=kavg, flops_per_launch=flops_gu,
-                flops_layer=flops_layer)
+    res = dict(tokens=K * T, seconds=dt, kernel_s=kavg, flops_per_launch=flops_gu,
+               flops_layer=flops_layer)
+    if slot:
+        res["hit_rate"] = 1.0 - sum(misses) / L / kcap
+    return res
 
 
 def bench_router(ctx, stack, K, W, use_graph, T, n_layers):
@@ -423,13 +436,13 @@ def bench_router(ctx, stack, K, W, use_graph, T, n_layers):
                 router_bytes=E * D * 2 + T * D * 2 + T * E * 4, router_flops=2.0 * T * E * D)
 
 
-def build_slot_stack(ctx, name):
+def build_slot_stack(ctx, name, n_layers=None):
     torch, moe, synth, np = ctx.torch, ctx.moe, ctx.synth, ctx.np
     w = synth.WORKLOADS[name]
     shape = ctx.shape(w)
     E, S = w["n_experts"], w["n_slots"]
     tables, keep = [], []
-    for l in range(w["layers"]):
+    for l in range(n_layers or w["layers"]):
         ranks = synth.expert_ranks(0, l, E)
         resident = [int(e) for e in np.argsort(ranks)[:S]]          # the S most popular
         staged = ctx.build_layer(shape, 0, l, ctx.dev, experts=resident)
@@ -976,6 +989,34 @@ def main():
             results["prefill_8192"]["cpu_baseline"] = cpu_baseline_prefill(ctx)
         print("prefill_8192: %.3f ms/step, gate/up kernel %.1f us (%.1f TFLOP/s)" %
               (sps * 1e3, r["kernel_s"] * 1e6, achieved), file=sys.stderr, flush=True)
+    for name in ("prefill_q3s_8192", "prefill_slot_q3s_8192"):
+        if name not in wl:
+            continue
+        if name == "prefill_q3s_8192":
+            pstack, ptables, pkeep = decode_stack(ctx, name, 4), None, None
+            cfg = "8192 tokens x 1 layer (rotated over 4 resident layers), Q3S, bf16 in/out"
+        else:
+            pstack, ptables, pkeep = build_slot_stack(ctx, name, 4)
+            cfg = ("8192 tokens x 1 layer (rotated over 4 layers), Q3S, 128 of 512 experts "
+                   "resident per layer: partial layer + miss list")
+        Kp = max(10, K // 48)
+        r = bench_prefill(ctx, pstack, Kp, 2, use_graph, name=name, slot=ptables)
+        sps = r["seconds"] / Kp
+        achieved = r["flops_per_launch"] / r["kernel_s"] / 1e12
+        results[name] = dict(
+            value=r["tokens"] / r["seconds"], unit="tokens/s", steps=Kp, ms_per_step=sps * 1e3,
+            config=cfg, layer_mfma_frac=r["flops_layer"] / sps / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            roofline={"bound": "mfma",
+                      "kernel": "pf_gemm_kernel<0, Q3S> (gate/up grouped GEMM + SwiGLU)",
+                      "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                      "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                      "flops_per_launch": r["flops_per_launch"],
+                      "kernel_us": r["kernel_s"] * 1e6})
+        if "hit_rate" in r:
+            results[name]["hit_rate"] = r["hit_rate"]
+        print("%s: %.3f ms/step, gate/up kernel %.1f us (%.1f TFLOP/s)" %
+              (name, sps * 1e3, r["kernel_s"] * 1e6, achieved), file=sys.stderr, flush=True)
+        del pstack, ptables, pkeep
     if "decode_router_t1" in wl:
         if stack is None or len(stack[2]) < 48:
             stack = decode_stack(ctx, "mtp_verify_t4_48l", 48)

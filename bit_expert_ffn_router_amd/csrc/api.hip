@@ -291,9 +291,7 @@ moe_status layer_forward_impl(const moe_shape* shape, int32_t tokens, const void
     }
     return hip_status(moe::launch_decode(a, w, (hipStream_t)stream), "decode launch");
   }
-  if (slots) return fail(MOE_EUNSUPPORTED, "slot tables are supported on the decode path (tokens <= 4)");
-  if (shape->qfmt == MOE_Q3S32) return fail(MOE_EUNSUPPORTED, "prefill path supports Q2SM and Q2S only");
-  moe::PrefillArgs a;
+  moe::PrefillArgs a = {};
   a.T = T;
   a.D = shape->d_model;
   a.F = shape->d_ff;
@@ -311,6 +309,10 @@ moe_status layer_forward_impl(const moe_shape* shape, int32_t tokens, const void
   a.out = out;
   a.out_bf16 = out_dtype == MOE_BF16;
   a.router = (const uint16_t*)table->router;
+  a.slot_of = slots ? table->slot_of : nullptr;
+  a.miss = slots ? (moe::MissRec*)miss : nullptr;
+  a.miss_count = slots ? miss_count : nullptr;
+  a.use_count = slots ? table->use_count : nullptr;
   return hip_status(moe::launch_prefill(a, ws, (hipStream_t)stream), "prefill launch");
 }
 

@@ -219,6 +219,13 @@ struct PrefillArgs {
   void* out;
   int out_bf16;
   const uint16_t* router;  // bf16 [E][D] or null: then `logits` is computed first
+  // slot table (all null without one): expert e at routed + slot_of[e]*stride
+  // or not resident (-1); non-resident pairs go to `miss` in (token, rank)
+  // order with their number in *miss_count; use_count[e] += routed pairs
+  const int32_t* slot_of;
+  MissRec* miss;
+  int32_t* miss_count;
+  uint32_t* use_count;
 };
 size_t prefill_ws_bytes(int T, int D, int F, int Fs, int E, int k);
 hipError_t launch_prefill(const PrefillArgs& a, void* ws, hipStream_t st);

@@ -50,7 +50,9 @@ __host__ __device__ inline size_t al256(size_t v) { return (v + 255) / 256 * 256
 struct PfWs {
   int32_t* idx;       // [T*k]
   float* gate;        // [T*k]
-  int32_t* offsets;   // [E+1]
+  int32_t* grp;       // [T*k] permutation group of each pair: its expert, or E
+                      // for a pair whose expert is not resident (slot table)
+  int32_t* offsets;   // [E+2] group offsets (group E: the misses)
   int32_t* sorted;    // [P]
   int32_t* inv;       // [P]
   PermWs perm;
@@ -76,11 +78,12 @@ PfWs pf_carve(void* ws, int T, int D, int F, int Fs, int E, int k) {
   auto take = [&](size_t n) { uint8_t* r = p; p += al256(n); return (void*)r; };
   w.idx = (int32_t*)take(4 * P);
   w.gate = (float*)take(4 * P);
-  w.offsets = (int32_t*)take(4 * ((size_t)E + 1));
+  w.grp = (int32_t*)take(4 * P);
+  w.offsets = (int32_t*)take(4 * ((size_t)E + 2));
   w.sorted = (int32_t*)take(4 * P);
   w.inv = (int32_t*)take(4 * P);
-  void* pw = take(perm_ws_bytes(T, k, E));
-  w.perm = perm_ws_carve(pw, T, k, E);
+  void* pw = take(perm_ws_bytes(T, k, E + 1));
+  w.perm = perm_ws_carve(pw, T, k, E + 1);
   w.tiles = (int4*)take(16 * (size_t)w.max_tiles);
   w.ntiles = (int32_t*)take(4);
   w.xb = (uint16_t*)take(2 * (size_t)T * D);
@@ -94,7 +97,7 @@ PfWs pf_carve(void* ws, int T, int D, int F, int Fs, int E, int k) {
 size_t prefill_ws_bytes(int T, int D, int F, int Fs, int E, int k) {
   const size_t P = (size_t)T * k;
   const int Fmax = F > Fs ? F : Fs;
-  size_t b = al256(4 * P) * 4 + al256(4 * ((size_t)E + 1)) + al256(perm_ws_bytes(T, k, E)) +
+  size_t b = al256(4 * P) * 5 + al256(4 * ((size_t)E + 2)) + al256(perm_ws_bytes(T, k, E + 1)) +
              al256(16 * (size_t)pf_max_tiles(T, E, k)) + 256 + al256(2 * (size_t)T * D) +
              al256(2 * (P + T) * (size_t)Fmax) + al256(2 * (P + T) * (size_t)D);
   return b;
@@ -171,6 +174,57 @@ __global__ __launch_bounds__(1024) void pf_tiles_kernel(const int32_t* __restric
 }
 
 // ----------------------------------------------------------------------------
+// Slot table: the permutation group of every pair (its expert when resident,
+// else the extra group E, which gets no tiles), and the usage counts: every
+// routed pair adds 1 to its expert, hit or miss (counted in LDS per block,
+// then one atomic add per expert and block; sums of integers, so the result
+// does not depend on their order).
+__global__ __launch_bounds__(256) void pf_slot_split_kernel(const int32_t* __restrict__ idx, int P,
+                                                            int E, const int32_t* __restrict__ slot_of,
+                                                            int32_t* __restrict__ grp,
+                                                            uint32_t* __restrict__ use_count) {
+  extern __shared__ uint32_t s_use[];
+  const int tid = threadIdx.x;
+  if (use_count) {
+    for (int e = tid; e < E; e += 256) s_use[e] = 0;
+    __syncthreads();
+  }
+  const int p0 = blockIdx.x * 4096;
+  for (int p = p0 + tid; p < P && p < p0 + 4096; p += 256) {
+    const int e = idx[p];
+    grp[p] = slot_of[e] >= 0 ? e : E;
+    if (use_count) atomicAdd(&s_use[e], 1u);
+  }
+  if (use_count) {
+    __syncthreads();
+    for (int e = tid; e < E; e += 256)
+      if (s_use[e]) atomicAdd(&use_count[e], s_use[e]);
+  }
+}
+
+// The miss list: group E of the stable permutation holds the non-resident
+// pairs in increasing pair index p = t*k + j, which is (token, rank) order.
+__global__ __launch_bounds__(256) void pf_miss_kernel(const int32_t* __restrict__ offsets, int E,
+                                                      int k, const int32_t* __restrict__ sorted,
+                                                      const int32_t* __restrict__ idx,
+                                                      const float* __restrict__ gate,
+                                                      MissRec* __restrict__ miss,
+                                                      int32_t* __restrict__ miss_count) {
+  const int m0 = offsets[E], n = offsets[E + 1] - m0;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i == 0) *miss_count = n;
+  if (i < n) {
+    const int p = sorted[m0 + i];
+    MissRec r;
+    r.token = p / k;
+    r.rank = p % k;
+    r.expert = idx[p];
+    r.gate = gate[p];
+    miss[i] = r;
+  }
+}
+
+// ----------------------------------------------------------------------------
 // Q2SM dequantisation into MFMA B fragments.
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
@@ -202,6 +256,27 @@ __device__ __forceinline__ uint4 q2_frag(uint32_t W, int sh, uint32_t lo, uint32
     const uint32_t t = (W >> (sh + 2 * j)) & 0x00030003u;  // u0 | u1 << 16
     const uint32_t sel = t * 0x202u + 0x01000100u;          // bytes 2u0, 2u0+1, 2u1, 2u1+1
     v[j] = __builtin_amdgcn_perm(hi, lo, sel);
+  }
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+// Q3S: the eight weights s*(u3 - 4) of block half KK of low-plane word W of
+// record word WD, whose high bits are in high-plane word H (for an even WD
+// the high bit of the code at bit p sits at bit p + 1 of H, for an odd one
+// at bit p).  s*u3 - 4s is exact in fp32 (an fp16 scale times an integer of
+// three bits), so each weight is rounded once, to bf16.  A 4-entry byte
+// select cannot index eight codes, and tables of both halves would not fit
+// the LDS; the codes go through the float converter instead.
+template <int WD, int KK>
+__device__ __forceinline__ uint4 q3_frag(uint32_t W, uint32_t H, float s) {
+  const float m4 = -4.f * s;
+  uint32_t v[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int p = 8 * KK + 2 * j;
+    const int hs = (WD & 1) ? p - 2 : p - 1;  // moves the high bit to bit 2 (and 18)
+    const uint32_t hh = hs >= 0 ? (H >> hs) : (H << -hs);
+    const uint32_t u = (hh & 0x00040004u) | ((W >> p) & 0x00030003u);  // u3 of columns 2j, 2j+1
+    v[j] = cvt_pk_bf16(fmaf(s, (float)(u & 0xFFu), m4), fmaf(s, (float)((u >> 16) & 0xFFu), m4));
   }
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
@@ -244,6 +319,7 @@ struct PfArgs {
   int T, D, F, Fs, E, k;
   const uint8_t* routed;
   size_t stride;
+  const int32_t* slot_of;  // slot table or null
   const uint8_t* shared;
   const uint16_t* x;      // bf16 [T][D]
   PfWs w;
@@ -252,7 +328,10 @@ struct PfArgs {
 };
 
 // LDS of the grouped GEMM: 4 x 16 KB activation stages + 2 x 48 KB weight
-// octets = 160 KB, the whole LDS of a CU (one block per CU).
+// octets = 160 KB, the whole LDS of a CU (one block per CU).  A Q3S octet
+// would need 7 KB per wave (low plane, high plane, scales) against the 6 KB
+// here, so its high plane goes to registers instead (8 bytes per lane per
+// tile).
 struct PfA {
   uint4 a[2][kRG * 4 * 16];  // [k-step][row group][quarter q][row m]: A fragments
 };
@@ -260,28 +339,34 @@ struct PfB {
   uint4 code[kPfWaves][4][64];  // [wave][tile][lane]: the lane's 4 code words of the octet
   uint4 sm[kPfWaves][2][64];    // [wave][tile pair][...]: (scale, min) of rows x 8 blocks
 };
-// direct loads per wave: activations per stage, weights per octet
+// vector-memory operations per wave: activations per stage, weights per
+// octet (Q3S adds one 8-byte register load of the high plane per tile)
 constexpr int kPfDmaA = 2;
-constexpr int kPfDmaB = 6;
+__host__ __device__ constexpr int pf_dma_b(int fmt) { return fmt == kQ3 ? 10 : 6; }
 
 // Grouped GEMM tile: rows row0 .. row0 + rows - 1 of the work list, weight
 // rows nb * kBN .. of the expert's matrix.  MODE 0: gate/up (A = gathered
 // activations, K = D, B = the expert's gate/up rows, SwiGLU epilogue into H).
 // MODE 1: down (A = H rows, K = F, B = W_down rows, epilogue into Y).  FMT:
-// Q2SM or Q2S weights (the same code words; Q2S records carry scales only).
+// Q2SM or Q2S weights (the same code words; Q2S records carry scales only)
+// or Q3S (low plane as those code words, then the high plane, then scales).
 // NG: row groups of 16 that get MFMAs (rows <= 16 NG); the loads and the
 // dequantisation are the same for every NG.
 template <int MODE, int FMT, int NG>
 __device__ __forceinline__ void pf_tile(const PfArgs& a, PfA& sa0, PfA& sa1, PfA& sa2, PfA& sa3,
                                         PfB& sb0, PfB& sb1, int e, int row0, int rows, int nb) {
   constexpr int kRec = rec_bytes(FMT);
-  constexpr int NV = 12 / NG;  // VALU slots per MFMA in the schedule (3 or 6)
+  constexpr int kPfDmaB = pf_dma_b(FMT);
+  // VALU instructions placed after each MFMA in the schedule (Q3S builds its
+  // fragments with about 9 instructions per register instead of 4)
+  constexpr int NV = (FMT == kQ3 ? 40 : 12) / NG;
   // wave index as a uniform (scalar) value: the weight addresses stay in SGPRs
   const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int P = a.T * a.k;
   const bool sh = e < 0;
   const int F = sh ? a.Fs : a.F;
-  const uint8_t* base = sh ? a.shared : a.routed + (size_t)e * a.stride;
+  const uint8_t* base =
+      sh ? a.shared : a.routed + (size_t)(a.slot_of ? a.slot_of[e] : e) * a.stride;
   const int K = MODE == 0 ? a.D : F;
   const int nkb = K / 32, nst = (nkb + 1) / 2;
   const int oK = octets(K);
@@ -313,12 +398,13 @@ __device__ __forceinline__ void pf_tile(const PfArgs& a, PfA& sa0, PfA& sa1, PfA
   // (scale, min) pieces: lanes 0..31 / 32..63 take tile 2i / 2i+1 of pair i,
   // 16 bytes each: row lane % 16, blocks 4 h .. 4 h + 3 with h = (lane / 16) % 2
   // (in LDS: [tile of pair][h][row], so a k-step's reads conflict at most 2-way).
-  // Q2S: the 16 bytes of row lane % 16 hold all 8 scales; both h take them.
+  // Q2S and Q3S: the 16 bytes of row lane % 16 hold all 8 scales; both h
+  // take them.
   const uint8_t* smp[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const ptrdiff_t d = trec[2 * i + 1] - trec[2 * i];  // uniform; no indexed pointer array
-    smp[i] = trec[2 * i] + (lane >= 32 ? d : 0) + 1024 +
+    smp[i] = trec[2 * i] + (lane >= 32 ? d : 0) + (FMT == kQ3 ? 1536 : 1024) +
              (FMT == kQ2 ? 32 * (lane & 15) + 16 * ((lane >> 4) & 1) : 16 * (lane & 15));
   }
   const int n = lane & 15, q = lane >> 4;
@@ -333,13 +419,21 @@ __device__ __forceinline__ void pf_tile(const PfArgs& a, PfA& sa0, PfA& sa1, PfA
       dma16(arow + (kb < nkb ? 32 * kb : 0), &A.a[kk][wv * 64]);
     }
   };
-  auto issue_b = [&](PfB& B, int o0) __attribute__((always_inline)) {
+  // Q3S high-plane words of the octets in sb0 / sb1: this lane's two words
+  // of each tile (they sit lane-major after the low plane)
+  uint2 hw0[4], hw1[4];
+  auto issue_b = [&](PfB& B, uint2 (&hw)[4], int o0) __attribute__((always_inline)) {
     const size_t ro = (size_t)(o0 < oK ? o0 : 0) * kRec;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       dma16(reinterpret_cast<const uint4*>(trec[j] + ro) + lane, &B.code[wv][j][0]);
 #pragma unroll
     for (int i = 0; i < 2; ++i) dma16(smp[i] + ro, &B.sm[wv][i][0]);
+    if constexpr (FMT == kQ3) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        hw[j] = *reinterpret_cast<const uint2*>(trec[j] + ro + 1024 + 8 * lane);
+    }
   };
 
   f32x4_t acc[NG][4];
@@ -389,14 +483,28 @@ __device__ __forceinline__ void pf_tile(const PfArgs& a, PfA& sa0, PfA& sa1, PfA
     }
   };
   // fragments of block b = 2 wd + kk (wd, kk compile-time) of the octet in B
-  auto dequant = [&](const PfB& B, auto WD, auto KK, uint4 (&bf)[4]) __attribute__((always_inline)) {
+  // (and, for Q3S, its high-plane words hw)
+  auto dequant = [&](const PfB& B, const uint2 (&hw)[4], auto WD, auto KK,
+                     uint4 (&bf)[4]) __attribute__((always_inline)) {
     constexpr int wd = decltype(WD)::value, kk = decltype(KK)::value, b = 2 * wd + kk;
-    const uint2* tbl = reinterpret_cast<const uint2*>(&B.code[wv][0][0]);
+    if constexpr (FMT == kQ3) {
+      // scale of (tile j, row n, block b): word wd of row n's 16 bytes
+      const uint32_t* scw = reinterpret_cast<const uint32_t*>(&B.sm[wv][0][0]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t w = wd == 0 ? cwo[j].x : (wd == 1 ? cwo[j].y : (wd == 2 ? cwo[j].z : cwo[j].w));
-      const uint2 t = tbl[(j * 8 + b) * 16 + n];
-      bf[j] = q2_frag(w, 8 * kk, t.x, t.y);
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t w = wd == 0 ? cwo[j].x : (wd == 1 ? cwo[j].y : (wd == 2 ? cwo[j].z : cwo[j].w));
+        const uint32_t sw = scw[(j >> 1) * 256 + ((j & 1) * 32 + n) * 4 + wd];
+        const float sc = f16_to_f32((uint16_t)(kk ? (sw >> 16) : (sw & 0xFFFFu)));
+        bf[j] = q3_frag<wd, kk>(w, (wd >> 1) ? hw[j].y : hw[j].x, sc);
+      }
+    } else {
+      const uint2* tbl = reinterpret_cast<const uint2*>(&B.code[wv][0][0]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t w = wd == 0 ? cwo[j].x : (wd == 1 ? cwo[j].y : (wd == 2 ? cwo[j].z : cwo[j].w));
+        const uint2 t = tbl[(j * 8 + b) * 16 + n];
+        bf[j] = q2_frag(w, 8 * kk, t.x, t.y);
+      }
     }
   };
   auto mfmas = [&](const PfA& A, int kk, const uint4 (&bf)[4]) __attribute__((always_inline)) {
@@ -431,19 +539,21 @@ __device__ __forceinline__ void pf_tile(const PfArgs& a, PfA& sa0, PfA& sa1, PfA
     block_barrier();
     PfB& bc = (i / 4) % 2 == 0 ? sb0 : sb1;  // this octet
     PfB& bn = (i / 4) % 2 == 0 ? sb1 : sb0;  // the next one
+    uint2(&hc)[4] = (i / 4) % 2 == 0 ? hw0 : hw1;
+    uint2(&hn)[4] = (i / 4) % 2 == 0 ? hw1 : hw0;
     if (s < nst) {
       const PfA& A = abuf(i % 4);
       // k-step 2s (fragments in bfa) || fragments of k-step 2s+1
-      dequant(bc, std::integral_constant<int, wd>(), std::integral_constant<int, 1>(), bfb);
+      dequant(bc, hc, std::integral_constant<int, wd>(), std::integral_constant<int, 1>(), bfb);
       mfmas(A, 0, bfa);
       // k-step 2s+1 (bfb) || fragments of k-step 2s+2 (next stage, maybe next octet)
       uint4 bfn[4];
       if constexpr (wd == 3) {
         load_codes(bn);
-        build_tables(bn, s / 4 + 1);
-        dequant(bn, std::integral_constant<int, 0>(), std::integral_constant<int, 0>(), bfn);
+        if constexpr (FMT != kQ3) build_tables(bn, s / 4 + 1);
+        dequant(bn, hn, std::integral_constant<int, 0>(), std::integral_constant<int, 0>(), bfn);
       } else {
-        dequant(bc, std::integral_constant<int, wd + 1>(), std::integral_constant<int, 0>(), bfn);
+        dequant(bc, hc, std::integral_constant<int, wd + 1>(), std::integral_constant<int, 0>(), bfn);
       }
       mfmas(A, 1, bfb);
 #pragma unroll
@@ -465,16 +575,16 @@ __device__ __forceinline__ void pf_tile(const PfArgs& a, PfA& sa0, PfA& sa1, PfA
       }
     }
     issue_a(abuf((i + 3) % 4), s + 3);
-    if constexpr (wd == 0) issue_b(bn, s / 4 + 1);
+    if constexpr (wd == 0) issue_b(bn, hn, s / 4 + 1);
   };
-  issue_b(sb0, 0);
+  issue_b(sb0, hw0, 0);
   issue_a(sa0, 0);
   issue_a(sa1, 1);
   issue_a(sa2, 2);
   wait_vm<3 * kPfDmaA>();  // B(0) has landed (this wave's own weight buffer)
   load_codes(sb0);
-  build_tables(sb0, 0);
-  dequant(sb0, std::integral_constant<int, 0>(), std::integral_constant<int, 0>(), bfa);
+  if constexpr (FMT != kQ3) build_tables(sb0, 0);
+  dequant(sb0, hw0, std::integral_constant<int, 0>(), std::integral_constant<int, 0>(), bfa);
 #pragma unroll 1
   for (int s = 0; s < nst; s += 8) {  // one exit: the register allocator keeps acc in place
     step(std::integral_constant<int, 0>(), s);
@@ -540,7 +650,7 @@ __device__ __forceinline__ void pf_tile(const PfArgs& a, PfA& sa0, PfA& sa1, PfA
 
 template <int MODE, int FMT>
 __global__ __launch_bounds__(kPfThreads, 1) void pf_gemm_kernel(PfArgs a, int nN, int nwork) {
-  static_assert(FMT == kQ2 || FMT == kQ2S, "prefill formats");
+  static_assert(FMT == kQ2 || FMT == kQ2S || FMT == kQ3, "prefill formats");
   __shared__ PfA sa0, sa1, sa2, sa3;
   __shared__ PfB sb0, sb1;
   // XCD-aware order: blocks are dispatched round-robin over the 8 XCDs, so
@@ -571,15 +681,17 @@ __global__ __launch_bounds__(kPfThreads, 1) void pf_gemm_kernel(PfArgs a, int nN
 // out_t = sum_j g_tj * Y[inv[t*k + j]] + Y[P + t], in a fixed order.  One
 // block per token: the token's rows and gates go to LDS first, then each
 // thread has all of its 16-byte pieces of those rows in flight together (up
-// to 16 at a time) before it sums them in order j = 0..k-1.
+// to 16 at a time) before it sums them in order j = 0..k-1.  With a slot
+// table the sum runs over the resident pairs only (the partial layer).
 __global__ __launch_bounds__(512) void pf_combine_kernel(PfArgs a, int has_shared) {
   __shared__ int32_t s_row[kMaxTopK];
   __shared__ float s_g[kMaxTopK];
   const int t = blockIdx.x, tid = threadIdx.x, k = a.k;
   const int P = a.T * k, D = a.D;
   if (tid < k) {
-    s_row[tid] = a.w.inv[(size_t)t * k + tid];
-    s_g[tid] = a.w.gate[(size_t)t * k + tid];
+    const size_t p = (size_t)t * k + tid;
+    s_row[tid] = a.slot_of && a.w.grp[p] == a.E ? -1 : a.w.inv[p];
+    s_g[tid] = a.w.gate[p];
   }
   __syncthreads();
   auto add = [](float (&o)[8], const uint4& y, float g) __attribute__((always_inline)) {
@@ -599,10 +711,11 @@ __global__ __launch_bounds__(512) void pf_combine_kernel(PfArgs a, int has_share
       uint4 y[16];
 #pragma unroll
       for (int jj = 0; jj < 16; ++jj)
-        if (j0 + jj < k) y[jj] = reinterpret_cast<const uint4*>(a.w.Y + (size_t)s_row[j0 + jj] * D)[c];
+        if (j0 + jj < k && s_row[j0 + jj] >= 0)
+          y[jj] = reinterpret_cast<const uint4*>(a.w.Y + (size_t)s_row[j0 + jj] * D)[c];
 #pragma unroll
       for (int jj = 0; jj < 16; ++jj)
-        if (j0 + jj < k) add(o, y[jj], s_g[j0 + jj]);
+        if (j0 + jj < k && s_row[j0 + jj] >= 0) add(o, y[jj], s_g[j0 + jj]);
     }
     if (has_shared) add(o, ys, 1.f);
     if (a.out_bf16) {
@@ -636,8 +749,28 @@ hipError_t launch_prefill(const PrefillArgs& pa, void* ws, hipStream_t st) {
     if ((e = launch_router(r, st)) != hipSuccess) return e;
   }
   if ((e = launch_route(pa.logits, T, E, k, w.idx, w.gate, st)) != hipSuccess) return e;
-  if ((e = launch_permute(w.idx, T, k, E, w.offsets, w.sorted, w.inv, w.perm, st)) != hipSuccess)
+  if (pa.slot_of) {
+    // group E collects the misses; the tiles cover groups 0..E-1 only
+    const int P = T * k;
+    pf_slot_split_kernel<<<(P + 4095) / 4096, 256, pa.use_count ? E * sizeof(uint32_t) : 0, st>>>(
+        w.idx, P, E, pa.slot_of, w.grp, pa.use_count);
+    if ((e = launch_permute(w.grp, T, k, E + 1, w.offsets, w.sorted, w.inv, w.perm, st)) !=
+        hipSuccess)
+      return e;
+    pf_miss_kernel<<<(P + 255) / 256, 256, 0, st>>>(w.offsets, E, k, w.sorted, w.idx, w.gate,
+                                                     pa.miss, pa.miss_count);
+  } else if ((e = launch_permute(w.idx, T, k, E, w.offsets, w.sorted, w.inv, w.perm, st)) !=
+             hipSuccess) {
     return e;
+  }
+  {  // the caller's route event (moe_set_route_event): routing and miss list are written
+    KernelTimer& re = route_event();
+    if (re.before != nullptr) {
+      const hipEvent_t ev = re.before;
+      re.before = nullptr;
+      if ((e = hipEventRecord(ev, st)) != hipSuccess) return e;
+    }
+  }
   const int has_sh = pa.shared != nullptr;
   pf_tiles_kernel<<<1, 1024, 0, st>>>(w.offsets, E, T * k, T, has_sh, w.tiles, w.ntiles);
   PfArgs a;
@@ -649,6 +782,7 @@ hipError_t launch_prefill(const PrefillArgs& pa, void* ws, hipStream_t st) {
   a.k = k;
   a.routed = pa.routed;
   a.stride = pa.stride;
+  a.slot_of = pa.slot_of;
   a.shared = pa.shared;
   a.x = xb;
   a.w = w;
@@ -662,6 +796,11 @@ hipError_t launch_prefill(const PrefillArgs& pa, void* ws, hipStream_t st) {
                           st, a, nN_gu, nw_gu)) != hipSuccess)
       return e;
     pf_gemm_kernel<1, kQ2><<<(nw_dn + 7) / 8 * 8, kPfThreads, 0, st>>>(a, nN_dn, nw_dn);
+  } else if (pa.fmt == kQ3) {
+    if ((e = launch_timed(pf_gemm_kernel<0, kQ3>, dim3((nw_gu + 7) / 8 * 8), dim3(kPfThreads), 0u,
+                          st, a, nN_gu, nw_gu)) != hipSuccess)
+      return e;
+    pf_gemm_kernel<1, kQ3><<<(nw_dn + 7) / 8 * 8, kPfThreads, 0, st>>>(a, nN_dn, nw_dn);
   } else {
     if ((e = launch_timed(pf_gemm_kernel<0, kQ2S>, dim3((nw_gu + 7) / 8 * 8), dim3(kPfThreads), 0u,
                           st, a, nN_gu, nw_gu)) != hipSuccess)

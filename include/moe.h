@@ -244,9 +244,10 @@ size_t moe_workspace_bytes(const moe_shape* shape, int32_t tokens);
  * Misaligned pointers are rejected with MOE_EINVAL before any launch.
  * Paths: T <= 4 runs the decode path (dequantising MFMA GEMV that streams
  * each distinct selected expert once); larger T runs the prefill path
- * (routing, stable token permutation, grouped MFMA GEMM, combine).  The
- * prefill path supports MOE_Q2SM32 and MOE_Q2S32 (MOE_EUNSUPPORTED for
- * MOE_Q3S32).
+ * (routing, stable token permutation, grouped MFMA GEMM, combine).  Both
+ * paths take all three formats and slot tables; with a slot table the
+ * prefill path leaves the non-resident pairs out of the permuted groups and
+ * lists them, in (token, rank) order, as the decode path does.
  * Results are deterministic: the same inputs give the same output bits. */
 moe_status moe_layer_forward(const moe_shape* shape, int32_t tokens,
                              const void* x, int32_t x_dtype, uint32_t flags,
@@ -329,10 +330,11 @@ void moe_host_pool_destroy(moe_host_pool* pool);
 
 /* Event for overlapping the host half with the GPU half.  `event` is a
  * hipEvent_t created by the caller (NULL clears a pending one).  The calling
- * thread's next moe_layer_forward call on the decode path records it on its
- * stream as soon as the routing, the miss list and its count are written --
- * after the first kernel (one token) or the routing kernel (2..4 tokens),
- * before the experts' FFNs finish -- and then forgets it.  A caller that
+ * thread's next moe_layer_forward call records it on its stream as soon as
+ * the routing, the miss list and its count are written -- after the first
+ * kernel (one token), the routing kernel (2..4 tokens) or the permutation
+ * and miss-list kernels (more tokens), before the experts' FFNs run or
+ * finish -- and then forgets it.  A caller that
  * waits for the event can copy the miss list and run moe_host_miss_ffn while
  * the GPU still computes the resident experts, as the pages' CPU and GPU
  * work on one layer at the same time ([AF] section "命中率七成，代价是答案会

@@ -282,6 +282,19 @@ WORKLOADS = {
     "prefill_8192": dict(d_model=3072, d_ff=512, n_experts=512, top_k=10, d_ff_shared=512,
                          tokens=8192, layers=1, fmt=FMT_Q2SM, x_dtype="bf16", zipf_s=1.1,
                          alpha=1.0, min_gap=None),
+    # The 8192-token chunk on the 3-bit experts of the slot workload's format
+    # (the pages quote prompt-processing rates for their 3-bit tier), routed
+    # as prefill_8192.
+    "prefill_q3s_8192": dict(d_model=3072, d_ff=512, n_experts=512, top_k=10, d_ff_shared=512,
+                             tokens=8192, layers=1, fmt=FMT_Q3S, x_dtype="bf16", zipf_s=1.1,
+                             alpha=1.0, min_gap=None),
+    # The same chunk on a slot table: 128 of 512 Q3S experts resident (the
+    # most popular), routed as the slot workload; the GPU computes the hits
+    # and the shared expert and lists the misses.
+    "prefill_slot_q3s_8192": dict(d_model=3072, d_ff=512, n_experts=512, top_k=10,
+                                  d_ff_shared=512, tokens=8192, layers=1, fmt=FMT_Q3S,
+                                  x_dtype="bf16", zipf_s=SLOT_ZIPF_S, alpha=SLOT_ALPHA,
+                                  min_gap=None, n_slots=128),
     "decode_q2s_t1": dict(d_model=3072, d_ff=512, n_experts=512, top_k=10, d_ff_shared=512,
                           tokens=1, layers=1, fmt=FMT_Q2S, x_dtype="bf16", zipf_s=1.1,
                           alpha=1.0, min_gap=None),

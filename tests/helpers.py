@@ -76,3 +76,21 @@ def ensure_built():
     if not (os.path.exists(lib) and os.path.exists(syn)):
         import runpy
         runpy.run_path(os.path.join(ROOT, "bit_expert_ffn_router_amd", "build.py"))["build"]()
+
+
+def forced_logits(T, E, k, counts, seed):
+    """Router logits whose top-k gives expert e exactly counts[e] pairs.
+
+    The expert ids, sorted and repeated counts[e] times, are dealt out with
+    stride T: token t takes ids[t + j*T] as its rank-j expert, which are
+    distinct because no count exceeds T.  Chosen logits are 4 - 0.3 j, the
+    rest lie near -3, so the routing is unambiguous in any precision."""
+    counts = list(counts) + [0] * (E - len(counts))
+    assert sum(counts) == T * k and max(counts) <= T
+    ids = np.repeat(np.arange(E), counts)
+    rng = np.random.default_rng(seed)
+    lg = (-3.0 + 0.1 * rng.standard_normal((T, E))).astype(np.float32)
+    for j in range(k):
+        lg[np.arange(T), ids[j * T:(j + 1) * T]] = np.float32(4.0 - 0.3 * j) + \
+            np.float32(0.01) * rng.random(T, dtype=np.float32)
+    return lg

@@ -125,14 +125,17 @@ def test_forward_argument_checks():
     call(tokens=0, x=None, lg=None, out=None, ws=None, wsb=0)
 
 
-def test_prefill_q3s_unsupported():
+def test_slot_prefill_needs_room_for_every_miss():
+    """Prefill on a slot table (64 tokens, Q3S) is refused before any launch
+    when the miss list cannot hold every routed pair."""
     sh = shape(qfmt=moe.MOE_Q3S32)
     stride = (moe.moe_packed_expert_bytes(sh, 64) + 255) // 256 * 256
-    t = moe.MoeExpertTable(0x10000, stride, None, 0, 0x20000)
+    t = moe.MoeExpertTable(0x10000, stride, 0x30000, 4, 0x20000)
+    T = 64
     with pytest.raises(moe.MoeError) as ei:
-        moe.moe_layer_forward(sh, 64, 0x1000, moe.MOE_BF16, 0, 0x1000, t, 0x1000, moe.MOE_BF16,
-                              None, 0, None, 0x100000, 1 << 34, S)
-    assert ei.value.status == moe.MOE_EUNSUPPORTED
+        moe.moe_layer_forward(sh, T, 0x1000, moe.MOE_BF16, 0, 0x1000, t, 0x1000, moe.MOE_BF16,
+                              0x40000, T * sh.top_k - 1, 0x50000, 0x100000, 1 << 34, S)
+    assert ei.value.status == moe.MOE_ENOSPACE
 
 
 def test_pack_and_route_argument_checks():

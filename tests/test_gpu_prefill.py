@@ -10,7 +10,7 @@ import pytest
 
 import synth
 from oracle import moe_oracle as O
-from helpers import RTOL_L2, OracleWeights, rel_l2
+from helpers import RTOL_L2, OracleWeights, forced_logits as _forced_logits, rel_l2
 
 pytestmark = pytest.mark.gpu
 
@@ -157,24 +157,6 @@ def test_identical_experts_prefill_equals_dense_swiglu(g):
     a2, b2 = x @ sg.T, x @ su.T
     dense += (a2 / (1 + np.exp(-a2)) * b2) @ sd.T
     assert rel_l2(got, dense) <= RTOL_L2
-
-
-def _forced_logits(T, E, k, counts, seed):
-    """Router logits whose top-k gives expert e exactly counts[e] pairs.
-
-    The expert ids, sorted and repeated counts[e] times, are dealt out with
-    stride T: token t takes ids[t + j*T] as its rank-j expert, which are
-    distinct because no count exceeds T.  Chosen logits are 4 - 0.3 j, the
-    rest lie near -3, so the routing is unambiguous in any precision."""
-    counts = list(counts) + [0] * (E - len(counts))
-    assert sum(counts) == T * k and max(counts) <= T
-    ids = np.repeat(np.arange(E), counts)
-    rng = np.random.default_rng(seed)
-    lg = (-3.0 + 0.1 * rng.standard_normal((T, E))).astype(np.float32)
-    for j in range(k):
-        lg[np.arange(T), ids[j * T:(j + 1) * T]] = np.float32(4.0 - 0.3 * j) + \
-            np.float32(0.01) * rng.random(T, dtype=np.float32)
-    return lg
 
 
 # group sizes on both sides of the 64-row switch between the two GEMM bodies
