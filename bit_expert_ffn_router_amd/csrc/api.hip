@@ -192,10 +192,16 @@ moe_status check_table(const moe_shape* shape, const moe_expert_table* table) {
   return ok();
 }
 
+// RMS partials of the stack with 2..4 tokens: two buffers of [d_model/16][T]
+// floats, written by layer l's down kernel and read by layer l+1's gate/up.
+size_t stack_rms_bytes(const moe_shape* s, int T) {
+  return T > 1 ? 2 * (((size_t)(s->d_model / 16) * T * 4 + 255) / 256 * 256) : 0;
+}
+
 size_t stack_ws_bytes(const moe_shape* s, int L, int T) {
   if (L <= 0 || T <= 0) return 0;
   const size_t plan = moe::decode_plan_bytes(T, s->n_experts, s->top_k);
-  return (size_t)L * plan +
+  return (size_t)L * plan + stack_rms_bytes(s, T) +
          moe::decode_ws_bytes(T, s->d_model, s->d_ff, s->d_ff_shared, s->n_experts, s->top_k);
 }
 
@@ -377,8 +383,15 @@ moe_status moe_decode_stack_forward(const moe_shape* shape, int32_t layers, int3
   const int D = shape->d_model, E = shape->n_experts, k = shape->top_k;
   const size_t plan_bytes = moe::decode_plan_bytes(T, E, k);
   uint8_t* plan = (uint8_t*)ws;
-  const moe::DecodeWs base = moe::decode_ws_carve(plan + (size_t)L * plan_bytes, T, D,
-                                                  shape->d_ff, shape->d_ff_shared, E, k);
+  float* rms_part[2] = {nullptr, nullptr};
+  if (T > 1) {
+    const size_t half = stack_rms_bytes(shape, T) / 2;
+    rms_part[0] = (float*)(plan + (size_t)L * plan_bytes);
+    rms_part[1] = (float*)(plan + (size_t)L * plan_bytes + half);
+  }
+  const moe::DecodeWs base = moe::decode_ws_carve(
+      plan + (size_t)L * plan_bytes + stack_rms_bytes(shape, T), T, D, shape->d_ff,
+      shape->d_ff_shared, E, k);
   hipStream_t st = (hipStream_t)stream;
   // 1. The routing of every layer.
   for (int l0 = 0; l0 < L; l0 += moe::kPlanLayers) {
@@ -403,7 +416,8 @@ moe_status moe_decode_stack_forward(const moe_shape* shape, int32_t layers, int3
     if (s != MOE_OK) return s;
   }
   // 2. The layers, each on its own list; layer l > 0 reads layer l - 1's
-  // output with the RMS rule.
+  // output with the RMS rule (with 2..4 tokens its factors come from the
+  // sums of squares that layer l - 1's down kernel left in rms_part).
   const size_t out_row = (size_t)T * D * (out_dtype == MOE_BF16 ? 2 : 4);
   for (int l = 0; l < L; ++l) {
     const moe_expert_table& t = tables[l];
@@ -427,6 +441,10 @@ moe_status moe_decode_stack_forward(const moe_shape* shape, int32_t layers, int3
     a.out = (uint8_t*)out + (size_t)l * out_row;
     a.out_bf16 = out_dtype == MOE_BF16;
     a.planned = 1;
+    if (T > 1) {
+      a.rms_in = l > 0 ? rms_part[(l - 1) & 1] : nullptr;
+      a.rms_out = l + 1 < L ? rms_part[l & 1] : nullptr;
+    }
     moe::DecodeWs w = base;
     moe::decode_plan_carve(plan + (size_t)l * plan_bytes, T, E, k, w);
     s = hip_status(moe::launch_decode(a, w, st), "decode launch");

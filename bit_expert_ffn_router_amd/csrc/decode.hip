@@ -578,6 +578,19 @@ __device__ __forceinline__ void gateup_body(const DecodeArgs& a, const DecodeWs&
 #pragma unroll
     for (int t = 0; t < T; ++t) rinv[t] = w.rinv[t];
   }
+  // A planned call with 2..4 tokens (decode stack): the previous layer's
+  // down blocks left the sums of squares of their output rows; every wave
+  // adds the D/16 partials of each token in the same fixed order, so all
+  // blocks agree on the factors without a block-wide pass over x.
+  float rpart[T];
+  if constexpr (RMS && T > 1 && PLANNED) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) rpart[t] = 0.f;
+    for (int i = lane; i < D / 16; i += 64) {
+#pragma unroll
+      for (int t = 0; t < T; ++t) rpart[t] += a.rms_in[i * T + t];
+    }
+  }
 
   // 2. Weight loads of this wave.
   const int mat = wv >> 1, kh = wv & 1;
@@ -596,12 +609,14 @@ __device__ __forceinline__ void gateup_body(const DecodeArgs& a, const DecodeWs&
   const DnPrefetch dpf = prefetch_down_rows(eb, D, Fu_pf, rec_bytes(FMT),
                                             down_offset(D, Fu_pf, FMT), vb, vb - g, Fu_pf / 16,
                                             tid, kGuThreads);
-  // The RMS factors of the input, in-block (one token, or a planned call).
-  // With 2..4 bf16 tokens of a planned call the raw pieces go to LDS first
-  // and come back after the block-wide sum, so they are not held in
-  // registers (beside the weight records in flight) across the barrier.
-  constexpr bool RMS_IN_BLOCK = RMS && (T == 1 || PLANNED);
-  constexpr bool TWO_PASS = RMS_IN_BLOCK && T > 1 && in_bf16;
+  // The RMS factors of the input: in-block with one token; from the
+  // previous layer's partials in a planned call with 2..4 tokens; from
+  // decode_list_kernel otherwise.
+  constexpr bool RMS_IN_BLOCK = RMS && T == 1;
+  if constexpr (RMS && T > 1 && PLANNED) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) rinv[t] = 1.0f / sqrtf(wave_sum_f32(rpart[t]) / (float)D + 1e-6f);
+  }
   if constexpr (RMS_IN_BLOCK) {
     float ss[T];
 #pragma unroll
@@ -621,9 +636,6 @@ __device__ __forceinline__ void gateup_body(const DecodeArgs& a, const DecodeWs&
       }
 #pragma unroll
       for (int tt = 0; tt < T; ++tt) ss[tt] += tt == t ? q2 : 0.f;  // invalid pieces are 0
-      if constexpr (TWO_PASS) {
-        if (i < nin) s_xhi[t * D8p + i % D8] = xr[j];  // raw, normalised in place below
-      }
     }
 #pragma unroll
     for (int t = 0; t < T; ++t) {
@@ -637,13 +649,6 @@ __device__ __forceinline__ void gateup_body(const DecodeArgs& a, const DecodeWs&
 #pragma unroll
       for (int w2 = 0; w2 < kGuWaves; ++w2) ssum += s_ss[w2][t];
       rinv[t] = 1.0f / sqrtf(ssum / (float)D + 1e-6f);
-    }
-    if constexpr (TWO_PASS) {
-#pragma unroll
-      for (int j = 0; j < XJ; ++j) {  // each thread reads back the pieces it wrote
-        const int i = tid + kGuThreads * j;
-        xr[j] = i < nin ? s_xhi[(i / D8) * D8p + i % D8] : make_uint4(0, 0, 0, 0);
-      }
     }
   }
   // bf16 operand(s) to LDS, and per-block sums X = sum x, X' = sum c x of the
@@ -998,16 +1003,28 @@ __global__ __launch_bounds__(1024) void decode_down_kernel(DecodeArgs a, DecodeW
     for (int t = 0; t < T; ++t) s_red[wv][t][n] = oacc[t];
   }
   __syncthreads();
-  if (tid < 16 * T) {
+  if (tid < 16 * T) {  // lanes 16t .. 16t+15 of wave 0: token t, rows nn
     const int t = tid >> 4, nn = tid & 15;
     float o = 0.f;
 #pragma unroll
     for (int i = 0; i < kDnWaves; ++i) o += s_red[i][t][nn];
     const size_t oi = (size_t)t * D + 16 * rt + nn;
-    if (a.out_bf16)
-      reinterpret_cast<uint16_t*>(a.out)[oi] = f32_to_bf16(o);
-    else
+    float stored = o;
+    if (a.out_bf16) {
+      const uint16_t ob = f32_to_bf16(o);
+      reinterpret_cast<uint16_t*>(a.out)[oi] = ob;
+      stored = bf16_to_f32(ob);
+    } else {
       reinterpret_cast<float*>(a.out)[oi] = o;
+    }
+    if (a.rms_out) {  // the next layer's RMS partial: sum over this block's 16 rows
+      float sq = stored * stored;
+      sq += __shfl_xor(sq, 1, 64);
+      sq += __shfl_xor(sq, 2, 64);
+      sq += __shfl_xor(sq, 4, 64);
+      sq += __shfl_xor(sq, 8, 64);
+      if (nn == 0) a.rms_out[rt * T + t] = sq;
+    }
   }
 }
 

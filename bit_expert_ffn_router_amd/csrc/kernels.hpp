@@ -132,6 +132,13 @@ struct DecodeArgs {
   uint32_t* use_count;  // NULL, or [E]: +1 per routed pair (slot policy statistics)
   int planned;          // 1: the routing and list are already in the workspace
                         // (decode_plan_kernel); the RMS rule is applied in-block
+                        // (one token) or from rms_in (2..4 tokens)
+  // Decode stack, 2..4 tokens: rms_out (or NULL) receives, per down block
+  // rt (16 output rows) and token t, the sum of squares of the stored
+  // outputs at [rt][T]; rms_in holds the previous layer's, from which a
+  // planned RMS call takes its factors.
+  float* rms_out;
+  const float* rms_in;
 };
 
 size_t decode_ws_bytes(int T, int D, int F, int Fs, int E, int k);

@@ -4,8 +4,9 @@ all inputs, routed by one kernel at the head of the call.
 Against chained moe_layer_forward calls with the RMS flag: identical output
 bits, miss lists and counts with one token (the same kernels run on the same
 lists; the RMS factor is summed the same way); with 2..4 tokens the RMS
-factors are summed in another order, so each layer is checked against the
-oracle, teacher-forced on the GPU's previous output.  Tokens whose
+factors come from the previous layer's down blocks (sums of squares of
+their output rows) and are summed in another order, so each layer is
+checked against the oracle, teacher-forced on the GPU's previous output.  Tokens whose
 reference output falls below fp32's range (a chained token whose gates go
 far negative decays by a square per layer) must come out as near zero.
 """
@@ -101,7 +102,10 @@ def test_multi_token_stack_teacher_forced(g, T):
     NL, D, E, k = 6, w["d_model"], w["n_experts"], w["top_k"]
     layers = [g.build_layer(shape, 0, l, g.DEV) for l in range(NL)]
     tables = [L.table() for L in layers]
-    xb = synth.activations_bf16(0, 12 + T, T, D)
+    # the first T tokens of one input (the generators fill row by row, and a
+    # token's layers depend on its own rows only), chosen so that every
+    # token's reference stays in fp32's range through the layers
+    xb = synth.activations_bf16(0, 16, T, D)
     logits = np.stack([synth.router_logits(0, l, T, E, zipf_s=w["zipf_s"], alpha=w["alpha"])
                        for l in range(NL)])
     out, _, _ = _stack(g, shape, tables, T, xb, logits, moe.MOE_BF16, False)
