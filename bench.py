@@ -1009,7 +1009,10 @@ def main():
             roofline={"bound": "mfma",
                       "kernel": "pf_gemm_kernel<0, Q3S> (gate/up grouped GEMM + SwiGLU)",
                       "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                      "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                      "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+                      "traffic": traffic_from_profile("prefill_q3s_gateup_8192",
+                                                      ["prefill.hip", "common.hpp", "kernels.hpp"],
+                                                      None) if name == "prefill_q3s_8192" else None,
                       "flops_per_launch": r["flops_per_launch"],
                       "kernel_us": r["kernel_s"] * 1e6})
         if "hit_rate" in r:

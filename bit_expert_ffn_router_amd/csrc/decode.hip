@@ -441,8 +441,10 @@ __device__ __forceinline__ void lds_barrier() {
 // share an XCD and its L2.  The gate/up block vb of expert u therefore reads
 // the records of the down rows rt with rt = vb (mod 8), shared out among the
 // expert's gate/up blocks of that residue class: one 4-byte load per 64-byte
-// line, which leaves the line in that XCD's L2 for the down kernel launched
-// next.  The loaded words are only kept alive to the end of the block (see
+// line.  The L2 copies do not survive to the down kernel (its HBM-side
+// fetch, FETCH_SIZE, still equals its records, 6.8 MB per one-token layer:
+// the L2s are invalidated between kernels); what the down kernel finds is the
+// line in the Infinity Cache (MALL), a shorter round trip than to HBM.  The loaded words are only kept alive to the end of the block (see
 // keep_alive), so nothing waits for them before then.  Only where the bytes
 // are cached depends on this placement, never a result.
 struct DnPrefetch {
