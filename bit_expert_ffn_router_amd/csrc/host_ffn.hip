@@ -13,6 +13,8 @@
 // reads it with its own host code.  Arithmetic: exact fp32 weights (an fp16
 // scale times a small integer, plus an fp16 min), fp32 activations, fp32
 // accumulation, fp32 h and output.
+#include <immintrin.h>
+
 #include <cstdlib>
 #include <cstring>
 #include <fstream>
@@ -205,75 +207,111 @@ __attribute__((target("avx2,fma"))) void record_rows4_avx2(const uint8_t* rec, i
   }
 }
 
-// The same four rows with AVX-512F.  One code word (lane 16 q + n, word wd)
-// holds row n's codes of column quarter q for both blocks 2 wd and 2 wd + 1
-// (block 2 wd in bits 0..7 and 16..23, block 2 wd + 1 in bits 8..15 and
-// 24..31), so one broadcast word shifted per lane gives 16 codes: lanes 0..7
-// block 2 wd, lanes 8..15 block 2 wd + 1, each in the record order of the
-// activation vector.  A word pair takes four multiply-adds per row (one per
-// quarter) instead of AVX2's eight, and the two blocks' scales multiply the
-// two halves of one accumulator.
-typedef float v16f __attribute__((vector_size(64)));
-typedef uint32_t v16u __attribute__((vector_size(64)));
-typedef float v8f_ __attribute__((vector_size(32)));
-__attribute__((target("avx512f"))) void record_rows4_avx512(const uint8_t* rec, int fmt, int n0,
-                                                            const float* xv, const float* xs,
-                                                            float* out) {
-  const uint32_t* lo = reinterpret_cast<const uint32_t*>(rec);
-  const uint32_t* hi = reinterpret_cast<const uint32_t*>(rec + 1024);
-  const v16u lanes = {0, 2, 4, 6, 16, 18, 20, 22, 8, 10, 12, 14, 24, 26, 28, 30};
-  const v16f zero = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  v16f tot[4] = {zero, zero, zero, zero};
-  float offs[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int wd = 0; wd < 4; ++wd) {
-    const int extra = (wd % 2 == 0) ? 1 : 0;  // Q3S: the third bit's position in the high word
-    const v16u shb = lanes + (uint32_t)extra;
-    v16f acc[4] = {zero, zero, zero, zero};
-    for (int q = 0; q < 4; ++q) {
-      v8f_ x0, x1;
-      __builtin_memcpy(&x0, xv + 32 * (2 * wd) + 8 * q, sizeof x0);
-      __builtin_memcpy(&x1, xv + 32 * (2 * wd + 1) + 8 * q, sizeof x1);
-      const v16f x = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13,
-                                             14, 15);
-      for (int r = 0; r < 4; ++r) {
-        const int L = 16 * q + n0 + r;
-        const uint32_t W = lo[4 * L + wd];
-        v16u c = ((v16u){W, W, W, W, W, W, W, W, W, W, W, W, W, W, W, W} >> lanes) & 3u;
-        if (fmt == kQ3) {  // u3 = u + 4 * (third bit)
-          const uint32_t H = hi[2 * L + wd / 2];
-          c += (((v16u){H, H, H, H, H, H, H, H, H, H, H, H, H, H, H, H} >> shb) & 1u) << 2;
-        }
-        acc[r] = __builtin_convertvector(c, v16f) * x + acc[r];
+// All 16 rows of one record dotted with octet o of a record-order vector,
+// with AVX-512F: the rows run across the 16 lanes.  For column quarter q the
+// record holds rows 0..15 x code words 0..3 in 256 contiguous bytes (word
+// (n, wd) at 4 n + wd); two two-source permutes gather word wd of all 16
+// rows into one vector.  Each of the word's 16 columns is then one shift, a
+// mask, a conversion and a multiply-add with the column's activation
+// broadcast to every row.  A block's sums stay separate per row and are
+// scaled once, as 16-row vectors, when the record is done.
+__attribute__((target("avx512f,f16c"))) void record_rows16_avx512(const uint8_t* rec, int fmt,
+                                                                  const float* xv, const float* xs,
+                                                                  float* out) {
+  const __m512i m3 = _mm512_set1_epi32(3), m4 = _mm512_set1_epi32(4);
+  const __m512i rows4 = _mm512_setr_epi32(0, 4, 8, 12, 16, 20, 24, 28, 0, 4, 8, 12, 16, 20, 24, 28);
+  const __m512i rows2 = _mm512_setr_epi32(0, 2, 4, 6, 8, 10, 12, 14, 16, 18, 20, 22, 24, 26, 28, 30);
+  __m512 acc[8];
+  for (int b = 0; b < 8; ++b) acc[b] = _mm512_setzero_ps();
+  for (int q = 0; q < 4; ++q) {
+    const uint8_t* slab = rec + 256 * q;
+    const __m512i A0 = _mm512_loadu_si512(slab), A1 = _mm512_loadu_si512(slab + 64);
+    const __m512i A2 = _mm512_loadu_si512(slab + 128), A3 = _mm512_loadu_si512(slab + 192);
+    __m512i H0 = _mm512_setzero_si512(), H1 = _mm512_setzero_si512();
+    if (fmt == kQ3) {  // high-plane words (n, h) at 2 n + h: rows 0..7, then 8..15
+      H0 = _mm512_loadu_si512(rec + 1024 + 128 * q);
+      H1 = _mm512_loadu_si512(rec + 1024 + 128 * q + 64);
+    }
+#pragma unroll
+    for (int wd = 0; wd < 4; ++wd) {
+      const __m512i idx = _mm512_add_epi32(rows4, _mm512_set1_epi32(wd));
+      const __m512i V = _mm512_mask_blend_epi32((__mmask16)0xFF00, _mm512_permutex2var_epi32(A0, idx, A1),
+                                                _mm512_permutex2var_epi32(A2, idx, A3));
+      __m512i HW = _mm512_setzero_si512();
+      if (fmt == kQ3)
+        HW = _mm512_permutex2var_epi32(H0, _mm512_add_epi32(rows2, _mm512_set1_epi32(wd / 2)), H1);
+      const int extra = (wd % 2 == 0) ? 1 : 0;  // the third bit sits one higher for even words
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int b = 2 * wd + kk;
+        __m512 a = acc[b];
+#pragma unroll
+        for (int par = 0; par < 2; ++par)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int pos = 8 * kk + 16 * par + 2 * j;  // bits of column 32 b + 8 q + 2 j + par
+            __m512i c = _mm512_and_si512(_mm512_srli_epi32(V, pos), m3);
+            if (fmt == kQ3) {  // u3 = u + 4 * (third bit)
+              const int hp = pos + extra;
+              const __m512i hb = hp >= 2 ? _mm512_srli_epi32(HW, hp - 2) : _mm512_slli_epi32(HW, 2 - hp);
+              c = _mm512_or_si512(c, _mm512_and_si512(hb, m4));
+            }
+            a = _mm512_fmadd_ps(_mm512_cvtepi32_ps(c),
+                                _mm512_set1_ps(xv[32 * b + 8 * q + 4 * par + j]), a);
+          }
+        acc[b] = a;
       }
     }
-    for (int r = 0; r < 4; ++r) {
-      float s0, o0, s1, o1;
-      block_params(rec, fmt, n0 + r, 2 * wd, s0, o0);
-      block_params(rec, fmt, n0 + r, 2 * wd + 1, s1, o1);
-      const v16f sv = {s0, s0, s0, s0, s0, s0, s0, s0, s1, s1, s1, s1, s1, s1, s1, s1};
-      tot[r] = sv * acc[r] + tot[r];
-      offs[r] += o0 * xs[2 * wd] + o1 * xs[2 * wd + 1];
+  }
+  // Block parameters of the 16 rows (fp16 -> fp32 16 at a time), then the
+  // scaled block sums: out[n] = sum over b of s[n][b] acc[b][n] + off[n][b] X[b].
+  alignas(64) float S[16 * 8], M[16 * 8];
+  if (fmt == kQ2) {  // (scale, min) pairs, row-major [n][b][2]
+    alignas(64) float P[16 * 16];
+    for (int i = 0; i < 16; ++i)
+      _mm512_store_ps(P + 16 * i, _mm512_cvtph_ps(_mm256_loadu_si256(
+                                      reinterpret_cast<const __m256i*>(rec + 1024 + 32 * i))));
+    for (int i = 0; i < 128; ++i) {
+      S[i] = P[2 * i];
+      M[i] = P[2 * i + 1];
     }
+  } else {  // scales [n][b]
+    const int base = fmt == kQ3 ? 1536 : 1024;
+    for (int i = 0; i < 8; ++i)
+      _mm512_store_ps(S + 16 * i, _mm512_cvtph_ps(_mm256_loadu_si256(
+                                      reinterpret_cast<const __m256i*>(rec + base + 32 * i))));
+    const float k = fmt == kQ3 ? -4.f : -2.f;  // w = s (u - 4) or s (u - 2)
+    for (int i = 0; i < 128; ++i) M[i] = k * S[i];
   }
-  for (int r = 0; r < 4; ++r) {
-    const v16f t = tot[r];
-    float s8[8];
-    for (int i = 0; i < 8; ++i) s8[i] = t[i] + t[i + 8];
-    out[r] = (((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]))) + offs[r];
+  const __m512i col8 = _mm512_setr_epi32(0, 8, 16, 24, 32, 40, 48, 56, 64, 72, 80, 88, 96, 104, 112, 120);
+  __m512 o = _mm512_setzero_ps();
+  for (int b = 0; b < 8; ++b) {
+    const __m512i ib = _mm512_add_epi32(col8, _mm512_set1_epi32(b));
+    o = _mm512_fmadd_ps(_mm512_i32gather_ps(ib, S, 4), acc[b], o);
+    o = _mm512_fmadd_ps(_mm512_i32gather_ps(ib, M, 4), _mm512_set1_ps(xs[b]), o);
   }
+  _mm512_storeu_ps(out, o);
 }
 
-// Four rows with the SSE2 row dot product.
+// All 16 rows of a record with the AVX2 + FMA or the SSE2 four-row kernels.
 void record_rows4_sse2(const uint8_t* rec, int fmt, int n0, const float* xv, const float* xs,
                        float* out) {
   for (int r = 0; r < 4; ++r) out[r] = record_row_dot_sse2(rec, fmt, n0 + r, xv, xs);
 }
+void record_rows16_sse2(const uint8_t* rec, int fmt, const float* xv, const float* xs, float* out) {
+  for (int n0 = 0; n0 < 16; n0 += 4) record_rows4_sse2(rec, fmt, n0, xv, xs, out + n0);
+}
+__attribute__((target("avx2,fma"))) void record_rows16_avx2(const uint8_t* rec, int fmt,
+                                                            const float* xv, const float* xs,
+                                                            float* out) {
+  for (int n0 = 0; n0 < 16; n0 += 4) record_rows4_avx2(rec, fmt, n0, xv, xs, out + n0);
+}
 
-// The row dot products this process uses: AVX-512F, else AVX2 + FMA, where
-// the CPU has them, else SSE2.  MOE_HOST_SIMD=avx2 or =sse2 in the
-// environment caps the choice (read at every host layer call).  They differ
-// only in fp32 rounding order.
-typedef void (*RowDot)(const uint8_t*, int, int, const float*, const float*, float*);
+// The record dot products this process uses: AVX-512F (with F16C), else
+// AVX2 + FMA, where the CPU has them, else SSE2.  MOE_HOST_SIMD=avx2 or
+// =sse2 in the environment caps the choice (read at every host layer call).
+// They differ only in fp32 rounding order.
+typedef void (*Rows16)(const uint8_t*, int, const float*, const float*, float*);
 // The CPU's features come from the flags line of /proc/cpuinfo, which lists
 // only what the kernel has enabled (AVX state included).
 struct CpuSimd {
@@ -287,38 +325,23 @@ CpuSimd cpu_simd() {
     if (line.compare(0, 5, "flags") != 0) continue;
     const std::string l = " " + line + " ";
     c.avx2_fma = l.find(" avx2 ") != std::string::npos && l.find(" fma ") != std::string::npos;
-    c.avx512f = l.find(" avx512f ") != std::string::npos;
+    c.avx512f = l.find(" avx512f ") != std::string::npos && l.find(" f16c ") != std::string::npos;
     break;
   }
   return c;
 }
-RowDot row_dot_impl() {
+Rows16 rows16_impl() {
   static const CpuSimd cpu = cpu_simd();
   const char* e = getenv("MOE_HOST_SIMD");
   const bool cap_sse2 = e && strcmp(e, "sse2") == 0, cap_avx2 = e && strcmp(e, "avx2") == 0;
-  if (cap_sse2) return record_rows4_sse2;
-  if (cpu.avx512f && !cap_avx2) return record_rows4_avx512;
-  return cpu.avx2_fma ? record_rows4_avx2 : record_rows4_sse2;
+  if (cap_sse2) return record_rows16_sse2;
+  if (cpu.avx512f && !cap_avx2) return record_rows16_avx512;
+  return cpu.avx2_fma ? record_rows16_avx2 : record_rows16_sse2;
 }
-// Which implementation row_dot_impl picks (for the callers' reports).
+// Which implementation rows16_impl picks (for the callers' reports).
 const char* row_dot_name() {
-  const RowDot d = row_dot_impl();
-  return d == record_rows4_avx512 ? "avx512" : (d == record_rows4_avx2 ? "avx2" : "sse2");
-}
-
-// Rows row0 .. row0 + 3 (row0 % 4 == 0) of a matrix stored from `base` as
-// 16-row groups of octet records (reduction length K), dotted with the
-// record-order vector v; out[r] gets row row0 + r.
-void matrix_rows4_dot(RowDot dot, const uint8_t* base, int fmt, int row0, int K, const RecVec& v,
-                      float* out) {
-  const int oK = (K + 255) / 256, rb = rec_bytes(fmt);
-  const uint8_t* grp = base + (size_t)(row0 / 16) * oK * rb;
-  float s[4] = {0.f, 0.f, 0.f, 0.f}, p[4];
-  for (int o = 0; o < oK; ++o) {
-    dot(grp + (size_t)o * rb, fmt, row0 % 16, &v.v[(size_t)o * 256], &v.sum[(size_t)o * 8], p);
-    for (int r = 0; r < 4; ++r) s[r] += p[r];
-  }
-  for (int r = 0; r < 4; ++r) out[r] = s[r];
+  const Rows16 d = rows16_impl();
+  return d == record_rows16_avx512 ? "avx512" : (d == record_rows16_avx2 ? "avx2" : "sse2");
 }
 
 }  // namespace
@@ -355,8 +378,8 @@ hipError_t launch_add_rows(void* out, int out_bf16, const float* y, size_t n, hi
 // y[t] = sum over the misses of token t, in list order, of gate * FFN_e(xhat_t).
 void host_miss_ffn(int D, int F, int fmt, int T, const float* xhat, const MissRec* miss, int nm,
                    const uint8_t* const* experts, float* y, moe_host_pool* pool) {
-  const int ng = F / 16, oD = D / 256, rb = rec_bytes(fmt);
-  const RowDot dot = row_dot_impl();
+  const int ng = F / 16, oD = D / 256, oF = (F + 255) / 256, rb = rec_bytes(fmt);
+  const Rows16 dot = rows16_impl();
   std::vector<RecVec> xr(T);
   for (int t = 0; t < T; ++t) xr[t].set(xhat + (size_t)t * D, D);
   std::vector<float> h((size_t)nm * F, 0.f);
@@ -367,17 +390,15 @@ void host_miss_ffn(int D, int F, int fmt, int T, const float* xhat, const MissRe
     const RecVec& x = xr[miss[m].token];
     const uint8_t* gate = ex + (size_t)(2 * g) * oD * rb;
     const uint8_t* up = ex + (size_t)(2 * g + 1) * oD * rb;
-    for (int n0 = 0; n0 < 16; n0 += 4) {
-      float a[4] = {0.f, 0.f, 0.f, 0.f}, b[4] = {0.f, 0.f, 0.f, 0.f}, p[4];
-      for (int o = 0; o < oD; ++o) {
-        dot(gate + (size_t)o * rb, fmt, n0, &x.v[(size_t)o * 256], &x.sum[(size_t)o * 8], p);
-        for (int r = 0; r < 4; ++r) a[r] += p[r];
-        dot(up + (size_t)o * rb, fmt, n0, &x.v[(size_t)o * 256], &x.sum[(size_t)o * 8], p);
-        for (int r = 0; r < 4; ++r) b[r] += p[r];
-      }
-      for (int r = 0; r < 4; ++r)
-        h[(size_t)m * F + 16 * g + n0 + r] = a[r] / (1.0f + expf(-a[r])) * b[r];
+    float a[16] = {}, b[16] = {}, p[16];
+    for (int o = 0; o < oD; ++o) {
+      dot(gate + (size_t)o * rb, fmt, &x.v[(size_t)o * 256], &x.sum[(size_t)o * 8], p);
+      for (int r = 0; r < 16; ++r) a[r] += p[r];
+      dot(up + (size_t)o * rb, fmt, &x.v[(size_t)o * 256], &x.sum[(size_t)o * 8], p);
+      for (int r = 0; r < 16; ++r) b[r] += p[r];
     }
+    for (int r = 0; r < 16; ++r)
+      h[(size_t)m * F + 16 * g + r] = a[r] / (1.0f + expf(-a[r])) * b[r];
   };
   if (pool) pool->run(nm * ng, gateup);
   else for (int i = 0; i < nm * ng; ++i) gateup(i);
@@ -388,13 +409,14 @@ void host_miss_ffn(int D, int F, int fmt, int T, const float* xhat, const MissRe
   for (size_t i = 0; i < (size_t)T * D; ++i) y[i] = 0.f;
   auto down = [&](int rg) {
     for (int m = 0; m < nm; ++m) {
-      const uint8_t* dn = experts[miss[m].expert] + down_offset(D, F, fmt);
-      float* yt = y + (size_t)miss[m].token * D;
-      for (int r0 = 16 * rg; r0 < 16 * rg + 16; r0 += 4) {
-        float p[4];
-        matrix_rows4_dot(dot, dn, fmt, r0, F, hr[m], p);
-        for (int r = 0; r < 4; ++r) yt[r0 + r] += miss[m].gate * p[r];
+      const uint8_t* grp = experts[miss[m].expert] + down_offset(D, F, fmt) + (size_t)rg * oF * rb;
+      float s[16] = {}, p[16];
+      for (int o = 0; o < oF; ++o) {
+        dot(grp + (size_t)o * rb, fmt, &hr[m].v[(size_t)o * 256], &hr[m].sum[(size_t)o * 8], p);
+        for (int r = 0; r < 16; ++r) s[r] += p[r];
       }
+      float* yt = y + (size_t)miss[m].token * D + 16 * rg;
+      for (int r = 0; r < 16; ++r) yt[r] += miss[m].gate * s[r];
     }
   };
   if (pool) pool->run(D / 16, down);
