@@ -646,6 +646,22 @@ def bench_slot_policy(ctx, name="slot_policy_q3s_t1_8l"):
     return w, static, adaptive
 
 
+def huge_host_array(nbytes):
+    """Zeroed host memory of nbytes, 2 MiB-aligned, advised to be backed by
+    transparent huge pages (madvise): the host miss path reads the experts of
+    random misses, and with 4 KiB pages those cold reads also miss the TLB.
+    Returns (keep-alive object, uint8 numpy view)."""
+    import ctypes
+    import mmap
+    import numpy as np
+    mm = mmap.mmap(-1, nbytes + (2 << 20), flags=mmap.MAP_PRIVATE | mmap.MAP_ANONYMOUS)
+    buf = np.frombuffer(mm, np.uint8)
+    off = (-buf.ctypes.data) % (2 << 20)
+    libc = ctypes.CDLL("libc.so.6")
+    libc.madvise(ctypes.c_void_p(buf.ctypes.data + off), ctypes.c_size_t(nbytes), 14)  # MADV_HUGEPAGE
+    return mm, buf[off:off + nbytes]
+
+
 def bench_slot_host(ctx, n_tokens=16, name="slot_host_q3s_t1_8l"):
     """Each token through L chained slot layers; after each layer the miss
     list comes to the host, the host pool computes those rows and they are
@@ -658,7 +674,8 @@ def bench_slot_host(ctx, n_tokens=16, name="slot_host_q3s_t1_8l"):
     st = []
     for l in range(L):
         full = ctx.build_layer(shape, 0, l, ctx.dev)
-        host = full.routed.cpu().numpy()                 # every routed expert in host memory
+        hmm, host = huge_host_array(full.routed.numel())  # every routed expert in host memory
+        torch.from_numpy(host).copy_(full.routed)
         ranks = synth.expert_ranks(0, l, E)
         resident = [int(e) for e in np.argsort(ranks)[:R]]
         slot_of = torch.empty(E, dtype=torch.int32, device=ctx.dev)
@@ -674,7 +691,7 @@ def bench_slot_host(ctx, n_tokens=16, name="slot_host_q3s_t1_8l"):
                                       [full.routed.data_ptr() + e * stride for e in resident[i0:i0 + 32]])
         torch.cuda.synchronize()
         del full.routed
-        st.append(dict(t=t, keep=(slot_of, eos, hs, he, storage, full.shared), host=host,
+        st.append(dict(t=t, keep=(slot_of, eos, hs, he, storage, full.shared, hmm), host=host,
                        ptrs=[host.ctypes.data + e * stride for e in range(E)],
                        table=moe.MoeExpertTable(storage.data_ptr(), stride, slot_of.data_ptr(), R,
                                                 full.shared.data_ptr())))

@@ -404,23 +404,28 @@ void host_miss_ffn(int D, int F, int fmt, int T, const float* xhat, const MissRe
   else for (int i = 0; i < nm * ng; ++i) gateup(i);
   std::vector<RecVec> hr(nm);
   for (int m = 0; m < nm; ++m) hr[m].set(&h[(size_t)m * F], F);
-  // Phase 2: output rows, one item per 16-row group of d_model; each y[t][d]
-  // sums its token's misses in list order.
+  // Phase 2: output rows, one item per kDownGroups 16-row groups of d_model
+  // (items of a few microseconds, so that claiming them stays cheap); each
+  // y[t][d] sums its token's misses in list order.
   for (size_t i = 0; i < (size_t)T * D; ++i) y[i] = 0.f;
-  auto down = [&](int rg) {
-    for (int m = 0; m < nm; ++m) {
-      const uint8_t* grp = experts[miss[m].expert] + down_offset(D, F, fmt) + (size_t)rg * oF * rb;
-      float s[16] = {}, p[16];
-      for (int o = 0; o < oF; ++o) {
-        dot(grp + (size_t)o * rb, fmt, &hr[m].v[(size_t)o * 256], &hr[m].sum[(size_t)o * 8], p);
-        for (int r = 0; r < 16; ++r) s[r] += p[r];
+  constexpr int kDownGroups = 4;
+  const int nrg = D / 16, nitems = (nrg + kDownGroups - 1) / kDownGroups;
+  auto down = [&](int it) {
+    for (int rg = it * kDownGroups; rg < nrg && rg < (it + 1) * kDownGroups; ++rg)
+      for (int m = 0; m < nm; ++m) {
+        const uint8_t* grp =
+            experts[miss[m].expert] + down_offset(D, F, fmt) + (size_t)rg * oF * rb;
+        float s[16] = {}, p[16];
+        for (int o = 0; o < oF; ++o) {
+          dot(grp + (size_t)o * rb, fmt, &hr[m].v[(size_t)o * 256], &hr[m].sum[(size_t)o * 8], p);
+          for (int r = 0; r < 16; ++r) s[r] += p[r];
+        }
+        float* yt = y + (size_t)miss[m].token * D + 16 * rg;
+        for (int r = 0; r < 16; ++r) yt[r] += miss[m].gate * s[r];
       }
-      float* yt = y + (size_t)miss[m].token * D + 16 * rg;
-      for (int r = 0; r < 16; ++r) yt[r] += miss[m].gate * s[r];
-    }
   };
-  if (pool) pool->run(D / 16, down);
-  else for (int i = 0; i < D / 16; ++i) down(i);
+  if (pool) pool->run(nitems, down);
+  else for (int i = 0; i < nitems; ++i) down(i);
 }
 
 void host_prepare_x(int T, int D, const void* x, bool x_bf16, bool rms, float* out) {

@@ -4,8 +4,10 @@
 //
 // A layer call runs two short parallel phases, so waking sleeping threads
 // would cost more than the work: workers poll for a new job for a while
-// (about 100 us) before they sleep on the condition variable, and the caller
-// waits for the items, not for every worker.  Items are claimed by
+// (kSpin polls with a pause instruction between them, a few milliseconds:
+// longer than the GPU half of a layer between two host phases) before they
+// sleep on the condition variable, and the caller waits for the items, not
+// for every worker.  Items are claimed by
 // compare-and-swap on one word, (generation << 32 | next item).
 //
 // Publication order of a job (run): first the word moves to the new
@@ -60,7 +62,12 @@ struct moe_host_pool {
       uint32_t g;
       int polls = 0;
       while ((g = gen.load(std::memory_order_acquire)) == seen) {
-        if (++polls < kSpin) continue;
+        if (++polls < kSpin) {
+#if defined(__x86_64__)
+          __builtin_ia32_pause();  // yields the core's issue slots while polling
+#endif
+          continue;
+        }
         std::unique_lock<std::mutex> lk(mu);
         cv.wait(lk, [&] { return stop || gen.load(std::memory_order_acquire) != seen; });
         if (stop) return;

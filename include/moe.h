@@ -358,7 +358,10 @@ const char* moe_host_simd(void);
  *             layer returns them (gates are the full top-k gates).
  *   experts:  host [n_experts] pointers to packed experts (the layout above,
  *             shape->qfmt) in host memory; the entry of every missed expert
- *             must be non-NULL.
+ *             must be non-NULL.  The misses of a layer are random experts,
+ *             read cold: memory backed by 2 MiB pages (madvise
+ *             MADV_HUGEPAGE) spares those reads TLB misses (measured: a
+ *             3-miss Q3S layer on 16 threads, 0.137 instead of 0.181 ms).
  *   y:        host fp32 [tokens][d_model], written in full.
  *   pool:     worker threads, or NULL for the calling thread alone.
  * fp32 throughout (weights exact in fp32).  Deterministic: each output
