@@ -200,3 +200,116 @@ def test_graph_slot_layer_miss_list(g):
         assert int(mcount.item()) == n
         assert torch.equal(miss.view(-1, 4)[:n], want)
     del graph
+
+
+def test_graph_decode_stack_four_tokens(g):
+    """Four tokens through six chained layers as one moe_decode_stack_forward
+    call: the plan kernel, the layers and the RMS partials between them."""
+    import torch
+    moe = g.moe
+    w = synth.WORKLOADS["mtp_verify_t4_48l"]
+    shape, T, D, E, NL = _shape(g, w), 4, w["d_model"], w["n_experts"], 6
+    layers = [g.build_layer(shape, 0, l, g.DEV) for l in range(NL)]
+    tables = [ly.table() for ly in layers]
+    x = g.u16_to_dev(synth.activations_bf16(0, 16, T, D))
+    x_other = g.u16_to_dev(synth.activations_bf16(0, 17, T, D))
+    lg = g.f32_to_dev(np.stack([synth.router_logits(0, l, T, E, zipf_s=w["zipf_s"], alpha=w["alpha"])
+                                for l in range(NL)]))
+    lg_other = g.f32_to_dev(np.stack([synth.router_logits(1, l, T, E, zipf_s=w["zipf_s"],
+                                                          alpha=w["alpha"]) for l in range(NL)]))
+    wsb = moe.moe_decode_stack_workspace_bytes(shape, NL, T)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=g.DEV)
+    out = torch.empty(NL * T * D, dtype=torch.int16, device=g.DEV)
+    out_other = torch.empty_like(out)
+
+    def step():
+        moe.moe_decode_stack_forward(shape, NL, T, x, moe.MOE_BF16, lg, tables, out, moe.MOE_BF16,
+                                     None, None, ws, wsb)
+
+    def dirty():
+        moe.moe_decode_stack_forward(shape, NL, T, x_other, moe.MOE_BF16, lg_other, tables,
+                                     out_other, moe.MOE_BF16, None, None, ws, wsb)
+
+    _check_replays(g, step, [out], dirty)
+
+
+def test_graph_q3s_slot_prefill(g):
+    """A 300-token Q3S prefill on a slot table (half of the experts
+    resident): partial output, miss list and its count."""
+    import torch
+    moe = g.moe
+    D, F, E, k, Fs, T = 256, 64, 16, 2, 64, 300
+    shape = moe.MoeShape(D, F, E, k, Fs, synth.FMT_Q3S)
+    L = g.build_layer(shape, 0, 9, g.DEV)
+    resident = list(range(0, E, 2))
+    slot_of = torch.full((E,), -1, dtype=torch.int32, device=g.DEV)
+    storage = torch.empty(len(resident) * L.stride, dtype=torch.uint8, device=g.DEV)
+    for s_, e in enumerate(resident):
+        slot_of[e] = s_
+        storage[s_ * L.stride:(s_ + 1) * L.stride].copy_(L.routed[e * L.stride:(e + 1) * L.stride])
+    table = L.table(slot_of=slot_of, n_slots=len(resident), routed=storage)
+    x = g.u16_to_dev(synth.activations_bf16(0, 40, T, D))
+    x_other = g.u16_to_dev(synth.activations_bf16(0, 41, T, D))
+    lg = g.f32_to_dev(synth.router_logits(0, 40, T, E, min_gap=1e-3))
+    lg_other = g.f32_to_dev(synth.router_logits(1, 41, T, E, min_gap=1e-3))
+    wsb = moe.moe_workspace_bytes(shape, T)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=g.DEV)
+    out = torch.empty(T * D, dtype=torch.float32, device=g.DEV)
+    # the miss entries past the count are never written: starting from the
+    # poison value of the replays, the whole buffer must replay exactly
+    miss = torch.full((T * k * 4,), -1, dtype=torch.int32, device=g.DEV)
+    cnt = torch.empty(1, dtype=torch.int32, device=g.DEV)
+    out_o, miss_o, cnt_o = torch.empty_like(out), torch.empty_like(miss), torch.empty_like(cnt)
+
+    def step():
+        moe.moe_layer_forward(shape, T, x, moe.MOE_BF16, 0, lg, table, out, moe.MOE_F32, miss,
+                              T * k, cnt, ws, wsb)
+
+    def dirty():
+        moe.moe_layer_forward(shape, T, x_other, moe.MOE_BF16, 0, lg_other, table, out_o,
+                              moe.MOE_F32, miss_o, T * k, cnt_o, ws, wsb)
+
+    _check_replays(g, step, [out, miss, cnt], dirty)
+
+
+def test_graph_slot_stack_one_token(g):
+    """One token through four chained Q3S slot layers as one stack call:
+    outputs, miss lists and counts of every layer."""
+    import torch
+    moe = g.moe
+    w = synth.WORKLOADS["slot_q3s_t1_48l"]
+    shape, T, D, E, k, NL, R = _shape(g, w), 1, w["d_model"], w["n_experts"], w["top_k"], 4, 128
+    keep, tables = [], []
+    for l in range(NL):
+        L = g.build_layer(shape, 0, l, g.DEV)
+        res = [int(e) for e in np.argsort(synth.expert_ranks(0, l, E))[:R]]
+        slot_of = torch.full((E,), -1, dtype=torch.int32, device=g.DEV)
+        storage = torch.empty(R * L.stride, dtype=torch.uint8, device=g.DEV)
+        for s_, e in enumerate(res):
+            slot_of[e] = s_
+            storage[s_ * L.stride:(s_ + 1) * L.stride].copy_(L.routed[e * L.stride:(e + 1) * L.stride])
+        keep.append((L.shared, slot_of, storage))
+        tables.append(L.table(slot_of=slot_of, n_slots=R, routed=storage))
+        del L
+    x = g.u16_to_dev(synth.activations_bf16(0, 50, T, D))
+    x_other = g.u16_to_dev(synth.activations_bf16(0, 51, T, D))
+    lg = g.f32_to_dev(np.stack([synth.router_logits(0, l, T, E, zipf_s=w["zipf_s"], alpha=w["alpha"])
+                                for l in range(NL)]))
+    lg_other = g.f32_to_dev(np.stack([synth.router_logits(1, l, T, E, zipf_s=w["zipf_s"],
+                                                          alpha=w["alpha"]) for l in range(NL)]))
+    wsb = moe.moe_decode_stack_workspace_bytes(shape, NL, T)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=g.DEV)
+    out = torch.empty(NL * T * D, dtype=torch.int16, device=g.DEV)
+    miss = torch.full((NL * T * k * 4,), -1, dtype=torch.int32, device=g.DEV)  # see above
+    cnt = torch.empty(NL, dtype=torch.int32, device=g.DEV)
+    out_o, miss_o, cnt_o = torch.empty_like(out), torch.empty_like(miss), torch.empty_like(cnt)
+
+    def step():
+        moe.moe_decode_stack_forward(shape, NL, T, x, moe.MOE_BF16, lg, tables, out, moe.MOE_BF16,
+                                     miss, cnt, ws, wsb)
+
+    def dirty():
+        moe.moe_decode_stack_forward(shape, NL, T, x_other, moe.MOE_BF16, lg_other, tables, out_o,
+                                     moe.MOE_BF16, miss_o, cnt_o, ws, wsb)
+
+    _check_replays(g, step, [out, miss, cnt], dirty)

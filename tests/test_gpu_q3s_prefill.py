@@ -140,3 +140,23 @@ def test_q3s_chunk_8192_whole_output(g, full):
     print("Q3S 8192-token chunk: whole-output rel_l2=%.3g, per-token max %.3g, median %.3g"
           % (err, per_token.max(), float(np.median(per_token))))
     assert err <= RTOL_L2
+
+
+@pytest.mark.parametrize("T", [7, 131])
+def test_q3s_prefill_odd_reduction_blocks(g, T):
+    """d_ff 96 and a shared width of 160: the down GEMM's reduction ends on an
+    odd 32-block, so its last k-step runs on the zero-scale padding of the
+    packed octet (Q3S builds no per-block tables that could zero it)."""
+    D, F, E, k, Fs = 256, 96, 16, 2, 160
+    shape = g.moe.MoeShape(D, F, E, k, Fs, synth.FMT_Q3S)
+    L = g.build_layer(shape, 0, 6, g.DEV)
+    ow = OracleWeights(0, 6, D, F, Fs, E, synth.FMT_Q3S)
+    logits = synth.router_logits(0, 27, T, E, min_gap=1e-3)
+    xb = synth.activations_bf16(0, 27, T, D)
+    run = g.LayerRun(shape, T)
+    out = run(L.table(), g.u16_to_dev(xb), g.moe.MOE_BF16, g.f32_to_dev(logits), g.moe.MOE_F32)
+    got = g.out_to_f64(out, False).reshape(T, D)
+    ref, _, _ = O.layer_forward(O.bf16_to_f64(xb), logits, k, ow, ow.shared)
+    err = rel_l2(got, ref)
+    print("Q3S prefill d_ff 96 / shared 160, T=%d: rel_l2=%.3g" % (T, err))
+    assert err <= RTOL_L2
