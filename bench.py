@@ -699,33 +699,21 @@ def bench_slot_host(ctx, n_tokens=16, name="slot_host_q3s_t1_8l"):
     logits = [ctx.dev_f32(synth.router_logits(0, l, n_tokens, E, zipf_s=w["zipf_s"],
                                               alpha=w["alpha"])) for l in range(L)]
     x0 = synth.activations_bf16(0, 0, n_tokens, D)
-    wsb = moe.moe_workspace_bytes(shape, 1)
+    # One moe_slot_layer_forward_host call per layer: the library enqueues
+    # the GPU half, copies the miss list and the input as soon as the
+    # routing is written, computes the missed experts on the host pool while
+    # the GPU computes the hits, and enqueues their addition into the output.
+    wsb = moe.moe_slot_host_workspace_bytes(shape, 1)
     ws = torch.empty(wsb, dtype=torch.uint8, device=ctx.dev)
+    stb = moe.moe_slot_host_staging_bytes(shape, 1)
+    stg = torch.empty(stb + 64, dtype=torch.uint8).pin_memory()
+    stg_addr = (stg.data_ptr() + 63) // 64 * 64
     outs = [torch.empty(D, dtype=torch.float32, device=ctx.dev) for _ in range(L)]
-    miss = torch.empty(k * 4, dtype=torch.int32, device=ctx.dev)
-    mcount = torch.zeros(1, dtype=torch.int32, device=ctx.dev)
-    miss_h = torch.empty(k * 4 + 1, dtype=torch.int32).pin_memory()
-    y_h = torch.empty(D, dtype=torch.float32).pin_memory()
-    y_d = torch.empty(D, dtype=torch.float32, device=ctx.dev)
-    xin_h = torch.empty(D, dtype=torch.float32).pin_memory()
     x0_d = ctx.dev_u16(x0).reshape(-1)
     threads = min(16, os.cpu_count() or 1)
     pool = moe.HostPool(threads)
     host_s = 0.0
     nmiss = 0
-    # The host starts on a layer's misses as soon as the GPU has written the
-    # miss list (moe_set_route_event), while the GPU still computes the hits:
-    # the list, its count and the layer input are copied on a side stream
-    # that waits for that event.
-    import ctypes
-    hip = ctypes.CDLL("libamdhip64.so")
-    hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
-    hip.hipStreamWaitEvent.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint]
-    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
-    ev_route = ctypes.c_void_p()
-    if hip.hipEventCreateWithFlags(ctypes.byref(ev_route), 2):     # hipEventDisableTiming
-        raise RuntimeError("hipEventCreateWithFlags failed")
-    side = torch.cuda.Stream()
 
     def token(i):
         nonlocal host_s, nmiss
@@ -733,29 +721,11 @@ def bench_slot_host(ctx, n_tokens=16, name="slot_host_q3s_t1_8l"):
             fl = 0 if l == 0 else moe.MOE_FLAG_RMSNORM_INPUT
             x = x0_d[i * D:(i + 1) * D] if l == 0 else outs[l - 1]
             xdt = moe.MOE_BF16 if l == 0 else moe.MOE_F32
-            moe.moe_set_route_event(ev_route.value)
-            moe.moe_layer_forward(shape, 1, x, xdt, fl, logits[l].data_ptr() + 4 * i * E,
-                                  st[l]["table"], outs[l], moe.MOE_F32, miss, k, mcount, ws, wsb)
-            if hip.hipStreamWaitEvent(side.cuda_stream, ev_route.value, 0):
-                raise RuntimeError("hipStreamWaitEvent failed")
-            with torch.cuda.stream(side):
-                miss_h[: 4 * k].copy_(miss, non_blocking=True)
-                miss_h[4 * k:].copy_(mcount, non_blocking=True)
-                if l > 0:
-                    xin_h.copy_(outs[l - 1], non_blocking=True)   # the layer input
-            side.synchronize()
-            nm = int(miss_h[4 * k].item())
-            nmiss += nm
             h0 = time.perf_counter()
-            if l == 0:
-                xp, xd = x0[i].ctypes.data, moe.MOE_BF16
-            else:
-                xp, xd = xin_h.data_ptr(), moe.MOE_F32
-            moe.moe_host_miss_ffn(shape, 1, xp, xd, fl, miss_h.data_ptr(), nm, st[l]["ptrs"],
-                                  y_h.data_ptr(), pool)
+            nmiss += moe.moe_slot_layer_forward_host(
+                shape, 1, x, xdt, fl, logits[l].data_ptr() + 4 * i * E, st[l]["table"], outs[l],
+                moe.MOE_F32, st[l]["ptrs"], ws, wsb, stg_addr, stb, pool)
             host_s += time.perf_counter() - h0
-            y_d.copy_(y_h, non_blocking=True)
-            moe.moe_add_rows(outs[l], moe.MOE_F32, y_d, 1, D)
 
     token(0)
     torch.cuda.synchronize()
@@ -766,7 +736,6 @@ def bench_slot_host(ctx, n_tokens=16, name="slot_host_q3s_t1_8l"):
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     pool.close()
-    hip.hipEventDestroy(ev_route)
     n = n_tokens - 1
     return dict(tokens=n, seconds=dt, host_s=host_s, misses_per_layer=nmiss / (n * L),
                 hit_rate=1.0 - nmiss / (n * L * k), threads=threads, layers=L,
@@ -1147,14 +1116,15 @@ def main():
         n, L = r["tokens"], r["layers"]
         results["slot_host_q3s_t1_8l"] = dict(
             value=n / r["seconds"], unit="tokens/s", steps=n, ms_per_step=r["seconds"] / n * 1e3,
-            host_ms_per_layer=r["host_s"] / (n * L) * 1e3,
+            host_call_ms_per_layer=r["host_s"] / (n * L) * 1e3,
             layer_ms=r["seconds"] / (n * L) * 1e3, misses_per_layer=r["misses_per_layer"],
             hit_rate=r["hit_rate"], host_threads=r["threads"], host_simd=r["host_simd"],
             config="1 token x 8 chained Q3S slot layers, 128/512 resident (Zipf 1.2, alpha "
-                   "0.331); misses computed on the host (fp32, %d threads, %s) while the GPU "
-                   "computes the hits, then added into each layer's output"
+                   "0.331); one moe_slot_layer_forward_host call per layer: misses computed "
+                   "on the host (fp32, %d threads, %s) while the GPU computes the hits, then "
+                   "added into the layer's output"
                    % (r["threads"], r["host_simd"]))
-        print("slot_host_q3s_t1_8l: %.2f ms/token, host %.3f ms/layer, %.2f misses/layer" %
+        print("slot_host_q3s_t1_8l: %.2f ms/token, layer call %.3f ms, %.2f misses/layer" %
               (r["seconds"] / n * 1e3, r["host_s"] / (n * L) * 1e3, r["misses_per_layer"]),
               file=sys.stderr, flush=True)
         torch.cuda.empty_cache()

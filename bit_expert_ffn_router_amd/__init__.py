@@ -28,6 +28,7 @@ __all__ = [
     "moe_slot_counts_take", "moe_slot_policy_plan", "moe_slot_table_stage",
     "moe_slot_table_commit", "HostPool", "moe_host_miss_ffn", "moe_add_rows",
     "moe_set_route_event", "moe_host_simd", "moe_decode_stack_workspace_bytes",
+    "moe_slot_host_workspace_bytes", "moe_slot_host_staging_bytes", "moe_slot_layer_forward_host",
     "moe_decode_stack_forward",
     "LIB_PATH",
 ]
@@ -120,6 +121,11 @@ _sigs = {
     "moe_host_miss_ffn": (_I, [ctypes.POINTER(MoeShape), _I, _P, _I, ctypes.c_uint32, _P, _I, _P,
                                _P, _P]),
     "moe_add_rows": (_I, [_P, _I, _P, _I, _I, _P]),
+    "moe_slot_host_workspace_bytes": (_Z, [ctypes.POINTER(MoeShape), _I]),
+    "moe_slot_host_staging_bytes": (_Z, [ctypes.POINTER(MoeShape), _I]),
+    "moe_slot_layer_forward_host": (_I, [ctypes.POINTER(MoeShape), _I, _P, _I, ctypes.c_uint32,
+                                         _P, ctypes.POINTER(MoeExpertTable), _P, _I, _P, _P, _P,
+                                         _Z, _P, _Z, _P, _P]),
     "moe_set_route_event": (_I, [_P]),
     "moe_decode_stack_workspace_bytes": (_Z, [ctypes.POINTER(MoeShape), _I, _I]),
     "moe_decode_stack_forward": (_I, [ctypes.POINTER(MoeShape), _I, _I, _P, _I, _P, _P, _P, _I,
@@ -283,6 +289,30 @@ def moe_host_miss_ffn(shape, tokens, x_host, x_dtype, flags, misses, n_miss, exp
 
 def moe_add_rows(out, out_dtype, y, tokens, d_model, stream=None):
     _check(_lib.moe_add_rows(_ptr(out), out_dtype, _ptr(y), tokens, d_model, _stream(stream)))
+
+
+def moe_slot_host_workspace_bytes(shape, tokens: int) -> int:
+    return _lib.moe_slot_host_workspace_bytes(ctypes.byref(shape), tokens)
+
+
+def moe_slot_host_staging_bytes(shape, tokens: int) -> int:
+    return _lib.moe_slot_host_staging_bytes(ctypes.byref(shape), tokens)
+
+
+def moe_slot_layer_forward_host(shape, tokens, x, x_dtype, flags, router_logits, table, out,
+                                out_dtype, expert_ptrs, ws, ws_bytes, staging, staging_bytes,
+                                pool=None, stream=None) -> int:
+    """expert_ptrs: host addresses of the packed experts (0/None for experts never
+    missed); staging: pinned host memory (address or tensor).  Returns the
+    number of misses the host computed."""
+    arr = (ctypes.c_void_p * max(len(expert_ptrs), 1))(*[p or None for p in expert_ptrs])
+    nm = ctypes.c_int32(0)
+    _check(_lib.moe_slot_layer_forward_host(
+        ctypes.byref(shape), tokens, _ptr(x), x_dtype, flags, _ptr(router_logits),
+        ctypes.byref(table), _ptr(out), out_dtype, ctypes.cast(arr, _P), ctypes.byref(nm),
+        _ptr(ws), ws_bytes, _ptr(staging), staging_bytes,
+        pool.h if pool is not None else None, _stream(stream)))
+    return nm.value
 
 
 def moe_route(logits, tokens, n_experts, top_k, idx, gate, stream=None):

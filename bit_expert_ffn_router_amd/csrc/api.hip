@@ -660,6 +660,136 @@ moe_status moe_add_rows(void* out, int32_t out_dtype, const float* y, int32_t to
                     "add launch");
 }
 
+}  // extern "C"
+
+namespace {
+
+// The calling thread's side stream and event on the current device, made on
+// first use and kept until the process ends (non-blocking, default priority).
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t ev = nullptr;
+};
+hipError_t side_stream(SideStream*& out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= moe::kMaxDevices) return hipErrorInvalidDevice;
+  thread_local SideStream per[moe::kMaxDevices];
+  SideStream& ss = per[dev];
+  if (!ss.ev) {
+    if (!ss.s && (e = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&ss.ev, hipEventDisableTiming)) != hipSuccess) return e;
+  }
+  out = &ss;
+  return hipSuccess;
+}
+
+// Device workspace of moe_slot_layer_forward_host: the layer's workspace,
+// the miss records with their count right behind them, the host rows.
+struct SlotHostWs {
+  size_t miss, y, total;
+};
+SlotHostWs slot_host_ws(const moe_shape* s, int T) {
+  auto a256 = [](size_t n) { return (n + 255) / 256 * 256; };
+  const size_t fws = a256(forward_ws_bytes(s, T));
+  const size_t miss = a256((size_t)T * s->top_k * sizeof(moe_miss) + 4);
+  return {fws, fws + miss, fws + miss + a256((size_t)T * s->d_model * 4)};
+}
+// Pinned host staging: miss records + count, the layer input (fp32-sized),
+// the host rows.
+struct SlotHostStaging {
+  size_t x, y, total;
+};
+SlotHostStaging slot_host_staging(const moe_shape* s, int T) {
+  auto a64 = [](size_t n) { return (n + 63) / 64 * 64; };
+  const size_t m = a64((size_t)T * s->top_k * sizeof(moe_miss) + 4);
+  const size_t row = a64((size_t)T * s->d_model * 4);
+  return {m, m + row, m + 2 * row};
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_slot_host_workspace_bytes(const moe_shape* shape, int32_t tokens) {
+  if (check_shape(shape) != MOE_OK || tokens <= 0) return 0;
+  return slot_host_ws(shape, tokens).total;
+}
+
+size_t moe_slot_host_staging_bytes(const moe_shape* shape, int32_t tokens) {
+  if (check_shape(shape) != MOE_OK || tokens <= 0) return 0;
+  return slot_host_staging(shape, tokens).total;
+}
+
+moe_status moe_slot_layer_forward_host(const moe_shape* shape, int32_t tokens, const void* x,
+                                       int32_t x_dtype, uint32_t flags, float* router_logits,
+                                       const moe_expert_table* table, void* out,
+                                       int32_t out_dtype, const void* const* host_experts,
+                                       int32_t* n_miss, void* ws, size_t ws_bytes,
+                                       void* staging, size_t staging_bytes, moe_host_pool* pool,
+                                       moe_stream_t stream) {
+  moe_status s = check_shape(shape);
+  if (s != MOE_OK) return s;
+  const int T = tokens;
+  if (T < 0) return fail(MOE_EINVAL, "tokens %d < 0", T);
+  if (!table || !table->slot_of) return fail(MOE_EINVAL, "a slot table (table->slot_of) is required");
+  if (T == 0) {
+    if (n_miss) *n_miss = 0;
+    return ok();
+  }
+  if (!host_experts) return fail(MOE_EINVAL, "host_experts is required");
+  if (!staging || ((uintptr_t)staging & 63u)) return fail(MOE_EINVAL, "staging must be 64-byte aligned");
+  if (!ws || !aligned256(ws)) return fail(MOE_EINVAL, "ws must be given and 256-byte aligned");
+  const SlotHostWs L = slot_host_ws(shape, T);
+  const SlotHostStaging S = slot_host_staging(shape, T);
+  if (ws_bytes < L.total) return fail(MOE_ENOSPACE, "ws_bytes %zu < %zu", ws_bytes, L.total);
+  if (staging_bytes < S.total)
+    return fail(MOE_ENOSPACE, "staging_bytes %zu < %zu", staging_bytes, S.total);
+  hipStream_t st = (hipStream_t)stream;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone)
+    return fail(MOE_EUNSUPPORTED, "moe_slot_layer_forward_host waits on the host: not for capture");
+  SideStream* side = nullptr;
+  s = hip_status(side_stream(side), "side stream");
+  if (s != MOE_OK) return s;
+  const int k = shape->top_k, D = shape->d_model;
+  const size_t mbytes = (size_t)T * k * sizeof(moe_miss);
+  uint8_t* wsb = (uint8_t*)ws;
+  uint8_t* stg = (uint8_t*)staging;
+  moe_miss* miss_d = (moe_miss*)(wsb + L.miss);
+  int32_t* cnt_d = (int32_t*)(wsb + L.miss + mbytes);
+  float* y_d = (float*)(wsb + L.y);
+  // 1. The layer on the stream; its routing records the side event.
+  moe::route_event().before = side->ev;
+  s = layer_forward_impl(shape, T, x, x_dtype, flags, router_logits, table, out, out_dtype, miss_d,
+                         T * k, cnt_d, ws, L.miss, false, stream);
+  const bool recorded = moe::route_event().before == nullptr;
+  moe::route_event().before = nullptr;
+  if (s != MOE_OK) return s;
+  if (!recorded) return fail(MOE_EHIP, "the layer did not record its routing event");
+  // 2. Miss list, count and input to the host once the routing is written.
+  hipError_t e;
+  if ((e = hipStreamWaitEvent(side->s, side->ev, 0)) != hipSuccess ||
+      (e = hipMemcpyAsync(stg, miss_d, mbytes + 4, hipMemcpyDeviceToHost, side->s)) != hipSuccess ||
+      (e = hipMemcpyAsync(stg + S.x, x, (size_t)T * D * (x_dtype == MOE_BF16 ? 2 : 4),
+                          hipMemcpyDeviceToHost, side->s)) != hipSuccess ||
+      (e = hipStreamSynchronize(side->s)) != hipSuccess)
+    return hip_status(e, "miss list copy");
+  const int32_t nm = *reinterpret_cast<const int32_t*>(stg + mbytes);
+  if (n_miss) *n_miss = nm;
+  if (nm == 0) return ok();
+  // 3. The missed experts' rows, while the GPU computes the resident ones.
+  s = moe_host_miss_ffn(shape, T, stg + S.x, x_dtype, flags, reinterpret_cast<const moe_miss*>(stg),
+                        nm, host_experts, reinterpret_cast<float*>(stg + S.y), pool);
+  if (s != MOE_OK) return s;
+  // 4. Into the layer output, behind the layer on the stream.
+  if ((e = hipMemcpyAsync(y_d, stg + S.y, (size_t)T * D * 4, hipMemcpyHostToDevice, st)) != hipSuccess)
+    return hip_status(e, "host rows copy");
+  return hip_status(moe::launch_add_rows(out, out_dtype == MOE_BF16, y_d, (size_t)T * D, st),
+                    "add launch");
+}
+
 moe_status moe_router_logits(const moe_shape* shape, int32_t tokens, const void* x,
                              int32_t x_dtype, uint32_t flags, const void* w_router, float* logits,
                              moe_stream_t stream) {

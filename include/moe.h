@@ -378,6 +378,50 @@ moe_status moe_host_miss_ffn(const moe_shape* shape, int32_t tokens, const void*
 moe_status moe_add_rows(void* out, int32_t out_dtype, const float* y, int32_t tokens,
                         int32_t d_model, moe_stream_t stream);
 
+/* A whole slot-mode layer with the host computing the misses, in one call:
+ * the pages' GPU computes the resident experts while the CPU computes the
+ * others, and both go into the same layer ([AF] section "命中率七成，代价是
+ * 答案会变"; [SL] section "12GB 显存装下 1250 亿参数").
+ *
+ * Enqueues moe_layer_forward on `stream` (partial layer and miss list, into
+ * the workspace); as soon as the routing and the miss list are written it
+ * copies the list, its count and the layer input into `staging` on a side
+ * stream of the calling thread, computes the missed experts' rows on the
+ * host (moe_host_miss_ffn on `pool`) while the GPU still computes the
+ * resident experts, then enqueues their copy to the workspace and their
+ * addition into `out` (moe_add_rows) on `stream`.  The call returns once
+ * the host rows are computed; `out` holds the whole layer when `stream`
+ * reaches that point.  Not for stream capture (it waits on the host).
+ *   shape, tokens, x (device), x_dtype, flags, router_logits, out,
+ *   out_dtype: as moe_layer_forward; table->slot_of is required.
+ *   host_experts: host [n_experts] pointers to every expert packed in host
+ *             memory (as moe_host_miss_ffn's experts; NULL allowed for
+ *             experts that are never missed).
+ *   n_miss:   host int32 receiving the number of misses, or NULL.
+ *   ws, ws_bytes: device workspace of moe_slot_host_workspace_bytes(shape,
+ *             tokens) bytes, 256-byte aligned.
+ *   staging, staging_bytes: pinned host memory (hipHostMalloc) of
+ *             moe_slot_host_staging_bytes(shape, tokens) bytes, 64-byte
+ *             aligned.  Its host rows are read by the copy this call
+ *             enqueues; a later call on the same stream overwrites them only
+ *             after its own routing, which follows that copy.
+ *   pool:     host worker threads, or NULL.
+ * The side stream (non-blocking, default priority) and its event are
+ * created on a thread's first call on a device and kept until the process
+ * ends.  Errors: those of moe_layer_forward; MOE_EINVAL for a miss whose
+ * host expert is NULL (then nothing is added: `out` stays the partial);
+ * MOE_EUNSUPPORTED while `stream` is capturing; MOE_EHIP for a failed copy
+ * or wait. */
+size_t moe_slot_host_workspace_bytes(const moe_shape* shape, int32_t tokens);
+size_t moe_slot_host_staging_bytes(const moe_shape* shape, int32_t tokens);
+moe_status moe_slot_layer_forward_host(const moe_shape* shape, int32_t tokens, const void* x,
+                                       int32_t x_dtype, uint32_t flags, float* router_logits,
+                                       const moe_expert_table* table, void* out,
+                                       int32_t out_dtype, const void* const* host_experts,
+                                       int32_t* n_miss, void* ws, size_t ws_bytes,
+                                       void* staging, size_t staging_bytes, moe_host_pool* pool,
+                                       moe_stream_t stream);
+
 /* Router projection (the router the pages keep resident on the GPU, [AF]
  * section "命中率七成，代价是答案会变"; they give no formula; reading taken:
  * an unquantised bf16 linear map without bias):

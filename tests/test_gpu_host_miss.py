@@ -195,3 +195,101 @@ def test_route_event_marks_a_complete_miss_list(g, T):
         assert early == ref_miss, rep
         assert torch.equal(out, ref_out)
     hip.hipEventDestroy(ev)
+
+
+def _slot_layer(g, shape, E, layer, resident):
+    import torch
+    L = g.build_layer(shape, 0, layer, g.DEV)
+    hbuf, hptrs = _host_copy(L, E)
+    S = max(len(resident), 1)
+    slot_of = torch.full((E,), -1, dtype=torch.int32, device=g.DEV)
+    storage = torch.empty(S * L.stride, dtype=torch.uint8, device=g.DEV)
+    for s_, e in enumerate(resident):
+        slot_of[e] = s_
+        storage[s_ * L.stride:(s_ + 1) * L.stride].copy_(L.routed[e * L.stride:(e + 1) * L.stride])
+    table = L.table(slot_of=slot_of, n_slots=S, routed=storage)
+    return table, hptrs, (L, hbuf, slot_of, storage)
+
+
+@pytest.mark.parametrize("T,flags,fmt", [(1, 0, synth.FMT_Q3S), (4, 1, synth.FMT_Q2SM),
+                                         (64, 0, synth.FMT_Q3S), (64, 1, synth.FMT_Q2S)])
+def test_native_host_layer_equals_the_manual_sequence(g, T, flags, fmt):
+    """moe_slot_layer_forward_host against moe_layer_forward + moe_host_miss_ffn
+    + moe_add_rows on the same inputs: the same output bits and miss count,
+    and the oracle's full layer within the bar."""
+    import torch
+    moe = g.moe
+    w = synth.WORKLOADS["tiny"]
+    D, E, k = w["d_model"], w["n_experts"], w["top_k"]
+    shape = moe.MoeShape(D, w["d_ff"], E, k, w["d_ff_shared"], fmt)
+    resident = [1, 3, 5, 7, 9, 11]
+    table, hptrs, keep = _slot_layer(g, shape, E, 2, resident)
+    logits = synth.router_logits(0, 81, T, E, min_gap=1e-3)
+    x = synth.activations_f32(0, 81, T, D) * (3.0 if flags else 1.0)
+    x_dev = g.f32_to_dev(x)
+    pool = moe.HostPool(4)
+    # the native call
+    wsb = moe.moe_slot_host_workspace_bytes(shape, T)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=g.DEV)
+    stb = moe.moe_slot_host_staging_bytes(shape, T)
+    stg = torch.empty(stb + 64, dtype=torch.uint8).pin_memory()
+    stg_addr = (stg.data_ptr() + 63) // 64 * 64
+    out = torch.empty(T * D, dtype=torch.float32, device=g.DEV)
+    nm = moe.moe_slot_layer_forward_host(shape, T, x_dev, moe.MOE_F32, flags,
+                                         g.f32_to_dev(logits), table, out, moe.MOE_F32, hptrs, ws,
+                                         wsb, stg_addr, stb, pool)
+    torch.cuda.synchronize()
+    # the manual sequence
+    run = g.LayerRun(shape, T, slots=True)
+    ref = run(table, x_dev, moe.MOE_F32, g.f32_to_dev(logits), moe.MOE_F32, flags=flags)
+    nref = int(run.miss_count.item())
+    mrec = run.miss[: 4 * nref].cpu().numpy().copy()
+    y = np.zeros((T, D), np.float32)
+    moe.moe_host_miss_ffn(shape, T, np.ascontiguousarray(x).ctypes.data, moe.MOE_F32, flags,
+                          mrec.ctypes.data, nref, hptrs, y.ctypes.data, pool)
+    moe.moe_add_rows(ref, moe.MOE_F32, g.f32_to_dev(y), T, D)
+    torch.cuda.synchronize()
+    pool.close()
+    assert nm == nref and nm > 0
+    assert torch.equal(out, ref)
+    ow = OracleWeights(0, 2, D, w["d_ff"], w["d_ff_shared"], E, fmt)
+    x64 = x.astype(np.float64)
+    if flags:
+        x64 = O.bf16_to_f64(O.rms_chain(x64))
+    full, _, _ = O.layer_forward(x64, logits, k, ow, ow.shared)
+    assert rel_l2(g.out_to_f64(out, False).reshape(T, D), full) <= RTOL_L2
+
+
+def test_native_host_layer_without_misses_and_with_a_missing_host_expert(g):
+    import torch
+    moe = g.moe
+    w = synth.WORKLOADS["tiny"]
+    T, D, E, k = 4, w["d_model"], w["n_experts"], w["top_k"]
+    shape = moe.MoeShape(D, w["d_ff"], E, k, w["d_ff_shared"], synth.FMT_Q2SM)
+    logits = g.f32_to_dev(synth.router_logits(0, 82, T, E, min_gap=1e-3))
+    x_dev = g.f32_to_dev(synth.activations_f32(0, 82, T, D))
+    wsb = moe.moe_slot_host_workspace_bytes(shape, T)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=g.DEV)
+    stb = moe.moe_slot_host_staging_bytes(shape, T)
+    stg = torch.empty(stb + 64, dtype=torch.uint8).pin_memory()
+    stg_addr = (stg.data_ptr() + 63) // 64 * 64
+    # every expert resident: no misses, the output is the plain layer
+    table, hptrs, keep = _slot_layer(g, shape, E, 3, list(range(E)))
+    out = torch.empty(T * D, dtype=torch.float32, device=g.DEV)
+    nm = moe.moe_slot_layer_forward_host(shape, T, x_dev, moe.MOE_F32, 0, logits, table, out,
+                                         moe.MOE_F32, hptrs, ws, wsb, stg_addr, stb)
+    torch.cuda.synchronize()
+    plain = g.LayerRun(shape, T)(keep[0].table(), x_dev, moe.MOE_F32, logits, moe.MOE_F32)
+    assert nm == 0 and torch.equal(out, plain)
+    # nothing resident and no host copies: refused, the output stays the partial
+    table2, hptrs2, keep2 = _slot_layer(g, shape, E, 3, [])
+    hptrs2 = [0] * E
+    out2 = torch.empty(T * D, dtype=torch.float32, device=g.DEV)
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_slot_layer_forward_host(shape, T, x_dev, moe.MOE_F32, 0, logits, table2, out2,
+                                        moe.MOE_F32, hptrs2, ws, wsb, stg_addr, stb)
+    assert ei.value.status == moe.MOE_EINVAL
+    torch.cuda.synchronize()
+    run = g.LayerRun(shape, T, slots=True)
+    partial = run(table2, x_dev, moe.MOE_F32, logits, moe.MOE_F32)
+    assert torch.equal(out2, partial)
