@@ -504,7 +504,14 @@ struct GuLds {
 
 // Gate/up work item vb (the block index of decode_gateup_kernel).  Returns
 // early, with the same decision in every wave, when its list entry is unused.
-template <int T, int FMT, int XM, bool PLANNED>
+// OPW > 0: every wave has exactly OPW octets (d_model = 512 OPW), so its
+// record loads are unconditional.  With conditional loads (OPW = 0, any
+// d_model) the compiler cannot count the loads issued after the
+// activations, and its wait before staging them drains every record: the
+// GEMV then starts only once the last record has landed.  With a fixed
+// count the staging waits for the activations alone and each octet's GEMV
+// waits for its own record.
+template <int T, int FMT, int XM, bool PLANNED, int OPW>
 __device__ __forceinline__ void gateup_body(const DecodeArgs& a, const DecodeWs& w, int vb,
                                             GuLds& L, uint4* s_dyn) {
   RouteLds& R = L.R;
@@ -598,12 +605,14 @@ __device__ __forceinline__ void gateup_body(const DecodeArgs& a, const DecodeWs&
   const int mat = wv >> 1, kh = wv & 1;
   const int n = lane & 15, q = lane >> 4;
   const uint8_t* tile = eb + (size_t)(g * 2 + mat) * oD * rec_bytes(FMT);
-  uint4 cw[kMaxOctPerWave], pa[kMaxOctPerWave], pb[kMaxOctPerWave];
-  uint2 hw[kMaxOctPerWave];
+  constexpr int NOCT = OPW > 0 ? OPW : kMaxOctPerWave;
+  uint4 cw[NOCT], pa[NOCT], pb[NOCT];
+  uint2 hw[NOCT];
 #pragma unroll
-  for (int i = 0; i < kMaxOctPerWave; ++i) {
+  for (int i = 0; i < NOCT; ++i) {
     const int o = kh + 2 * i;
-    if (o < oD) load_record<FMT>(tile + (size_t)o * rec_bytes(FMT), lane, cw[i], hw[i], pa[i], pb[i]);
+    if (OPW > 0 || o < oD)
+      load_record<FMT>(tile + (size_t)o * rec_bytes(FMT), lane, cw[i], hw[i], pa[i], pb[i]);
   }
   // 3. The expert's down records for the down blocks of this XCD, last, so
   // that no wait for the loads above covers them.
@@ -728,9 +737,9 @@ __device__ __forceinline__ void gateup_body(const DecodeArgs& a, const DecodeWs&
   for (int t = 0; t < T; ++t) acc[t] = mt[t] = 0.f;
   const int xrow = (n < T ? n : 0) * D8p + q;  // this lane's A-operand row
 #pragma unroll
-  for (int i = 0; i < kMaxOctPerWave; ++i) {
+  for (int i = 0; i < NOCT; ++i) {
     const int o = kh + 2 * i;
-    if (o < oD) {
+    if (OPW > 0 || o < oD) {
       auto xfrag = [&](int beta, bool lo) -> uint4 {
         const int idx = xrow + 4 * (8 * o + beta);
         return lo ? s_xlo[idx] : s_xhi[idx];
@@ -888,11 +897,11 @@ __global__ __launch_bounds__(kGuThreads) void decode_plan_kernel(PlanArgs p) {
   if (wv == 0) build_list<T>(a, w, R, s_first, lane, true, p.has_shared[l]);
 }
 
-template <int T, int FMT, int XM, bool PLANNED>
+template <int T, int FMT, int XM, bool PLANNED, int OPW>
 __global__ __launch_bounds__(kGuThreads, 2) void decode_gateup_kernel(DecodeArgs a, DecodeWs w) {
   extern __shared__ uint4 s_dyn[];
   __shared__ GuLds L;
-  gateup_body<T, FMT, XM, PLANNED>(a, w, (int)blockIdx.x, L, s_dyn);
+  gateup_body<T, FMT, XM, PLANNED, OPW>(a, w, (int)blockIdx.x, L, s_dyn);
 }
 
 
@@ -1032,15 +1041,28 @@ __global__ __launch_bounds__(1024) void decode_down_kernel(DecodeArgs a, DecodeW
 
 template <int T, int FMT, int XM>
 static hipError_t launch_decode_x(const DecodeArgs& a, const DecodeWs& w, hipStream_t st) {
-  static std::atomic<size_t> lds_gu[kMaxDevices], lds_gp[kMaxDevices], lds_dn[kMaxDevices];
+  static std::atomic<size_t> lds_gu[2][kMaxDevices], lds_gp[2][kMaxDevices], lds_dn[kMaxDevices];
   const int D8 = a.D / 8, nbD = a.D / 32;
   const int D8p = D8 + (T > 1 ? 1 : 0);  // padded token rows (see gateup_body)
   const size_t lds = (size_t)T * D8p * 16 * (XM == kXF32 ? 2 : 1) + (size_t)T * nbD * 8;
   const size_t lds_down =
       (size_t)kDnWaves * ((size_t)T * 2 * (w.Fp / 8) + (size_t)T * (w.Fp / 32) / 2) * 16;
   hipError_t e;
-  if ((e = allow_lds(decode_gateup_kernel<T, FMT, XM, false>, lds, lds_gu)) != hipSuccess) return e;
-  if ((e = allow_lds(decode_gateup_kernel<T, FMT, XM, true>, lds, lds_gp)) != hipSuccess) return e;
+  // One token with d_model 3072 (the pages' model): six octets per wave, a
+  // fixed count.  The fixed-count form holds more registers (186 instead of
+  // 163 for Q2SM: two waves per SIMD, which still fit every block of a
+  // one-token layer at once); with 2..4 tokens it would spill or need a
+  // second round of blocks, so those keep the counted form.
+  constexpr int kOpw = T == 1 ? 6 : 0;
+  const bool six = kOpw > 0 && a.D == 3072;
+  auto gu_kernel = [&](bool planned) {
+    return planned ? (six ? decode_gateup_kernel<T, FMT, XM, true, kOpw>
+                          : decode_gateup_kernel<T, FMT, XM, true, 0>)
+                   : (six ? decode_gateup_kernel<T, FMT, XM, false, kOpw>
+                          : decode_gateup_kernel<T, FMT, XM, false, 0>);
+  };
+  if ((e = allow_lds(gu_kernel(false), lds, lds_gu[six])) != hipSuccess) return e;
+  if ((e = allow_lds(gu_kernel(true), lds, lds_gp[six])) != hipSuccess) return e;
   if ((e = allow_lds(decode_down_kernel<T, FMT>, lds_down, lds_dn)) != hipSuccess) return e;
   const int nblk = (a.shared ? a.Fs / 16 : 0) + (w.Wmax - 1) * (a.F / 16);
   // The caller's route event (moe_set_route_event), recorded as soon as the
@@ -1057,9 +1079,8 @@ static hipError_t launch_decode_x(const DecodeArgs& a, const DecodeWs& w, hipStr
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = route_done()) != hipSuccess) return e;
   }
-  if ((e = launch_timed(a.planned ? decode_gateup_kernel<T, FMT, XM, true>
-                                  : decode_gateup_kernel<T, FMT, XM, false>,
-                        dim3(nblk), dim3(kGuThreads), (uint32_t)lds, st, a, w)) != hipSuccess)
+  if ((e = launch_timed(gu_kernel(a.planned != 0), dim3(nblk), dim3(kGuThreads), (uint32_t)lds, st,
+                        a, w)) != hipSuccess)
     return e;
   if constexpr (T == 1) {
     if ((e = route_done()) != hipSuccess) return e;
