@@ -316,6 +316,7 @@ moe_status layer_forward_impl(const moe_shape* shape, int32_t tokens, const void
   a.out_bf16 = out_dtype == MOE_BF16;
   a.router = (const uint16_t*)table->router;
   a.slot_of = slots ? table->slot_of : nullptr;
+  a.n_slots = slots ? table->n_slots : 0;
   a.miss = slots ? (moe::MissRec*)miss : nullptr;
   a.miss_count = slots ? miss_count : nullptr;
   a.use_count = slots ? table->use_count : nullptr;

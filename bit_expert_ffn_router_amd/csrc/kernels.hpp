@@ -230,6 +230,7 @@ struct PrefillArgs {
   // or not resident (-1); non-resident pairs go to `miss` in (token, rank)
   // order with their number in *miss_count; use_count[e] += routed pairs
   const int32_t* slot_of;
+  int n_slots;
   MissRec* miss;
   int32_t* miss_count;
   uint32_t* use_count;

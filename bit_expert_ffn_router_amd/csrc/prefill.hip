@@ -181,7 +181,7 @@ __global__ __launch_bounds__(1024) void pf_tiles_kernel(const int32_t* __restric
 // does not depend on their order).
 __global__ __launch_bounds__(256) void pf_slot_split_kernel(const int32_t* __restrict__ idx, int P,
                                                             int E, const int32_t* __restrict__ slot_of,
-                                                            int32_t* __restrict__ grp,
+                                                            int n_slots, int32_t* __restrict__ grp,
                                                             uint32_t* __restrict__ use_count) {
   extern __shared__ uint32_t s_use[];
   const int tid = threadIdx.x;
@@ -192,7 +192,8 @@ __global__ __launch_bounds__(256) void pf_slot_split_kernel(const int32_t* __res
   const int p0 = blockIdx.x * 4096;
   for (int p = p0 + tid; p < P && p < p0 + 4096; p += 256) {
     const int e = idx[p];
-    grp[p] = slot_of[e] >= 0 ? e : E;
+    const int sl = slot_of[e];  // a slot outside 0..n_slots-1 counts as not resident
+    grp[p] = sl >= 0 && sl < n_slots ? e : E;
     if (use_count) atomicAdd(&s_use[e], 1u);
   }
   if (use_count) {
@@ -753,7 +754,7 @@ hipError_t launch_prefill(const PrefillArgs& pa, void* ws, hipStream_t st) {
     // group E collects the misses; the tiles cover groups 0..E-1 only
     const int P = T * k;
     pf_slot_split_kernel<<<(P + 4095) / 4096, 256, pa.use_count ? E * sizeof(uint32_t) : 0, st>>>(
-        w.idx, P, E, pa.slot_of, w.grp, pa.use_count);
+        w.idx, P, E, pa.slot_of, pa.n_slots, w.grp, pa.use_count);
     if ((e = launch_permute(w.grp, T, k, E + 1, w.offsets, w.sorted, w.inv, w.perm, st)) !=
         hipSuccess)
       return e;

@@ -154,3 +154,27 @@ def test_q3s_slot_prefill_8192_tokens(g):
     print("Q3S slot prefill 8192: sampled rel_l2=%.3g, hit rate %.3f"
           % (err, 1 - len(run.misses()) / (T * k)))
     assert err <= RTOL_L2
+
+
+@pytest.mark.parametrize("T", [3, 131])
+def test_slot_past_n_slots_counts_as_miss(g, T):
+    """A table entry at or past n_slots names no slot: both the few-token
+    path (T=3) and prefill (T=131) take that expert as not resident and never
+    read slot storage for it."""
+    shape, L, ow = _tiny(g, synth.FMT_Q2SM)
+    D, E, k = shape.d_model, shape.n_experts, shape.top_k
+    table, keep = _slot_table(g, L, E, list(range(0, E, 2)), n_slots=8)
+    keep[0][1] = 8            # one past the last slot
+    keep[0][3] = 1 << 30      # far past it
+    logits = synth.router_logits(0, 28, T, E, min_gap=1e-3)
+    xb = synth.activations_bf16(0, 28, T, D)
+    run = g.LayerRun(shape, T, slots=True)
+    out = run(table, g.u16_to_dev(xb), g.moe.MOE_BF16, g.f32_to_dev(logits), g.moe.MOE_F32)
+    got = g.out_to_f64(out, False).reshape(T, D)
+    slot_host = keep[0].cpu().numpy().copy()
+    slot_host[slot_host >= 8] = -1
+    ref, misses, idx, gate = O.slot_layer_forward(O.bf16_to_f64(xb), logits, k, ow, ow.shared,
+                                                  slot_host)
+    assert any(int(e) in (1, 3) for e in idx.ravel()), "no pair routed to a bad entry"
+    assert rel_l2(got, ref) <= RTOL_L2
+    _check_misses(run.misses(), idx, gate, slot_host)
