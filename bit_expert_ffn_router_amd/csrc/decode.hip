@@ -558,9 +558,12 @@ __device__ __forceinline__ void gateup_body(const DecodeArgs& a, const DecodeWs&
           __ballot(((hits >> lane) & 1ull) && __popcll(hits & below) == ui);
       ref = __builtin_amdgcn_readlane(rl, __builtin_ctzll(pick));
     } else {  // the list was built by decode_list_kernel or decode_plan_kernel
+      // The entry (has_sh + ui < Wmax for every block of the grid) is read
+      // together with the count, not after it: one round trip instead of two.
       const int nu = *w.nwork;
-      if (has_sh + ui >= nu) return;
       ref = w.work_ref[has_sh + ui];
+      asm volatile("" ::"v"(ref));  // keeps the load ahead of the branch
+      if (has_sh + ui >= nu) return;
     }
     u = has_sh + ui;
     eb = a.routed + (size_t)ref * a.stride;
@@ -948,13 +951,13 @@ __global__ __launch_bounds__(1024) void decode_down_kernel(DecodeArgs a, DecodeW
     sv = lane < nsum ? v : make_uint4(0, 0, 0, 0);
   };
 
+  // The count and this wave's first entry are read together (the entry
+  // index clamped into the list's capacity), not one after the other.
   const int nwork = *w.nwork;
-  int ref = 0;
-  float4 gt = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (wv < nwork) {
-    ref = w.work_ref[wv];
-    gt = reinterpret_cast<const float4*>(w.work_gate)[wv];
-  }
+  const int u0 = wv < w.Wmax ? wv : w.Wmax - 1;
+  int ref = w.work_ref[u0];
+  float4 gt = reinterpret_cast<const float4*>(w.work_gate)[u0];
+  asm volatile("" ::"v"(ref));  // keeps the loads ahead of the branches on nwork
   float oacc[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) oacc[t] = 0.f;
