@@ -41,10 +41,15 @@ namespace moe {
 
 namespace {
 
-constexpr int kGuWaves = 4;        // gate/up block: {gate, up} x 2 K halves, 16 FFN rows
+constexpr int kGuWaves = 4;        // routing blocks (list and plan kernels): 4 waves
 constexpr int kGuThreads = 64 * kGuWaves;
+// Gate/up block: 16 FFN rows; the reduction over d_model of each matrix
+// (gate, up) is split kGuSplit ways, one wave each.
+constexpr int kGuSplit = 4;
+constexpr int kGuBlkWaves = 2 * kGuSplit;
+constexpr int kGuBlkThreads = 64 * kGuBlkWaves;
 constexpr int kDnWaves = 16;       // down block: waves share the expert list
-constexpr int kMaxOctPerWave = 8;  // d_model <= 4096 on the decode path (16 octets / 2 halves)
+constexpr int kMaxOctPerWave = 16 / kGuSplit;  // d_model <= 4096 on the decode path (16 octets)
 constexpr int kMaxDecodeFOct = 2;  // d_ff, d_ff_shared <= 512 on the decode path
 // Down-record prefetch loads per gate/up thread (one 64-byte line each):
 // 32 KiB per block, a block's whole share up to d_model 4096 in every
@@ -488,18 +493,23 @@ __device__ __forceinline__ void keep_alive(const DnPrefetch& p) {
 
 // ----------------------------------------------------------------------------
 // decode_gateup.  Grid: d_ff_shared/16 shared-expert blocks, then
-// (routed list capacity x d_ff/16) blocks, of 256 threads, two blocks per
+// (routed list capacity x d_ff/16) blocks, of 512 threads, two blocks per
 // CU.  A routed block first routes (see above) and drops out when its list
 // entry is not used.  Then every block issues its weight loads -- wave w
-// holds matrix w/2 (gate, up) over the K octets o = w%2, w%2 + 2, ... of one
-// 16-row h-group -- and, while they are in flight, the activation loads, the
-// input rule, the bf16 operand(s) in LDS and the per-32-block activation sums.
+// holds matrix w / kGuSplit (gate, up) over the K octets o = w % kGuSplit,
+// + kGuSplit, ... of one 16-row h-group -- and, while they are in flight,
+// the activation loads, the input rule, the bf16 operand(s) in LDS and the
+// per-32-block activation sums.  Splitting each matrix's reduction four ways
+// rather than two halves the GEMV work of a wave (at d_model 3072, 3 octets
+// instead of 6: the dequantising GEMV of one wave costs a few microseconds
+// of issue at one or two waves per SIMD) and doubles the waves that can
+// hide one another's waits.
 // Static LDS of a gate/up block.
 struct GuLds {
   RouteLds R;
-  TopkScratch topk[kGuWaves];
-  float red[kGuWaves][kDecodeMaxT][16];
-  float ss[kGuWaves][kDecodeMaxT];
+  TopkScratch topk[kGuBlkWaves];
+  float red[kGuBlkWaves][kDecodeMaxT][16];
+  float ss[kGuBlkWaves][kDecodeMaxT];
 };
 
 // Gate/up work item vb (the block index of decode_gateup_kernel).  Returns
@@ -575,11 +585,11 @@ __device__ __forceinline__ void gateup_body(const DecodeArgs& a, const DecodeWs&
   constexpr bool in_bf16 = XM == kXBf16 || XM == kXRms;
   constexpr bool RMS = XM == kXRms || XM == kXRmsF32;
   const int nin = in_bf16 ? T * D8 : 2 * T * D8;
-  constexpr int XJ = (in_bf16 ? 2 : 4) * T;  // pieces per thread, D <= 4096
+  constexpr int XJ = (in_bf16 ? 1 : 2) * T * 512 / kGuBlkThreads;  // pieces per thread, D <= 4096
   uint4 xr[XJ];
 #pragma unroll
   for (int j = 0; j < XJ; ++j) {
-    const int i = tid + kGuThreads * j;
+    const int i = tid + kGuBlkThreads * j;
     const uint4 v = reinterpret_cast<const uint4*>(a.x)[i < nin ? i : 0];
     xr[j] = i < nin ? v : make_uint4(0, 0, 0, 0);
   }
@@ -605,7 +615,7 @@ __device__ __forceinline__ void gateup_body(const DecodeArgs& a, const DecodeWs&
   }
 
   // 2. Weight loads of this wave.
-  const int mat = wv >> 1, kh = wv & 1;
+  const int mat = wv / kGuSplit, kh = wv % kGuSplit;
   const int n = lane & 15, q = lane >> 4;
   const uint8_t* tile = eb + (size_t)(g * 2 + mat) * oD * rec_bytes(FMT);
   constexpr int NOCT = OPW > 0 ? OPW : kMaxOctPerWave;
@@ -613,7 +623,7 @@ __device__ __forceinline__ void gateup_body(const DecodeArgs& a, const DecodeWs&
   uint2 hw[NOCT];
 #pragma unroll
   for (int i = 0; i < NOCT; ++i) {
-    const int o = kh + 2 * i;
+    const int o = kh + kGuSplit * i;
     if (OPW > 0 || o < oD)
       load_record<FMT>(tile + (size_t)o * rec_bytes(FMT), lane, cw[i], hw[i], pa[i], pb[i]);
   }
@@ -622,7 +632,7 @@ __device__ __forceinline__ void gateup_body(const DecodeArgs& a, const DecodeWs&
   const int Fu_pf = vb < nsh ? a.Fs : a.F;
   const DnPrefetch dpf = prefetch_down_rows(eb, D, Fu_pf, rec_bytes(FMT),
                                             down_offset(D, Fu_pf, FMT), vb, vb - g, Fu_pf / 16,
-                                            tid, kGuThreads);
+                                            tid, kGuBlkThreads);
   // The RMS factors of the input: in-block with one token; from the
   // previous layer's partials in a planned call with 2..4 tokens; from
   // decode_list_kernel otherwise.
@@ -637,7 +647,7 @@ __device__ __forceinline__ void gateup_body(const DecodeArgs& a, const DecodeWs&
     for (int t = 0; t < T; ++t) ss[t] = 0.f;
 #pragma unroll
     for (int j = 0; j < XJ; ++j) {
-      const int i = tid + kGuThreads * j;
+      const int i = tid + kGuBlkThreads * j;
       const int t = in_bf16 ? i / D8 : i / (2 * D8);
       const uint32_t qq[4] = {xr[j].x, xr[j].y, xr[j].z, xr[j].w};
       float q2 = 0.f;
@@ -661,7 +671,7 @@ __device__ __forceinline__ void gateup_body(const DecodeArgs& a, const DecodeWs&
     for (int t = 0; t < T; ++t) {
       float ssum = 0.f;
 #pragma unroll
-      for (int w2 = 0; w2 < kGuWaves; ++w2) ssum += s_ss[w2][t];
+      for (int w2 = 0; w2 < kGuBlkWaves; ++w2) ssum += s_ss[w2][t];
       rinv[t] = 1.0f / sqrtf(ssum / (float)D + 1e-6f);
     }
   }
@@ -669,7 +679,7 @@ __device__ __forceinline__ void gateup_body(const DecodeArgs& a, const DecodeWs&
   // operand values (lanes holding the pieces of one block combine by DPP).
 #pragma unroll
   for (int j = 0; j < XJ; ++j) {
-    const int i = tid + kGuThreads * j;
+    const int i = tid + kGuBlkThreads * j;
     const bool ok = i < nin;
     float X = 0.f, Xc = 0.f;
     if (in_bf16) {  // piece i = bf16 elements 8(i % D8) .. +7 of token i / D8
@@ -741,7 +751,7 @@ __device__ __forceinline__ void gateup_body(const DecodeArgs& a, const DecodeWs&
   const int xrow = (n < T ? n : 0) * D8p + q;  // this lane's A-operand row
 #pragma unroll
   for (int i = 0; i < NOCT; ++i) {
-    const int o = kh + 2 * i;
+    const int o = kh + kGuSplit * i;
     if (OPW > 0 || o < oD) {
       auto xfrag = [&](int beta, bool lo) -> uint4 {
         const int idx = xrow + 4 * (8 * o + beta);
@@ -765,8 +775,12 @@ __device__ __forceinline__ void gateup_body(const DecodeArgs& a, const DecodeWs&
   // 5. SwiGLU over 16 FFN rows x T tokens; h in bf16 hi + lo; half-block sums.
   if (tid < 16 * T) {
     const int t = tid >> 4, nn = tid & 15;
-    const float ga = s_red[0][t][nn] + s_red[1][t][nn];
-    const float ub = s_red[2][t][nn] + s_red[3][t][nn];
+    float ga = s_red[0][t][nn], ub = s_red[kGuSplit][t][nn];
+#pragma unroll
+    for (int j = 1; j < kGuSplit; ++j) {
+      ga += s_red[j][t][nn];
+      ub += s_red[kGuSplit + j][t][nn];
+    }
     const float h = silu(ga) * ub;
     const uint16_t hi = f32_to_bf16(h);
     const uint16_t lo = f32_to_bf16(h - bf16_to_f32(hi));
@@ -901,7 +915,7 @@ __global__ __launch_bounds__(kGuThreads) void decode_plan_kernel(PlanArgs p) {
 }
 
 template <int T, int FMT, int XM, bool PLANNED, int OPW>
-__global__ __launch_bounds__(kGuThreads, 2) void decode_gateup_kernel(DecodeArgs a, DecodeWs w) {
+__global__ __launch_bounds__(kGuBlkThreads, 2) void decode_gateup_kernel(DecodeArgs a, DecodeWs w) {
   extern __shared__ uint4 s_dyn[];
   __shared__ GuLds L;
   gateup_body<T, FMT, XM, PLANNED, OPW>(a, w, (int)blockIdx.x, L, s_dyn);
@@ -1051,12 +1065,12 @@ static hipError_t launch_decode_x(const DecodeArgs& a, const DecodeWs& w, hipStr
   const size_t lds_down =
       (size_t)kDnWaves * ((size_t)T * 2 * (w.Fp / 8) + (size_t)T * (w.Fp / 32) / 2) * 16;
   hipError_t e;
-  // One token with d_model 3072 (the pages' model): six octets per wave, a
-  // fixed count.  The fixed-count form holds more registers (186 instead of
-  // 163 for Q2SM: two waves per SIMD, which still fit every block of a
-  // one-token layer at once); with 2..4 tokens it would spill or need a
-  // second round of blocks, so those keep the counted form.
-  constexpr int kOpw = T == 1 ? 6 : 0;
+  // One token with d_model 3072 (the pages' model): a fixed count of
+  // 12 / kGuSplit octets per wave, so the record loads are unconditional
+  // (see gateup_body); 105 VGPRs for Q2SM, two blocks per CU.  With 2..4
+  // tokens the same form takes 164 (one block per CU, so a 4-token layer's
+  // blocks would run in three rounds), so those keep the generic form.
+  constexpr int kOpw = T == 1 ? 12 / kGuSplit : 0;
   const bool six = kOpw > 0 && a.D == 3072;
   auto gu_kernel = [&](bool planned) {
     return planned ? (six ? decode_gateup_kernel<T, FMT, XM, true, kOpw>
@@ -1082,7 +1096,7 @@ static hipError_t launch_decode_x(const DecodeArgs& a, const DecodeWs& w, hipStr
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = route_done()) != hipSuccess) return e;
   }
-  if ((e = launch_timed(gu_kernel(a.planned != 0), dim3(nblk), dim3(kGuThreads), (uint32_t)lds, st,
+  if ((e = launch_timed(gu_kernel(a.planned != 0), dim3(nblk), dim3(kGuBlkThreads), (uint32_t)lds, st,
                         a, w)) != hipSuccess)
     return e;
   if constexpr (T == 1) {
