@@ -681,9 +681,14 @@ __global__ __launch_bounds__(kPfThreads, 1) void pf_gemm_kernel(PfArgs a, int nN
 // ----------------------------------------------------------------------------
 // out_t = sum_j g_tj * Y[inv[t*k + j]] + Y[P + t], in a fixed order.  One
 // block per token: the token's rows and gates go to LDS first, then each
-// thread has all of its 16-byte pieces of those rows in flight together (up
-// to 16 at a time) before it sums them in order j = 0..k-1.  With a slot
-// table the sum runs over the resident pairs only (the partial layer).
+// thread has its 16-byte pieces of KJ rows in flight together before it sums
+// them in order j = 0..k-1.  With a slot table the sum runs over the resident
+// pairs only (the partial layer).  Every one of the KJ loads is issued: a
+// slot past k or a non-resident pair reads a row that is there anyway (the
+// shared expert's, else row 0) and is left out of the sum by a select.  As
+// guarded loads, each sat in a branch of its own behind a wait for the one
+// before it, so a token's k rows came in one round trip after another.
+template <int KJ>
 __global__ __launch_bounds__(512) void pf_combine_kernel(PfArgs a, int has_shared) {
   __shared__ int32_t s_row[kMaxTopK];
   __shared__ float s_g[kMaxTopK];
@@ -703,20 +708,33 @@ __global__ __launch_bounds__(512) void pf_combine_kernel(PfArgs a, int has_share
       o[2 * i + 1] += g * bf16_hi(yy[i]);
     }
   };
+  auto add_if = [](float (&o)[8], const uint4& y, float g, bool on) __attribute__((always_inline)) {
+    const uint32_t yy[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float lo = o[2 * i] + g * bf16_lo(yy[i]), hi = o[2 * i + 1] + g * bf16_hi(yy[i]);
+      o[2 * i] = on ? lo : o[2 * i];
+      o[2 * i + 1] = on ? hi : o[2 * i + 1];
+    }
+  };
+  const size_t fallback = has_shared ? (size_t)(P + t) : 0;
   for (int c = tid; c < D / 8; c += blockDim.x) {
     float o[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) o[i] = 0.f;
-    const uint4 ys = reinterpret_cast<const uint4*>(a.w.Y + (size_t)(P + t) * D)[has_shared ? c : 0];
-    for (int j0 = 0; j0 < k; j0 += 16) {
-      uint4 y[16];
+    const uint4 ys = reinterpret_cast<const uint4*>(a.w.Y + fallback * D)[c];
+    for (int j0 = 0; j0 < k; j0 += KJ) {
+      uint4 y[KJ];
+      bool on[KJ];
 #pragma unroll
-      for (int jj = 0; jj < 16; ++jj)
-        if (j0 + jj < k && s_row[j0 + jj] >= 0)
-          y[jj] = reinterpret_cast<const uint4*>(a.w.Y + (size_t)s_row[j0 + jj] * D)[c];
+      for (int jj = 0; jj < KJ; ++jj) {
+        const int j = j0 + jj;  // < kMaxTopK: the host picks KJ with j0 + KJ <= 32
+        on[jj] = j < k && s_row[j] >= 0;
+        const size_t r = on[jj] ? (size_t)s_row[j] : fallback;
+        y[jj] = reinterpret_cast<const uint4*>(a.w.Y + r * D)[c];
+      }
 #pragma unroll
-      for (int jj = 0; jj < 16; ++jj)
-        if (j0 + jj < k && s_row[j0 + jj] >= 0) add(o, y[jj], s_g[j0 + jj]);
+      for (int jj = 0; jj < KJ; ++jj) add_if(o, y[jj], s_g[j0 + jj], on[jj]);
     }
     if (has_shared) add(o, ys, 1.f);
     if (a.out_bf16) {
@@ -811,7 +829,16 @@ hipError_t launch_prefill(const PrefillArgs& pa, void* ws, hipStream_t st) {
   // One thread per 16-byte piece of a row (384 for d_model 3072), at least
   // one wave, at most 512 threads.
   const int cthreads = std::min(512, std::max(64, (D / 8 + 63) / 64 * 64));
-  pf_combine_kernel<<<T, cthreads, 0, st>>>(a, has_sh);
+  // rows in flight per pass: the fewest of 4, 8, 12, 16 that cover k in
+  // whole passes with the least slack (k = 10: 12)
+  if (k <= 4)
+    pf_combine_kernel<4><<<T, cthreads, 0, st>>>(a, has_sh);
+  else if (k <= 8)
+    pf_combine_kernel<8><<<T, cthreads, 0, st>>>(a, has_sh);
+  else if (k <= 12)
+    pf_combine_kernel<12><<<T, cthreads, 0, st>>>(a, has_sh);
+  else
+    pf_combine_kernel<16><<<T, cthreads, 0, st>>>(a, has_sh);
   return hipGetLastError();
 }
 
