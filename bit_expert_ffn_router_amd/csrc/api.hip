@@ -6,6 +6,8 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
+#include <chrono>
 #include <vector>
 
 #include "../../include/moe.h"
@@ -78,6 +80,10 @@ KernelTimer& router_timer() {
 KernelTimer& route_event() {
   thread_local KernelTimer t;
   return t;
+}
+HostPub& host_pub() {
+  thread_local HostPub p = {};
+  return p;
 }
 
 }  // namespace moe
@@ -288,6 +294,10 @@ moe_status layer_forward_impl(const moe_shape* shape, int32_t tokens, const void
     a.miss = (moe::MissRec*)miss;
     a.miss_count = miss_count;
     a.use_count = slots ? table->use_count : nullptr;
+    if (slots) {  // an armed copy of the routing outcome to the host (taken once)
+      a.pub = moe::host_pub();
+      moe::host_pub() = {};
+    }
     const moe::DecodeWs w = moe::decode_ws_carve(ws, T, a.D, a.F, a.Fs, a.E, a.k);
     if (table->router) {
       moe::RouterArgs r{T, a.D, a.E, x, a.x_bf16, a.rmsnorm, (const uint16_t*)table->router,
@@ -698,15 +708,18 @@ SlotHostWs slot_host_ws(const moe_shape* s, int T) {
   return {fws, fws + miss, fws + miss + a256((size_t)T * s->d_model * 4)};
 }
 // Pinned host staging: miss records + count, the layer input (fp32-sized),
-// the host rows.
+// the host rows, and (on a 128-byte line of its own) the flag the decode
+// kernel raises once it has written the first two.
 struct SlotHostStaging {
-  size_t x, y, total;
+  size_t x, y, flag, total;
 };
 SlotHostStaging slot_host_staging(const moe_shape* s, int T) {
   auto a64 = [](size_t n) { return (n + 63) / 64 * 64; };
+  auto a128 = [](size_t n) { return (n + 127) / 128 * 128; };
   const size_t m = a64((size_t)T * s->top_k * sizeof(moe_miss) + 4);
   const size_t row = a64((size_t)T * s->d_model * 4);
-  return {m, m + row, m + 2 * row};
+  const size_t flag = a128(m + 2 * row);
+  return {m, m + row, flag, flag + 128};
 }
 
 }  // namespace
@@ -751,9 +764,11 @@ moe_status moe_slot_layer_forward_host(const moe_shape* shape, int32_t tokens, c
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
   if (hipStreamIsCapturing(st, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone)
     return fail(MOE_EUNSUPPORTED, "moe_slot_layer_forward_host waits on the host: not for capture");
-  SideStream* side = nullptr;
-  s = hip_status(side_stream(side), "side stream");
-  if (s != MOE_OK) return s;
+  void* stg_dev = nullptr;
+  if (hipHostGetDevicePointer(&stg_dev, staging, 0) != hipSuccess || !stg_dev) {
+    (void)hipGetLastError();
+    return fail(MOE_EINVAL, "staging must be page-locked host memory the device can address (hipHostMalloc)");
+  }
   const int k = shape->top_k, D = shape->d_model;
   const size_t mbytes = (size_t)T * k * sizeof(moe_miss);
   uint8_t* wsb = (uint8_t*)ws;
@@ -761,22 +776,54 @@ moe_status moe_slot_layer_forward_host(const moe_shape* shape, int32_t tokens, c
   moe_miss* miss_d = (moe_miss*)(wsb + L.miss);
   int32_t* cnt_d = (int32_t*)(wsb + L.miss + mbytes);
   float* y_d = (float*)(wsb + L.y);
-  // 1. The layer on the stream; its routing records the side event.
-  moe::route_event().before = side->ev;
-  s = layer_forward_impl(shape, T, x, x_dtype, flags, router_logits, table, out, out_dtype, miss_d,
-                         T * k, cnt_d, ws, L.miss, false, stream);
-  const bool recorded = moe::route_event().before == nullptr;
-  moe::route_event().before = nullptr;
-  if (s != MOE_OK) return s;
-  if (!recorded) return fail(MOE_EHIP, "the layer did not record its routing event");
-  // 2. Miss list, count and input to the host once the routing is written.
   hipError_t e;
-  if ((e = hipStreamWaitEvent(side->s, side->ev, 0)) != hipSuccess ||
-      (e = hipMemcpyAsync(stg, miss_d, mbytes + 4, hipMemcpyDeviceToHost, side->s)) != hipSuccess ||
-      (e = hipMemcpyAsync(stg + S.x, x, (size_t)T * D * (x_dtype == MOE_BF16 ? 2 : 4),
-                          hipMemcpyDeviceToHost, side->s)) != hipSuccess ||
-      (e = hipStreamSynchronize(side->s)) != hipSuccess)
-    return hip_status(e, "miss list copy");
+  if (use_decode_path(T)) {
+    // 1-2. The layer on the stream; the kernel that publishes its routing
+    // also writes the miss list, its count and the input into the staging
+    // and then raises the flag (no event, copy or synchronisation calls,
+    // which cost the host tens of microseconds per layer).
+    static std::atomic<uint32_t> g_seq{0};
+    uint32_t seq = ++g_seq;
+    if (seq == 0) seq = ++g_seq;
+    volatile uint32_t* flag = reinterpret_cast<volatile uint32_t*>(stg + S.flag);
+    *flag = 0u;
+    uint8_t* dv = (uint8_t*)stg_dev;
+    moe::host_pub() = {(moe::MissRec*)dv, (int32_t*)(dv + mbytes), dv + S.x,
+                       (uint32_t*)(dv + S.flag), seq};
+    s = layer_forward_impl(shape, T, x, x_dtype, flags, router_logits, table, out, out_dtype,
+                           miss_d, T * k, cnt_d, ws, L.miss, false, stream);
+    const bool armed = moe::host_pub().flag != nullptr;
+    moe::host_pub() = {};
+    if (s != MOE_OK) return s;
+    if (armed) return fail(MOE_EHIP, "the layer did not take the host copy of its routing");
+    const auto t0 = std::chrono::steady_clock::now();
+    for (uint32_t polls = 0; __atomic_load_n(flag, __ATOMIC_ACQUIRE) != seq; ++polls) {
+#if defined(__x86_64__)
+      __builtin_ia32_pause();
+#endif
+      if ((polls & 4095u) == 4095u && std::chrono::steady_clock::now() - t0 > std::chrono::seconds(10))
+        return fail(MOE_EHIP, "the layer's routing did not reach the host within 10 s");
+    }
+  } else {
+    SideStream* side = nullptr;
+    s = hip_status(side_stream(side), "side stream");
+    if (s != MOE_OK) return s;
+    // 1. The layer on the stream; its routing records the side event.
+    moe::route_event().before = side->ev;
+    s = layer_forward_impl(shape, T, x, x_dtype, flags, router_logits, table, out, out_dtype,
+                           miss_d, T * k, cnt_d, ws, L.miss, false, stream);
+    const bool recorded = moe::route_event().before == nullptr;
+    moe::route_event().before = nullptr;
+    if (s != MOE_OK) return s;
+    if (!recorded) return fail(MOE_EHIP, "the layer did not record its routing event");
+    // 2. Miss list, count and input to the host once the routing is written.
+    if ((e = hipStreamWaitEvent(side->s, side->ev, 0)) != hipSuccess ||
+        (e = hipMemcpyAsync(stg, miss_d, mbytes + 4, hipMemcpyDeviceToHost, side->s)) != hipSuccess ||
+        (e = hipMemcpyAsync(stg + S.x, x, (size_t)T * D * (x_dtype == MOE_BF16 ? 2 : 4),
+                            hipMemcpyDeviceToHost, side->s)) != hipSuccess ||
+        (e = hipStreamSynchronize(side->s)) != hipSuccess)
+      return hip_status(e, "miss list copy");
+  }
   const int32_t nm = *reinterpret_cast<const int32_t*>(stg + mbytes);
   if (n_miss) *n_miss = nm;
   if (nm == 0) return ok();

@@ -135,6 +135,22 @@ __device__ __forceinline__ int resident_ref(const DecodeArgs& a, int e) {
   return (s >= 0 && s < a.n_slots) ? s : -1;
 }
 
+// The routing outcome into the caller's page-locked staging (HostPub), by
+// the publishing wave once its miss records are written there too: the count
+// and the layer input, then -- after a system-scope release fence by every
+// lane, so that all the wave's stores are out -- the flag the host polls.
+__device__ __forceinline__ void publish_host(const DecodeArgs& a, int lane, int nmiss) {
+  const HostPub& p = a.pub;
+  if (lane == 0) *p.count = nmiss;
+  const int n16 = a.T * a.D * (a.x_bf16 ? 2 : 4) / 16;
+  const uint4* src = reinterpret_cast<const uint4*>(a.x);
+  uint4* dst = reinterpret_cast<uint4*>(p.x);
+  for (int i = lane; i < n16; i += 64) dst[i] = src[i];
+  __threadfence_system();  // the wave's stores reach host memory before the flag
+  __builtin_amdgcn_wave_barrier();
+  if (lane == 0) __hip_atomic_store(p.flag, p.seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
 // One token: lane j < k holds expert e, gate g and residency ref (-1 = miss);
 // `hits` has bit j set for resident ranks.  Hit i (in rank order) is list
 // entry base + i.  Writes the list, the routing and the miss list.
@@ -158,6 +174,7 @@ __device__ __forceinline__ void publish_t1(const DecodeArgs& a, const DecodeWs& 
       r.expert = e;
       r.gate = g;
       a.miss[__popcll(~hits & kmask & below)] = r;
+      if (a.pub.flag) a.pub.miss[__popcll(~hits & kmask & below)] = r;
     }
   }
   if (lane == 0) {
@@ -168,6 +185,7 @@ __device__ __forceinline__ void publish_t1(const DecodeArgs& a, const DecodeWs& 
     *w.nwork = base + __popcll(hits);
     if (a.miss_count) *a.miss_count = k - __popcll(hits);
   }
+  if (a.pub.flag) publish_host(a, lane, k - __popcll(hits));
 }
 
 // 2..4 tokens, wave 0, once every token's routing is in R.e / R.g.  The
@@ -249,8 +267,10 @@ __device__ __forceinline__ void build_list(const DecodeArgs& a, const DecodeWs& 
       r.expert = e[h];
       r.gate = R.g[p];
       a.miss[(h ? nm0 : 0) + __popcll(bm[h] & ((1ull << lane) - 1ull))] = r;
+      if (a.pub.flag) a.pub.miss[(h ? nm0 : 0) + __popcll(bm[h] & ((1ull << lane) - 1ull))] = r;
     }
   }
+  if (a.pub.flag) publish_host(a, lane, M);
 }
 
 // ----------------------------------------------------------------------------

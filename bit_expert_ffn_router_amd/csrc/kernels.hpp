@@ -114,6 +114,19 @@ struct DecodeWs {
   int Fp;              // padded FFN width of the h rows
 };
 
+// The routing outcome of a decode call copied into page-locked host memory
+// by the kernel that publishes it (the host half of a slot layer): the miss
+// records, their count and the layer input, then `flag` = seq, stored with a
+// system-scope release.  flag == NULL: no copy.
+struct HostPub {
+  MissRec* miss;
+  int32_t* count;
+  void* x;
+  uint32_t* flag;
+  uint32_t seq;
+};
+HostPub& host_pub();  // armed by the caller (thread-local) for its next decode call
+
 struct DecodeArgs {
   int T, D, F, Fs, E, k, fmt;
   const void* x;
@@ -139,6 +152,7 @@ struct DecodeArgs {
   // planned RMS call takes its factors.
   float* rms_out;
   const float* rms_in;
+  HostPub pub;
 };
 
 size_t decode_ws_bytes(int T, int D, int F, int Fs, int E, int k);

@@ -384,14 +384,20 @@ moe_status moe_add_rows(void* out, int32_t out_dtype, const float* y, int32_t to
  * 答案会变"; [SL] section "12GB 显存装下 1250 亿参数").
  *
  * Enqueues moe_layer_forward on `stream` (partial layer and miss list, into
- * the workspace); as soon as the routing and the miss list are written it
- * copies the list, its count and the layer input into `staging` on a side
- * stream of the calling thread, computes the missed experts' rows on the
- * host (moe_host_miss_ffn on `pool`) while the GPU still computes the
- * resident experts, then enqueues their copy to the workspace and their
- * addition into `out` (moe_add_rows) on `stream`.  The call returns once
- * the host rows are computed; `out` holds the whole layer when `stream`
- * reaches that point.  Not for stream capture (it waits on the host).
+ * the workspace); as soon as the routing and the miss list are written they
+ * reach `staging` with their count and the layer input, and the host
+ * computes the missed experts' rows (moe_host_miss_ffn on `pool`) while the
+ * GPU still computes the resident experts; then it enqueues their copy to
+ * the workspace and their addition into `out` (moe_add_rows) on `stream`.
+ * With 1..4 tokens the decode kernel that publishes the routing writes the
+ * list, the count and the input into `staging` itself and then raises a
+ * flag word there (a system-scope release), which the host polls: no event,
+ * copy or synchronisation call stands between the routing and the host
+ * rows.  With more tokens the layer records an event once its routing is
+ * written, and a side stream of the calling thread copies them.  The call
+ * returns once the host rows are computed; `out` holds the whole layer when
+ * `stream` reaches that point.  Not for stream capture (it waits on the
+ * host).
  *   shape, tokens, x (device), x_dtype, flags, router_logits, out,
  *   out_dtype: as moe_layer_forward; table->slot_of is required.
  *   host_experts: host [n_experts] pointers to every expert packed in host
@@ -400,18 +406,20 @@ moe_status moe_add_rows(void* out, int32_t out_dtype, const float* y, int32_t to
  *   n_miss:   host int32 receiving the number of misses, or NULL.
  *   ws, ws_bytes: device workspace of moe_slot_host_workspace_bytes(shape,
  *             tokens) bytes, 256-byte aligned.
- *   staging, staging_bytes: pinned host memory (hipHostMalloc) of
+ *   staging, staging_bytes: page-locked host memory the device can address
+ *             (hipHostMalloc; MOE_EINVAL otherwise) of
  *             moe_slot_host_staging_bytes(shape, tokens) bytes, 64-byte
  *             aligned.  Its host rows are read by the copy this call
  *             enqueues; a later call on the same stream overwrites them only
  *             after its own routing, which follows that copy.
  *   pool:     host worker threads, or NULL.
  * The side stream (non-blocking, default priority) and its event are
- * created on a thread's first call on a device and kept until the process
- * ends.  Errors: those of moe_layer_forward; MOE_EINVAL for a miss whose
- * host expert is NULL (then nothing is added: `out` stays the partial);
- * MOE_EUNSUPPORTED while `stream` is capturing; MOE_EHIP for a failed copy
- * or wait. */
+ * created on a thread's first call with more than 4 tokens on a device and
+ * kept until the process ends.  Errors: those of moe_layer_forward;
+ * MOE_EINVAL for a miss whose host expert is NULL (then nothing is added:
+ * `out` stays the partial) or for pageable staging; MOE_EUNSUPPORTED while
+ * `stream` is capturing; MOE_EHIP for a failed copy or wait, or a routing
+ * that has not reached the host 10 s after the launch. */
 size_t moe_slot_host_workspace_bytes(const moe_shape* shape, int32_t tokens);
 size_t moe_slot_host_staging_bytes(const moe_shape* shape, int32_t tokens);
 moe_status moe_slot_layer_forward_host(const moe_shape* shape, int32_t tokens, const void* x,

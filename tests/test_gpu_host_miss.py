@@ -293,3 +293,55 @@ def test_native_host_layer_without_misses_and_with_a_missing_host_expert(g):
     run = g.LayerRun(shape, T, slots=True)
     partial = run(table2, x_dev, moe.MOE_F32, logits, moe.MOE_F32)
     assert torch.equal(out2, partial)
+
+
+def test_native_host_layer_back_to_back_calls_and_pageable_staging(g):
+    """With 1..4 tokens the routing kernel writes the miss list and the input
+    into the staging and raises a flag the host waits for: five calls in a
+    row on one staging buffer (different inputs and routings) each give the
+    manual sequence's bits, so no call reads an earlier call's flag or list.
+    Staging in pageable memory is refused."""
+    import torch
+    moe = g.moe
+    w = synth.WORKLOADS["tiny"]
+    D, E, k = w["d_model"], w["n_experts"], w["top_k"]
+    shape = moe.MoeShape(D, w["d_ff"], E, k, w["d_ff_shared"], synth.FMT_Q2SM)
+    table, hptrs, keep = _slot_layer(g, shape, E, 2, [0, 2, 4, 6, 8, 10])
+    pool = moe.HostPool(4)
+    wsb = moe.moe_slot_host_workspace_bytes(shape, 4)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=g.DEV)
+    stb = moe.moe_slot_host_staging_bytes(shape, 4)
+    stg = torch.empty(stb + 64, dtype=torch.uint8).pin_memory()
+    stg_addr = (stg.data_ptr() + 63) // 64 * 64
+    for i, T in enumerate([1, 4, 2, 1, 3]):
+        logits = synth.router_logits(0, 90 + i, T, E, min_gap=1e-3)
+        x = synth.activations_f32(0, 90 + i, T, D)
+        x_dev = g.f32_to_dev(x)
+        out = torch.empty(T * D, dtype=torch.float32, device=g.DEV)
+        nm = moe.moe_slot_layer_forward_host(shape, T, x_dev, moe.MOE_F32, 0, g.f32_to_dev(logits),
+                                             table, out, moe.MOE_F32, hptrs, ws, wsb, stg_addr,
+                                             stb, pool)
+        torch.cuda.synchronize()
+        # the manual sequence on the same inputs
+        rl = g.LayerRun(shape, T, slots=True)
+        ref = rl(table, x_dev, moe.MOE_F32, g.f32_to_dev(logits), moe.MOE_F32)
+        nref = int(rl.miss_count.item())
+        idx, _ = O.route(logits, k)
+        assert nm == nref == int(np.isin(idx, [0, 2, 4, 6, 8, 10], invert=True).sum()), (i, T)
+        if nref:
+            y = np.zeros((T, D), np.float32)
+            mrec = rl.miss[: 4 * nref].cpu().numpy().copy()
+            moe.moe_host_miss_ffn(shape, T, np.ascontiguousarray(x).ctypes.data, moe.MOE_F32, 0,
+                                  mrec.ctypes.data, nref, hptrs, y.ctypes.data, pool)
+            moe.moe_add_rows(ref, moe.MOE_F32, g.f32_to_dev(y), T, D)
+            torch.cuda.synchronize()
+        assert torch.equal(out, ref), (i, T)
+    pageable = np.zeros(stb + 64, np.uint8)
+    p_addr = (pageable.ctypes.data + 63) // 64 * 64
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_slot_layer_forward_host(shape, 1, g.f32_to_dev(synth.activations_f32(0, 99, 1, D)),
+                                        moe.MOE_F32, 0, g.f32_to_dev(synth.router_logits(0, 99, 1, E)),
+                                        table, torch.empty(D, dtype=torch.float32, device=g.DEV),
+                                        moe.MOE_F32, hptrs, ws, wsb, p_addr, stb, pool)
+    assert ei.value.status == moe.MOE_EINVAL
+    pool.close()
