@@ -700,9 +700,10 @@ def bench_slot_host(ctx, n_tokens=16, name="slot_host_q3s_t1_8l"):
                                               alpha=w["alpha"])) for l in range(L)]
     x0 = synth.activations_bf16(0, 0, n_tokens, D)
     # One moe_slot_layer_forward_host call per layer: the library enqueues
-    # the GPU half, copies the miss list and the input as soon as the
-    # routing is written, computes the missed experts on the host pool while
-    # the GPU computes the hits, and enqueues their addition into the output.
+    # the GPU half, whose routing kernel writes the miss list and the input
+    # into the pinned staging and raises a flag there; the host computes the
+    # missed experts on the pool while the GPU computes the hits, and the
+    # library enqueues their addition into the output.
     wsb = moe.moe_slot_host_workspace_bytes(shape, 1)
     ws = torch.empty(wsb, dtype=torch.uint8, device=ctx.dev)
     stb = moe.moe_slot_host_staging_bytes(shape, 1)
