@@ -27,14 +27,16 @@
  *     CPU addresses.  The caller allocates and frees every buffer, including
  *     the workspace.  The GPU entry points allocate no device memory and
  *     keep no state between calls, except: moe_last_error's per-thread
- *     message; the per-thread event pairs of the profiling aids; and, per
+ *     message; the per-thread event pairs of the profiling aids; per
  *     device, the largest dynamic-LDS limit already set on a kernel (set
- *     once with hipFuncSetAttribute, thread-safe).  The host half of the
+ *     once with hipFuncSetAttribute, thread-safe); and the side stream and
+ *     event moe_slot_layer_forward_host keeps per thread and device.  The host half of the
  *     slot-mode layer is different: moe_host_pool_create starts threads,
  *     and moe_host_miss_ffn allocates and frees its own host scratch (the
  *     rearranged activations and the h rows) within each call.
  *   - All device work is enqueued on the caller's stream (NULL = the null
- *     stream); nothing waits on the host.  Device-resident results (outputs,
+ *     stream); nothing waits on the host, except moe_slot_layer_forward_host,
+ *     which waits for its layer's routing.  Device-resident results (outputs,
  *     miss lists, counts) are valid after the caller synchronises the stream.
  *   - Arguments are validated on the host before anything is enqueued; a
  *     rejected call returns a negative moe_status, sets moe_last_error(),
@@ -179,7 +181,9 @@ typedef struct {
  * shape->d_model (0 if the shape is invalid). */
 size_t moe_packed_expert_bytes(const moe_shape* shape, int32_t d_ff);
 
-/* Pack n logical experts (layout above) into the packed format.
+/* Pack n logical experts (layout above) into the packed format: the pages'
+ * low-bit block-quantised experts ([KC-en] section "Hardware Configuration
+ * and Quantization Approach") in the record layout the kernels stream.
  *   codes:  device, n*3*d_ff*d_model bytes (Q2SM, Q2S: u in 0..3; Q3S:
  *           signed q in -4..3; only the low 2 resp. 3 bits of u resp. q+4
  *           are used).
