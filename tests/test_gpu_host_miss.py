@@ -345,3 +345,42 @@ def test_native_host_layer_back_to_back_calls_and_pageable_staging(g):
                                         moe.MOE_F32, hptrs, ws, wsb, p_addr, stb, pool)
     assert ei.value.status == moe.MOE_EINVAL
     pool.close()
+
+
+def test_native_host_layer_bf16_input_and_output(g):
+    """Two tokens with bf16 input and output: the list kernel's copy of the
+    input to the host is half as many bytes; the same bits as the manual
+    sequence on the same inputs."""
+    import torch
+    moe = g.moe
+    w = synth.WORKLOADS["tiny"]
+    T, D, E, k = 2, w["d_model"], w["n_experts"], w["top_k"]
+    shape = moe.MoeShape(D, w["d_ff"], E, k, w["d_ff_shared"], synth.FMT_Q3S)
+    table, hptrs, keep = _slot_layer(g, shape, E, 4, [1, 2, 3, 5, 8, 13])
+    pool = moe.HostPool(4)
+    logits = g.f32_to_dev(synth.router_logits(0, 95, T, E, min_gap=1e-3))
+    xb = synth.activations_bf16(0, 95, T, D)
+    x_dev = g.u16_to_dev(xb)
+    wsb = moe.moe_slot_host_workspace_bytes(shape, T)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=g.DEV)
+    stb = moe.moe_slot_host_staging_bytes(shape, T)
+    stg = torch.empty(stb + 64, dtype=torch.uint8).pin_memory()
+    stg_addr = (stg.data_ptr() + 63) // 64 * 64
+    out = torch.empty(T * D, dtype=torch.int16, device=g.DEV)
+    nm = moe.moe_slot_layer_forward_host(shape, T, x_dev, moe.MOE_BF16, moe.MOE_FLAG_RMSNORM_INPUT,
+                                         logits, table, out, moe.MOE_BF16, hptrs, ws, wsb, stg_addr,
+                                         stb, pool)
+    torch.cuda.synchronize()
+    rl = g.LayerRun(shape, T, slots=True)
+    ref = rl(table, x_dev, moe.MOE_BF16, logits, moe.MOE_BF16, flags=moe.MOE_FLAG_RMSNORM_INPUT)
+    nref = int(rl.miss_count.item())
+    assert nm == nref and nm > 0
+    y = np.zeros((T, D), np.float32)
+    mrec = rl.miss[: 4 * nref].cpu().numpy().copy()
+    moe.moe_host_miss_ffn(shape, T, np.ascontiguousarray(xb).ctypes.data, moe.MOE_BF16,
+                          moe.MOE_FLAG_RMSNORM_INPUT, mrec.ctypes.data, nref, hptrs, y.ctypes.data,
+                          pool)
+    moe.moe_add_rows(ref, moe.MOE_BF16, g.f32_to_dev(y), T, D)
+    torch.cuda.synchronize()
+    pool.close()
+    assert torch.equal(out, ref)
