@@ -10,10 +10,9 @@
 //
 // Two kernels:
 //   * router_gemv_kernel, T <= 4 tokens: the step is one 3 MB read of W_r
-//     (d_model 3072, 512 experts), so it is latency- and HBM-bound.  One wave
-//     per expert row; every lane's row pieces are requested before the
-//     activations are staged into LDS, so the weight reads overlap the
-//     staging; then a wave-wide sum per token.
+//     (d_model 3072, 512 experts), so it is latency- and HBM-bound.  One
+//     one-wave block per expert row; each lane requests its row pieces and
+//     the matching activation pieces at once, then a wave-wide sum per token.
 //   * router_gemm_kernel, more tokens: a bf16 MFMA GEMM (16x16x32) over
 //     tiles of 64 tokens x 256 experts with k-steps of 64 staged through LDS
 //     (next k-step prefetched into registers while the current one runs).
@@ -53,132 +52,112 @@ __device__ __forceinline__ float wave_rinv(const void* x, bool x_bf16, size_t ba
 }
 
 // ---------------------------------------------------------------------------
-// GEMV, T <= 4.  Block: 4 waves, expert rows 4 b .. 4 b + 3.  Dynamic LDS:
-// the T x D activation values (fp32) the dot products use.  Every global load
-// of the block is issued before the first one is waited for: the row pieces,
-// then the activation pieces (16 bytes each, at most kRvX per thread).
-constexpr int kRvJ = 8;  // row pieces (16 bytes) per lane: d_model <= 4096
-constexpr int kRvX = 8;  // activation pieces (8 values) per thread: T * d_model <= 16384
+// GEMV, T <= 4.  One wave per expert row and one wave per block, so the grid
+// has E blocks and every CU reads a share of W_r.  Lane l owns the 16-byte
+// pieces c = l + 64 j (8 values each) of the row and, for every token, the
+// same pieces of the activations, so the dot products need neither LDS nor a
+// block barrier.  Every load of the wave is issued before the first one is
+// used.  Piece indices past the row are clamped into it (the same line for
+// every lane) and their activation values replaced by zeros with a select,
+// so the loads carry no branches and the clamped pieces add exact zeros.
+// Under the RMS rule each lane sums the squares of its pieces of a token in
+// order, a wave-wide sum completes it, and every activation value is scaled
+// and rounded to bf16 before use.
+constexpr int kRvJ = 8;  // pieces per lane: d_model <= 4096
 
 template <int T, bool X_BF16, bool RMS>
-__global__ __launch_bounds__(256) void router_gemv_kernel(const void* __restrict__ x,
-                                                          const uint16_t* __restrict__ W,
-                                                          float* __restrict__ logits, int D, int E) {
-  extern __shared__ float s_x[];  // [T][D]
-  __shared__ float s_ss[4][T];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int e = blockIdx.x * 4 + wv;
-  const int nch = D / 8, npc = T * nch;
-  // 1. This wave's row pieces c = lane + 64 j (rows past E read row E-1).
-  const uint4* wrow = reinterpret_cast<const uint4*>(W + (size_t)(e < E ? e : E - 1) * D);
+__global__ __launch_bounds__(64) void router_gemv_kernel(const void* __restrict__ x,
+                                                         const uint16_t* __restrict__ W,
+                                                         float* __restrict__ logits, int D, int E) {
+  const int lane = threadIdx.x, e = blockIdx.x;
+  const int nch = D / 8;
+  int cc[kRvJ];
+  bool ok[kRvJ];
+#pragma unroll
+  for (int j = 0; j < kRvJ; ++j) {
+    const int c = lane + 64 * j;
+    ok[j] = c < nch;
+    cc[j] = ok[j] ? c : nch - 1;
+  }
+  const uint4* wrow = reinterpret_cast<const uint4*>(W + (size_t)e * D);
   uint4 wr[kRvJ];
 #pragma unroll
-  for (int j = 0; j < kRvJ; ++j) {
-    const int c = lane + 64 * j;
-    wr[j] = c < nch ? wrow[c] : make_uint4(0, 0, 0, 0);
-  }
-  // 2. Activation pieces p = tid + 256 i: values 8 p .. 8 p + 7 of the
-  // row-major [T][D] input (a piece never straddles two tokens).
-  float xv[kRvX][8];
+  for (int j = 0; j < kRvJ; ++j) wr[j] = wrow[cc[j]];
+  // One token's dot product over the lane's pieces (values v[j][0..7]).
+  auto dot = [&](const float (&v)[kRvJ][8]) __attribute__((always_inline)) -> float {
+    float s = 0.f;
 #pragma unroll
-  for (int i = 0; i < kRvX; ++i) {
-    const int pc = tid + 256 * i;
-    if (X_BF16) {
-      const uint4 u = pc < npc ? reinterpret_cast<const uint4*>(x)[pc] : make_uint4(0, 0, 0, 0);
-      const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        xv[i][2 * h] = bf16_lo(uu[h]);
-        xv[i][2 * h + 1] = bf16_hi(uu[h]);
-      }
-    } else {
-      const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-      const float4 a = pc < npc ? reinterpret_cast<const float4*>(x)[2 * pc] : z;
-      const float4 b = pc < npc ? reinterpret_cast<const float4*>(x)[2 * pc + 1] : z;
-      xv[i][0] = a.x; xv[i][1] = a.y; xv[i][2] = a.z; xv[i][3] = a.w;
-      xv[i][4] = b.x; xv[i][5] = b.y; xv[i][6] = b.z; xv[i][7] = b.w;
-    }
-  }
-  // 3. RMS rule: per-token sums of squares (thread, then wave, then the four
-  // waves in order), the same in every block.
-  float rinv[T];
-#pragma unroll
-  for (int t = 0; t < T; ++t) rinv[t] = 1.f;
-  if (RMS) {
-    float ss[T];
-#pragma unroll
-    for (int t = 0; t < T; ++t) ss[t] = 0.f;
-#pragma unroll
-    for (int i = 0; i < kRvX; ++i) {
-      const int pc = tid + 256 * i;
-      float q = 0.f;
-#pragma unroll
-      for (int h = 0; h < 8; ++h) q = fmaf(xv[i][h], xv[i][h], q);
-#pragma unroll
-      for (int t = 0; t < T; ++t) ss[t] += (pc < npc && pc / nch == t) ? q : 0.f;
-    }
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-      const float r = wave_sum(ss[t]);
-      if (lane == 0) s_ss[wv][t] = r;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-      const float tot = s_ss[0][t] + s_ss[1][t] + s_ss[2][t] + s_ss[3][t];
-      rinv[t] = 1.0f / sqrtf(tot / (float)D + 1e-6f);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < kRvX; ++i) {
-    const int pc = tid + 256 * i;
-    if (pc < npc) {
-      float v[8];
-      if (RMS) {
-        const int t = pc / nch;
-        float r = rinv[0];
-#pragma unroll
-        for (int tt = 1; tt < T; ++tt) r = t == tt ? rinv[tt] : r;
-#pragma unroll
-        for (int h = 0; h < 8; ++h) v[h] = bf16_to_f32(f32_to_bf16(xv[i][h] * r));
-      } else {
-#pragma unroll
-        for (int h = 0; h < 8; ++h) v[h] = xv[i][h];
-      }
-      float4* d = reinterpret_cast<float4*>(&s_x[8 * (size_t)pc]);
-      d[0] = make_float4(v[0], v[1], v[2], v[3]);
-      d[1] = make_float4(v[4], v[5], v[6], v[7]);
-    }
-  }
-  __syncthreads();
-  // 4. Dot products over the lane's pieces, then a wave-wide sum per token.
-  float acc[T];
-#pragma unroll
-  for (int t = 0; t < T; ++t) acc[t] = 0.f;
-#pragma unroll
-  for (int j = 0; j < kRvJ; ++j) {
-    const int c = lane + 64 * j;
-    if (c < nch) {
+    for (int j = 0; j < kRvJ; ++j) {
       const uint32_t ww[4] = {wr[j].x, wr[j].y, wr[j].z, wr[j].w};
 #pragma unroll
-      for (int t = 0; t < T; ++t) {
-        const float4 xa = *reinterpret_cast<const float4*>(&s_x[(size_t)t * D + 8 * c]);
-        const float4 xb = *reinterpret_cast<const float4*>(&s_x[(size_t)t * D + 8 * c + 4]);
-        const float xs[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
-        float s = acc[t];
+      for (int i = 0; i < 4; ++i) {
+        s = fmaf(bf16_lo(ww[i]), v[j][2 * i], s);
+        s = fmaf(bf16_hi(ww[i]), v[j][2 * i + 1], s);
+      }
+    }
+    return s;
+  };
+  // The RMS rule on one token's values, in place.
+  auto rms = [&](float (&v)[kRvJ][8]) __attribute__((always_inline)) {
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < kRvJ; ++j)
+#pragma unroll
+      for (int h = 0; h < 8; ++h) ss = fmaf(v[j][h], v[j][h], ss);
+    const float r = 1.0f / sqrtf(wave_sum(ss) / (float)D + 1e-6f);
+#pragma unroll
+    for (int j = 0; j < kRvJ; ++j)
+#pragma unroll
+      for (int h = 0; h < 8; ++h) v[j][h] = bf16_to_f32(f32_to_bf16(v[j][h] * r));
+  };
+  float acc[T];
+  if constexpr (X_BF16) {
+    uint4 xr[T][kRvJ];
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int j = 0; j < kRvJ; ++j)
+        xr[t][j] = reinterpret_cast<const uint4*>(x)[(size_t)t * nch + cc[j]];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      float v[kRvJ][8];
+#pragma unroll
+      for (int j = 0; j < kRvJ; ++j) {
+        const uint32_t uu[4] = {xr[t][j].x, xr[t][j].y, xr[t][j].z, xr[t][j].w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          s = fmaf(bf16_lo(ww[i]), xs[2 * i], s);
-          s = fmaf(bf16_hi(ww[i]), xs[2 * i + 1], s);
+          v[j][2 * i] = ok[j] ? bf16_lo(uu[i]) : 0.f;
+          v[j][2 * i + 1] = ok[j] ? bf16_hi(uu[i]) : 0.f;
         }
-        acc[t] = s;
       }
+      if (RMS) rms(v);
+      acc[t] = dot(v);
+    }
+  } else {  // fp32 input: one token's pieces at a time (64 registers each)
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const float4* xp = reinterpret_cast<const float4*>(x) + (size_t)t * 2 * nch;
+      float4 xa[kRvJ], xb[kRvJ];
+#pragma unroll
+      for (int j = 0; j < kRvJ; ++j) {
+        xa[j] = xp[2 * cc[j]];
+        xb[j] = xp[2 * cc[j] + 1];
+      }
+      float v[kRvJ][8];
+#pragma unroll
+      for (int j = 0; j < kRvJ; ++j) {
+        const float f[8] = {xa[j].x, xa[j].y, xa[j].z, xa[j].w, xb[j].x, xb[j].y, xb[j].z, xb[j].w};
+#pragma unroll
+        for (int h = 0; h < 8; ++h) v[j][h] = ok[j] ? f[h] : 0.f;
+      }
+      if (RMS) rms(v);
+      acc[t] = dot(v);
     }
   }
 #pragma unroll
   for (int t = 0; t < T; ++t) {
-    const float v = wave_sum(acc[t]);
-    if (lane == 0 && e < E) logits[(size_t)t * E + e] = v;
+    const float s = wave_sum(acc[t]);
+    if (lane == t) logits[(size_t)t * E + e] = s;
   }
 }
 
@@ -346,21 +325,17 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const void* __restrict
 
 template <int T>
 hipError_t launch_gemv_t(const RouterArgs& a, hipStream_t st) {
-  const dim3 grid((a.E + 3) / 4);
-  const size_t lds = (size_t)T * a.D * sizeof(float);
   auto k = a.x_bf16 ? (a.rmsnorm ? router_gemv_kernel<T, true, true> : router_gemv_kernel<T, true, false>)
                     : (a.rmsnorm ? router_gemv_kernel<T, false, true> : router_gemv_kernel<T, false, false>);
-  return launch_timed_by(router_timer(), k, grid, dim3(256), (uint32_t)lds, st, a.x, a.w, a.logits,
-                         a.D, a.E);
+  return launch_timed_by(router_timer(), k, dim3(a.E), dim3(64), 0u, st, a.x, a.w, a.logits, a.D,
+                         a.E);
 }
 
 }  // namespace
 
-// The GEMV holds a lane's whole row share in registers (d_model <= 4096) and
-// the T x d_model activations in registers and LDS (at most 60 KB).
-bool router_uses_gemv(int T, int D) {
-  return T <= 4 && D <= 64 * 8 * kRvJ && T * D <= 15360 && T * D <= 256 * 8 * kRvX;
-}
+// The GEMV holds a lane's share of one row and of the T x d_model
+// activations in registers (d_model <= 4096).
+bool router_uses_gemv(int T, int D) { return T <= 4 && D <= 64 * 8 * kRvJ; }
 
 hipError_t launch_router(const RouterArgs& a, hipStream_t st) {
   if (a.T <= 0) return hipSuccess;
