@@ -621,32 +621,16 @@ __device__ __forceinline__ void gateup_body(const DecodeArgs& a, const DecodeWs&
     for (int t = 0; t < T; ++t) rinv[t] = w.rinv[t];
   }
   // A planned call with 2..4 tokens (decode stack): the previous layer's
-  // down blocks left the sums of squares of their output rows; wave 0 of
-  // every block adds the D/16 partials of each token in the same fixed
-  // order, so all blocks agree on the factors without a block-wide pass over
-  // x.  The partials are requested here, a fixed count per lane (indices past
-  // D/16 read partial 0 and are dropped by a select), and the factors are
-  // applied to the projections after the GEMV (RMS_POST below), not to the
-  // staged input, so nothing before the GEMV waits for them.  Only wave 0
-  // reads them (it alone finishes the SwiGLU): the loads of a gate/up block
-  // share its CU's vector-memory path with the weight records.
-  constexpr int kRp = (RMS && T > 1 && PLANNED) ? 4096 / 16 / 64 : 0;
-  float rp[kRp > 0 ? kRp : 1][T];
-  if (kRp > 0 && wv == 0) {
+  // down blocks left the sums of squares of their output rows; every wave
+  // adds the D/16 partials of each token in the same fixed order, so all
+  // blocks agree on the factors without a block-wide pass over x.
+  float rpart[T];
+  if constexpr (RMS && T > 1 && PLANNED) {
 #pragma unroll
-    for (int j = 0; j < kRp; ++j) {
-      const int i = lane + 64 * j;
-      const int ic = i < D / 16 ? i : 0;
-      if constexpr (T == 4) {  // one 16-byte row (the array is 256-byte aligned)
-        const float4 v = *reinterpret_cast<const float4*>(a.rms_in + ic * 4);
-        rp[j][0] = v.x;
-        rp[j][T > 1 ? 1 : 0] = v.y;
-        rp[j][T > 2 ? 2 : 0] = v.z;
-        rp[j][T > 3 ? 3 : 0] = v.w;
-      } else {
+    for (int t = 0; t < T; ++t) rpart[t] = 0.f;
+    for (int i = lane; i < D / 16; i += 64) {
 #pragma unroll
-        for (int t = 0; t < T; ++t) rp[j][t] = a.rms_in[ic * T + t];
-      }
+      for (int t = 0; t < T; ++t) rpart[t] += a.rms_in[i * T + t];
     }
   }
 
@@ -673,14 +657,10 @@ __device__ __forceinline__ void gateup_body(const DecodeArgs& a, const DecodeWs&
   // previous layer's partials in a planned call with 2..4 tokens; from
   // decode_list_kernel otherwise.
   constexpr bool RMS_IN_BLOCK = RMS && T == 1;
-  // RMS_POST: the input is staged as it is and the RMS factor multiplies
-  // the gate and up projections of each token instead (they are linear in
-  // the input); the input is then not rounded to bf16 after the scaling.
-  // Measured on the 4-token stack: scaling the staged input cost about
-  // 0.9 us per layer of VALU work, and holding the staging for the
-  // partials another 1.6 us.
-  constexpr bool RMS_POST = kRp > 0;
-  constexpr bool RMS_STAGE = RMS && !RMS_POST;
+  if constexpr (RMS && T > 1 && PLANNED) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) rinv[t] = 1.0f / sqrtf(wave_sum_f32(rpart[t]) / (float)D + 1e-6f);
+  }
   if constexpr (RMS_IN_BLOCK) {
     float ss[T];
 #pragma unroll
@@ -728,7 +708,7 @@ __device__ __forceinline__ void gateup_body(const DecodeArgs& a, const DecodeWs&
       uint32_t hi[4];
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
-        if (RMS_STAGE) {
+        if (RMS) {
           const float r = rinv[0] * (t == 0) + (T > 1 ? rinv[T > 1 ? 1 : 0] * (t == 1) : 0.f) +
                           (T > 2 ? rinv[T > 2 ? 2 : 0] * (t == 2) : 0.f) +
                           (T > 3 ? rinv[T > 3 ? 3 : 0] * (t == 3) : 0.f);
@@ -752,7 +732,7 @@ __device__ __forceinline__ void gateup_body(const DecodeArgs& a, const DecodeWs&
 #pragma unroll
       for (int q2 = 0; q2 < 2; ++q2) {
         float v0 = v4[2 * q2], v1 = v4[2 * q2 + 1];
-        if (RMS_STAGE) {
+        if (RMS) {
           const float r = rinv[0] * (t == 0) + (T > 1 ? rinv[T > 1 ? 1 : 0] * (t == 1) : 0.f) +
                           (T > 2 ? rinv[T > 2 ? 2 : 0] * (t == 2) : 0.f) +
                           (T > 3 ? rinv[T > 3 ? 3 : 0] * (t == 3) : 0.f);
@@ -806,15 +786,6 @@ __device__ __forceinline__ void gateup_body(const DecodeArgs& a, const DecodeWs&
     mt[t] += __shfl_xor(mt[t], 16, 64);
     mt[t] += __shfl_xor(mt[t], 32, 64);
   }
-  if (RMS_POST && wv == 0) {  // every record has landed: the partials have too
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-      float rpart = 0.f;
-#pragma unroll
-      for (int j = 0; j < kRp; ++j) rpart += lane + 64 * j < D / 16 ? rp[j][t] : 0.f;
-      rinv[t] = 1.0f / sqrtf(wave_sum_f32(rpart) / (float)D + 1e-6f);
-    }
-  }
   if (lane < 16) {
 #pragma unroll
     for (int t = 0; t < T; ++t) s_red[wv][t][n] = acc[t] + mt[t];
@@ -829,13 +800,6 @@ __device__ __forceinline__ void gateup_body(const DecodeArgs& a, const DecodeWs&
     for (int j = 1; j < kGuSplit; ++j) {
       ga += s_red[j][t][nn];
       ub += s_red[kGuSplit + j][t][nn];
-    }
-    if constexpr (RMS_POST) {  // wave 0 (16 T <= 64 threads)
-      float r = rinv[0];
-#pragma unroll
-      for (int tt = 1; tt < T; ++tt) r = t == tt ? rinv[tt] : r;
-      ga *= r;
-      ub *= r;
     }
     const float h = silu(ga) * ub;
     const uint16_t hi = f32_to_bf16(h);
