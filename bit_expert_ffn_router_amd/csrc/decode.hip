@@ -511,6 +511,14 @@ __device__ __forceinline__ void keep_alive(const DnPrefetch& p) {
   for (int r = 0; r < kDnPrefetchPerThread; ++r) asm volatile("" ::"v"(p.v[r]));
 }
 
+// Two fp32 values rounded to nearest even bf16 and packed (lo in bits 0..15):
+// one v_cvt_pk_bf16_f32, the same bits as f32_to_bf16 for finite values.
+typedef __bf16 dq_bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t rne_pk_bf16(float lo, float hi) {
+  const dq_bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 // ----------------------------------------------------------------------------
 // decode_gateup.  Grid: d_ff_shared/16 shared-expert blocks, then
 // (routed list capacity x d_ff/16) blocks, of 512 threads, two blocks per
@@ -712,7 +720,7 @@ __device__ __forceinline__ void gateup_body(const DecodeArgs& a, const DecodeWs&
           const float r = rinv[0] * (t == 0) + (T > 1 ? rinv[T > 1 ? 1 : 0] * (t == 1) : 0.f) +
                           (T > 2 ? rinv[T > 2 ? 2 : 0] * (t == 2) : 0.f) +
                           (T > 3 ? rinv[T > 3 ? 3 : 0] * (t == 3) : 0.f);
-          hi[e2] = pack_bf16x2(bf16_lo(qq[e2]) * r, bf16_hi(qq[e2]) * r);
+          hi[e2] = rne_pk_bf16(bf16_lo(qq[e2]) * r, bf16_hi(qq[e2]) * r);
         } else {
           hi[e2] = qq[e2];
         }
