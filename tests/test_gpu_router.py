@@ -80,7 +80,7 @@ def _check_routing_decision(gpu_logits, x_seen, w, rms, bound, k, min_checked=0.
 
 
 @pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 64, 131])
-@pytest.mark.parametrize("D,E", [(256, 16), (3072, 512), (512, 300)])
+@pytest.mark.parametrize("D,E", [(256, 16), (3072, 512), (512, 300), (4096, 64)])
 @pytest.mark.parametrize("x_f32", [False, True])
 def test_router_logits_match_oracle(g, T, D, E, x_f32):
     import torch
