@@ -442,8 +442,8 @@ moe_status moe_slot_layer_forward_host(const moe_shape* shape, int32_t tokens, c
  *   x:        device [T][d_model], x_dtype MOE_BF16 or MOE_F32, 16-byte aligned.
  *   w_router: device bf16 [n_experts][d_model], 16-byte aligned.
  *   logits:   device fp32 [T][n_experts], 4-byte aligned; written in full.
- * T <= 4 with T*d_model <= 15360 (at d_model 3072: every T <= 4): a GEMV on
- * the activations as given (fp32 input stays fp32).  Otherwise a bf16 MFMA
+ * T <= 4 with d_model <= 4096: a GEMV on the activations as given (fp32
+ * input stays fp32).  Otherwise a bf16 MFMA
  * GEMM: fp32 input is rounded to bf16
  * first, exactly as the layer's prefill path rounds it, so that the logits
  * moe_layer_forward computes for the same input are the same bits.  Only
